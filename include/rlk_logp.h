@@ -1,0 +1,142 @@
+/*
+ * rlk_logp.h - strict, batch- and partition-invariant token log-probabilities
+ * from BF16 logits, computed by HIP kernels for gfx950 (MI355X).
+ *
+ * Defining passages (RL-Kernel documentation pages):
+ *  [CFG-SAMPLING] "Configurable H100 consistency runs", sampling paragraph:
+ *      both sides scale the same BF16 model logits by a float32 temperature;
+ *      temperature is finite and >= 0 (0 selects greedy sampling); top-p lies
+ *      in (0, 1]; top-k is -1 (disabled) or a positive integer up to the real
+ *      vocabulary size; the top-p/top-k support is computed over the real
+ *      vocabulary; temperatures may differ per request.
+ *  [CFG-TOPOLOGY] same page, topology paragraph: fixed virtual TP8 partitions
+ *      and a padded vocabulary of 152576 across physical TP sizes.
+ *  [CFG-KL] same page, mode/KL paragraph: the KL reference logprob is
+ *      temperature-scaled over the full vocabulary; the policy logprob keeps
+ *      its actual top-p/top-k support.
+ *  [CFG-CMDS] same page, command examples: top-k is independent of top-p and
+ *      temperature.
+ *  [REPRO-CANON] "Reproduce and profile the Qwen3-8B TP4/CP2 experiment",
+ *      section "How non-default CUDA topology reuses TP4/CP2": logp emits
+ *      per-virtual-shard vocabulary summaries and merges them in fixed
+ *      global-vocabulary order; a coarser physical rank owns several virtual
+ *      shards, which only adds launches.
+ *
+ * What is computed, per row i (token position) with target column t_i:
+ *   x_j   = BF16 logit of column j, widened exactly to float32, j < vocab_real
+ *   z_j   = fl32(x_j / T_i)                       (IEEE division, [CFG-SAMPLING])
+ *   lse_i = log(sum_j exp(z_j))                   (over the real vocabulary)
+ *   ref_i = z_{t_i} - lse_i                       ([CFG-KL])
+ * The sum is formed from 8 canonical shards of width vocab_padded/8; each
+ * shard is reduced to a summary (an integer reference exponent r_s at or near
+ * the shard maximum in log2 units, and l_s = sum of 2^(x_j*log2(e)/T - r_s)
+ * accumulated in one fixed order), and the 8 summaries are merged left to
+ * right as lse = ln2 * (R + log2(sum_s l_s * 2^(r_s - R))), R = max_s r_s
+ * ([REPRO-CANON]). The order of every floating-point operation depends only
+ * on the column geometry, never on the batch, the row position or `groups`,
+ * so identical rows give identical output bytes in any call.
+ *
+ * Memory: every pointer argument is caller-owned DEVICE memory, except
+ * `layout`, which is a host pointer read during the call. The library never
+ * allocates, frees or synchronises: a call validates its arguments on the
+ * host, enqueues kernels on `stream` and returns. Outputs are complete when
+ * the stream reaches that point. Calls are hipGraph-capturable.
+ *
+ * Errors: argument errors detectable on the host return a negative status
+ * before any HIP call is made (nothing is enqueued). A failed launch returns
+ * RLK_ERR_HIP. Per-row values live on the device and are not checked on the
+ * host; a row with an invalid temperature (NaN, +-inf, < 0) or target
+ * (outside [0, vocab_real)), or whose real logits contain NaN or +inf, or are
+ * all -inf, produces NaN outputs. Columns >= vocab_real are never used,
+ * whatever they hold.
+ */
+#ifndef RLK_LOGP_H
+#define RLK_LOGP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  RLK_OK = 0,
+  RLK_ERR_NULL = -1,      /* a required pointer is NULL */
+  RLK_ERR_ALIGN = -2,     /* logits/workspace not 16-byte aligned, or another array misaligned */
+  RLK_ERR_SHAPE = -3,     /* n_rows or a layout field out of range */
+  RLK_ERR_GROUPS = -4,    /* groups is not 1, 2, 4 or 8 */
+  RLK_ERR_WORKSPACE = -5, /* workspace missing or smaller than rlk_logp_workspace_bytes() */
+  RLK_ERR_HIP = -6        /* the HIP runtime reported an error when launching */
+};
+
+/* Row layout of the logits [CFG-TOPOLOGY], [REPRO-CANON].
+ * Row i starts at element i * row_stride of `logits`; columns are BF16 bit
+ * patterns (uint16). The canonical partition splits columns [0, vocab_padded)
+ * into n_shards shards of width vocab_padded / n_shards. */
+typedef struct rlk_vocab_layout {
+  int64_t vocab_padded; /* multiple of 8 * n_shards, 8 * n_shards <= vocab_padded <= 2^30 */
+  int64_t vocab_real;   /* 1 <= vocab_real <= vocab_padded; columns >= vocab_real are ignored */
+  int64_t row_stride;   /* elements between rows; >= vocab_padded and a multiple of 8 */
+  int32_t n_shards;     /* canonical virtual shards; must be 8 */
+  int32_t groups;       /* physical blocks per row (1, 2, 4 or 8): a block owns n_shards/groups
+                           consecutive shards, like a physical TP rank owning several virtual
+                           shards. Never changes any output byte. */
+} rlk_vocab_layout;
+
+/* Full-vocabulary (reference) logprob of target[i] for each row
+ * [CFG-SAMPLING], [CFG-KL], [REPRO-CANON].
+ *   logits       [n_rows * row_stride] BF16 bits, 16-byte aligned
+ *   temperature  [n_rows] float32; 0 selects greedy: logp = 0 for the
+ *                lowest-index maximum of the real logits, -inf elsewhere
+ *   target       [n_rows] int64 column indices
+ *   logp_out     [n_rows] float32
+ *   lse_out      [n_rows] float32 log-sum-exp of the scaled row (NaN for
+ *                greedy rows), or NULL
+ *   workspace    rlk_logp_workspace_bytes(n_rows, layout, 0) bytes, 16-byte
+ *                aligned; may be NULL when that size is 0 (groups == 1)
+ * Returns RLK_OK or a negative status. n_rows == 0 (with a valid layout)
+ * returns RLK_OK without reading any other argument and enqueues nothing. */
+int32_t rlk_logp_full(const uint16_t* logits, int64_t n_rows, const rlk_vocab_layout* layout,
+                      const float* temperature, const int64_t* target,
+                      float* logp_out, float* lse_out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Policy logprob over the top-k-then-top-p support, and the full-vocabulary
+ * reference logprob used for KL [CFG-SAMPLING], [CFG-KL], [CFG-CMDS].
+ * Support of row i: top-k (when top_k[i] != -1 and < vocab_real) keeps every
+ * column whose scaled logit is >= the k-th largest (ties at the boundary are
+ * all kept); top-p (when top_p[i] < 1) then keeps, among those, every column
+ * whose value is >= the largest value v for which the kept mass at values >= v
+ * reaches top_p[i] times the mass of the top-k set.
+ *   policy_out[i] = z_t - log(sum over the support of exp(z_j)) if t is in the
+ *                   support, else -inf; exactly ref_out[i] when the support
+ *                   is the whole real vocabulary; NaN for an invalid top_p
+ *                   (outside (0, 1]) or top_k (not -1 and not in
+ *                   [1, vocab_real]).
+ *   ref_out[i]    = byte-identical to rlk_logp_full's logp_out[i].
+ *   top_p  [n_rows] float32;  top_k [n_rows] int32.
+ *   workspace      rlk_logp_workspace_bytes(n_rows, layout, 1) bytes, 16-byte aligned.
+ * Greedy rows (temperature 0) put a point mass on the lowest-index maximum for
+ * both outputs. The support decision is taken on integer masses, so it is the
+ * same for any batch or grouping. */
+int32_t rlk_logp_nucleus(const uint16_t* logits, int64_t n_rows, const rlk_vocab_layout* layout,
+                         const float* temperature, const float* top_p, const int32_t* top_k,
+                         const int64_t* target, float* policy_out, float* ref_out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace the calls above need (0 for rlk_logp_full with
+ * groups == 1). Returns 0 for an invalid layout or n_rows < 0. */
+size_t rlk_logp_workspace_bytes(int64_t n_rows, const rlk_vocab_layout* layout, int32_t nucleus);
+
+/* Static, NUL-terminated description of a status code. */
+const char* rlk_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLK_LOGP_H */

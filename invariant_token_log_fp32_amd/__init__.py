@@ -1,0 +1,198 @@
+"""Strict, batch- and partition-invariant token log-probabilities on MI355X.
+
+Thin Python binding of ``librlk_logp.so`` (C ABI declared in
+``include/rlk_logp.h``). This module only marshals arguments: it checks
+tensor dtypes, devices and shapes, passes raw device pointers and the current
+HIP stream, and turns negative status codes into exceptions. Every step of the
+computation runs in the HIP kernels of the library; there is no fallback.
+
+Build the library first with ``python -m invariant_token_log_fp32_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple, Union
+
+__all__ = [
+    "LIB_PATH", "HEADER_PATH", "VocabLayout", "load_library", "status_string", "workspace_bytes",
+    "logp_full", "logp_nucleus", "RlkError", "N_SHARDS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librlk_logp.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "rlk_logp.h")
+N_SHARDS = 8
+
+RLK_OK = 0
+STATUS_NAMES = {
+    0: "RLK_OK", -1: "RLK_ERR_NULL", -2: "RLK_ERR_ALIGN", -3: "RLK_ERR_SHAPE",
+    -4: "RLK_ERR_GROUPS", -5: "RLK_ERR_WORKSPACE", -6: "RLK_ERR_HIP",
+}
+
+
+class RlkError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+class VocabLayout(ctypes.Structure):
+    """Mirror of ``rlk_vocab_layout``."""
+
+    _fields_ = [
+        ("vocab_padded", ctypes.c_int64),
+        ("vocab_real", ctypes.c_int64),
+        ("row_stride", ctypes.c_int64),
+        ("n_shards", ctypes.c_int32),
+        ("groups", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m invariant_token_log_fp32_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    lay = ctypes.POINTER(VocabLayout)
+    lib.rlk_logp_full.argtypes = [vp, i64, lay, vp, vp, vp, vp, vp, sz, vp]
+    lib.rlk_logp_full.restype = i32
+    lib.rlk_logp_nucleus.argtypes = [vp, i64, lay, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.rlk_logp_nucleus.restype = i32
+    lib.rlk_logp_workspace_bytes.argtypes = [i64, lay, i32]
+    lib.rlk_logp_workspace_bytes.restype = sz
+    lib.rlk_status_string.argtypes = [i32]
+    lib.rlk_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def declared_functions(header: str = HEADER_PATH):
+    """Names of the functions that include/rlk_logp.h declares."""
+    text = open(header).read()
+    return sorted(set(re.findall(r"^\s*(?:int32_t|size_t|const char\*)\s+(rlk_\w+)\s*\(", text, re.M)))
+
+
+def status_string(status: int) -> str:
+    return load_library().rlk_status_string(int(status)).decode()
+
+
+def make_layout(vocab_padded: int, vocab_real: int, row_stride: int, groups: int = 1) -> VocabLayout:
+    return VocabLayout(int(vocab_padded), int(vocab_real), int(row_stride), N_SHARDS, int(groups))
+
+
+def workspace_bytes(n_rows: int, vocab_padded: int, vocab_real: int, row_stride: Optional[int] = None,
+                    groups: int = 1, nucleus: bool = False) -> int:
+    lay = make_layout(vocab_padded, vocab_real, row_stride or vocab_padded, groups)
+    return int(load_library().rlk_logp_workspace_bytes(int(n_rows), ctypes.byref(lay), 1 if nucleus else 0))
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check_logits(logits):
+    torch = _torch()
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D [n_rows, row_stride]")
+    if logits.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("logits must hold BF16 bit patterns (bfloat16, int16 or uint16)")
+    if not logits.is_cuda:
+        raise ValueError("logits must be a device tensor")
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    return logits.stride(0) if logits.shape[0] > 1 else max(logits.stride(0), logits.shape[1])
+
+
+def _per_row(value, n, dtype, device, name):
+    torch = _torch()
+    if isinstance(value, (int, float)):
+        return torch.full((n,), value, dtype=dtype, device=device)
+    if value.dtype != dtype or value.device != device or value.shape != (n,) or not value.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape ({n},) on {device}")
+    return value
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def logp_full(logits, temperature: Union[float, "torch.Tensor"], target, *, vocab_real: int,
+              vocab_padded: Optional[int] = None, groups: int = 1, return_lse: bool = False,
+              out=None, lse_out=None, workspace=None, stream=None):
+    """Full-vocabulary reference logprob of ``target`` per row (rlk_logp_full).
+
+    ``logits`` is a [n_rows, >= vocab_padded] device tensor of BF16 bits whose
+    row stride is a multiple of 8 elements; ``temperature`` is a float or a
+    float32 [n_rows] tensor; ``target`` is int64 [n_rows]. Returns the float32
+    logprobs (and the log-sum-exps when ``return_lse``).
+    """
+    torch = _torch()
+    stride = _check_logits(logits)
+    n = logits.shape[0]
+    dev = logits.device
+    vp = int(vocab_padded if vocab_padded is not None else logits.shape[1])
+    temperature = _per_row(temperature, n, torch.float32, dev, "temperature")
+    target = _per_row(target, n, torch.int64, dev, "target")
+    out = out if out is not None else torch.empty(n, dtype=torch.float32, device=dev)
+    if return_lse and lse_out is None:
+        lse_out = torch.empty(n, dtype=torch.float32, device=dev)
+    lay = make_layout(vp, vocab_real, stride, groups)
+    lib = load_library()
+    need = int(lib.rlk_logp_workspace_bytes(n, ctypes.byref(lay), 0))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = lib.rlk_logp_full(
+        logits.data_ptr(), n, ctypes.byref(lay), temperature.data_ptr(), target.data_ptr(),
+        out.data_ptr(), lse_out.data_ptr() if lse_out is not None else None,
+        workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0, _stream_handle(stream, dev))
+    if st != RLK_OK:
+        raise RlkError(st, "rlk_logp_full")
+    return (out, lse_out) if return_lse else out
+
+
+def logp_nucleus(logits, temperature, top_p, top_k, target, *, vocab_real: int,
+                 vocab_padded: Optional[int] = None, groups: int = 1, policy_out=None, ref_out=None,
+                 workspace=None, stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Policy logprob over the top-k-then-top-p support and the full-vocabulary
+    reference logprob (rlk_logp_nucleus). ``top_p`` float or float32 [n_rows],
+    ``top_k`` int or int32 [n_rows]. Returns (policy, reference)."""
+    torch = _torch()
+    stride = _check_logits(logits)
+    n = logits.shape[0]
+    dev = logits.device
+    vp = int(vocab_padded if vocab_padded is not None else logits.shape[1])
+    temperature = _per_row(temperature, n, torch.float32, dev, "temperature")
+    top_p = _per_row(top_p, n, torch.float32, dev, "top_p")
+    top_k = _per_row(top_k, n, torch.int32, dev, "top_k")
+    target = _per_row(target, n, torch.int64, dev, "target")
+    policy_out = policy_out if policy_out is not None else torch.empty(n, dtype=torch.float32, device=dev)
+    ref_out = ref_out if ref_out is not None else torch.empty(n, dtype=torch.float32, device=dev)
+    lay = make_layout(vp, vocab_real, stride, groups)
+    lib = load_library()
+    need = int(lib.rlk_logp_workspace_bytes(n, ctypes.byref(lay), 1))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = lib.rlk_logp_nucleus(
+        logits.data_ptr(), n, ctypes.byref(lay), temperature.data_ptr(), top_p.data_ptr(),
+        top_k.data_ptr(), target.data_ptr(), policy_out.data_ptr(), ref_out.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), _stream_handle(stream, dev))
+    if st != RLK_OK:
+        raise RlkError(st, "rlk_logp_nucleus")
+    return policy_out, ref_out

@@ -1,0 +1,55 @@
+"""Ahead-of-time build of the HIP library for gfx950.
+
+Produces ``librlk_logp.so`` next to this file from ``csrc/rlk_logp.hip``:
+    python -m invariant_token_log_fp32_amd.build
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "rlk_logp.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "librlk_logp.so")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    # every intended fused multiply-add is written explicitly
+    "-ffp-contract=off",
+    # no packed fp32 instructions in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found: the ROCm toolchain is required to build librlk_logp.so")
+    return exe
+
+
+def build(extra_flags=(), out: str = LIB, verbose: bool = False) -> str:
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-I", os.path.join(PKG, "csrc"), "-o", tmp, SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -11,3 +11,12 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _library_built():
+    """Build librlk_logp.so when it is missing (a fresh checkout)."""
+    from invariant_token_log_fp32_amd import LIB_PATH
+    if not os.path.exists(LIB_PATH):
+        from invariant_token_log_fp32_amd import build
+        build.build()

@@ -1,0 +1,116 @@
+"""Host-side tests of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function include/rlk_logp.h declares, and
+reject every host-detectable argument error with its documented status before
+any HIP call is made (so these calls return without touching a device). The
+pointers passed here are fake, aligned, non-null addresses that the library
+never dereferences on the host.
+"""
+import ctypes
+
+import pytest
+
+import invariant_token_log_fp32_amd as rlk
+from invariant_token_log_fp32_amd import VocabLayout
+
+OK, NULL, ALIGN, SHAPE, GROUPS, WS, HIP = 0, -1, -2, -3, -4, -5, -6
+P = 0x10000  # fake 64 KiB-aligned device address
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rlk.load_library()
+
+
+def lay(vp=1024, vr=1000, stride=None, shards=8, groups=1):
+    return VocabLayout(vp, vr, stride if stride is not None else vp, shards, groups)
+
+
+def full(lib, logits=P, n=4, L=None, t=P + 0x100, tg=P + 0x200, out=P + 0x300, lse=None, ws=None, wsb=0):
+    L = L if L is not None else lay()
+    return lib.rlk_logp_full(logits, n, ctypes.byref(L) if L is not False else None, t, tg, out, lse,
+                             ws, wsb, None)
+
+
+def nuc(lib, logits=P, n=4, L=None, t=P + 0x100, p=P + 0x140, k=P + 0x180, tg=P + 0x200, pol=P + 0x300,
+        ref=P + 0x400, ws=P + 0x1000, wsb=1 << 20):
+    L = L if L is not None else lay()
+    return lib.rlk_logp_nucleus(logits, n, ctypes.byref(L) if L is not False else None, t, p, k, tg, pol, ref,
+                                ws, wsb, None)
+
+
+def test_every_declared_function_is_exported(lib):
+    names = rlk.declared_functions()
+    assert set(names) == {"rlk_logp_full", "rlk_logp_nucleus", "rlk_logp_workspace_bytes", "rlk_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in (OK, NULL, ALIGN, SHAPE, GROUPS, WS, HIP):
+        s = rlk.status_string(code)
+        assert s and s != "unknown status"
+    assert rlk.status_string(12345) == "unknown status"
+
+
+def test_zero_rows_is_ok_without_launch(lib):
+    assert full(lib, n=0) == OK
+    assert nuc(lib, n=0, wsb=0) == OK
+    assert full(lib, n=0, L=lay(groups=4), ws=P + 0x2000, wsb=0) == OK
+    # empty arrays may come with NULL pointers
+    assert full(lib, n=0, logits=None, t=None, tg=None, out=None) == OK
+    assert nuc(lib, n=0, logits=None, p=None, k=None, ws=None, wsb=0) == OK
+    # the layout is still validated
+    assert full(lib, n=0, L=lay(groups=3)) == GROUPS
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), NULL), (dict(t=None), NULL), (dict(tg=None), NULL), (dict(out=None), NULL),
+    (dict(L=False), NULL),
+    (dict(logits=P + 2), ALIGN), (dict(logits=P + 8), ALIGN), (dict(t=P + 2), ALIGN), (dict(tg=P + 4), ALIGN),
+    (dict(out=P + 1), ALIGN), (dict(lse=P + 3), ALIGN),
+    (dict(n=-1), SHAPE),
+    (dict(L=lay(shards=4)), SHAPE), (dict(L=lay(vp=1000, vr=1000)), SHAPE), (dict(L=lay(vp=32, vr=32)), SHAPE),
+    (dict(L=lay(vr=0)), SHAPE), (dict(L=lay(vr=1025)), SHAPE), (dict(L=lay(stride=1020)), SHAPE),
+    (dict(L=lay(stride=1028)), SHAPE), (dict(L=lay(vp=(1 << 30) + 64, vr=10)), SHAPE),
+    (dict(L=lay(groups=3)), GROUPS), (dict(L=lay(groups=16)), GROUPS), (dict(L=lay(groups=0)), GROUPS),
+    (dict(L=lay(groups=2)), WS), (dict(L=lay(groups=2), ws=P + 0x2000, wsb=4 * 8 * 16 - 1), WS),
+    (dict(L=lay(groups=8), ws=P + 0x2008, wsb=1 << 20), ALIGN),
+    (dict(n=1 << 29, L=lay(groups=8), ws=P, wsb=1 << 40), SHAPE),
+])
+def test_full_rejects_bad_arguments(lib, kw, code):
+    assert full(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(p=None), NULL), (dict(k=None), NULL), (dict(pol=None), NULL), (dict(ref=None), NULL),
+    (dict(p=P + 2), ALIGN), (dict(k=P + 1), ALIGN), (dict(pol=P + 2), ALIGN), (dict(ref=P + 2), ALIGN),
+    (dict(ws=None), WS), (dict(wsb=4 * 8 * 16 - 1), WS), (dict(ws=P + 4), ALIGN), (dict(logits=None), NULL),
+    (dict(L=lay(groups=5)), GROUPS), (dict(n=-3), SHAPE), (dict(L=lay(vr=2000)), SHAPE),
+])
+def test_nucleus_rejects_bad_arguments(lib, kw, code):
+    assert nuc(lib, **kw) == code
+
+
+def test_workspace_sizes(lib):
+    assert rlk.workspace_bytes(8192, 152576, 151936) == 0
+    for g in (2, 4, 8):
+        assert rlk.workspace_bytes(8192, 152576, 151936, groups=g) == 8192 * 8 * 16
+    assert rlk.workspace_bytes(8192, 152576, 151936, nucleus=True) == 8192 * 8 * 16
+    assert rlk.workspace_bytes(-1, 152576, 151936) == 0
+    assert rlk.workspace_bytes(10, 152576, 151936, groups=3) == 0
+    L = lay()
+    assert lib.rlk_logp_workspace_bytes(5, None, 0) == 0
+    assert lib.rlk_logp_workspace_bytes(5, ctypes.byref(L), 1) == 5 * 128
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    mod = importlib.import_module("invariant_token_log_fp32_amd")
+    with pytest.raises(RuntimeError, match="missing"):
+        saved = mod._lib
+        try:
+            mod._lib = None
+            mod.load_library(str(tmp_path / "nope.so"))
+        finally:
+            mod._lib = saved

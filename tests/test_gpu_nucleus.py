@@ -1,0 +1,219 @@
+"""GPU parity of rlk_logp_nucleus (policy over the top-k-then-top-p support and
+the full-vocabulary reference) against the CPU oracle.
+
+Defining passages: RL-Kernel page "Configurable H100 consistency runs":
+sampling paragraph (top-p in (0, 1], top-k -1 or up to the real vocabulary,
+support from the real vocabulary, per-request temperatures), mode/KL paragraph
+(the policy keeps its top-p/top-k support, the KL reference is the
+full-vocabulary temperature-scaled logprob), command examples (top-k
+independent of top-p and temperature).
+
+Rows whose top-p decision lies within 2e-6 of p (the ambiguity band) may match
+the oracle under either neighbouring cut; every other row must match its
+support exactly and its value within 2e-5.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import datagen
+import invariant_token_log_fp32_amd as rlk
+from oracle import logp as O
+
+from gpu_util import TOL, assert_close, assert_nucleus_close, row_tolerance, say, to_host, upload, upload_logits
+
+pytestmark = pytest.mark.gpu
+
+GROUPS = (1, 2, 4, 8)
+
+
+def run_nucleus(logits_np, vr, temps, top_p, top_k, targets, groups=1, vp=None):
+    import torch
+    lg = upload_logits(logits_np)
+    pol, ref = rlk.logp_nucleus(lg, upload(temps, torch.float32), upload(top_p, torch.float32),
+                                upload(top_k, torch.int32), upload(targets, torch.int64),
+                                vocab_real=vr, vocab_padded=vp, groups=groups)
+    full = rlk.logp_full(lg, upload(temps, torch.float32), upload(targets, torch.int64), vocab_real=vr,
+                         vocab_padded=vp, groups=groups)
+    torch.cuda.synchronize()
+    return to_host(pol), to_host(ref), to_host(full)
+
+
+def check(logits, vr, temps, top_p, top_k, targets, what, vp=None, groups_list=GROUPS):
+    want_pol, want_ref, infos = O.nucleus_logp(logits, vr, temps, top_p, top_k, targets)
+    tol = row_tolerance(logits, vr, temps)
+    first = None
+    for groups in groups_list:
+        pol, ref, full = run_nucleus(logits, vr, temps, top_p, top_k, targets, groups, vp)
+        assert ref.tobytes() == full.tobytes(), f"{what}: reference bytes differ from rlk_logp_full"
+        assert_close(ref, want_ref, tol=tol, what=f"{what} ref g{groups}")
+        n_amb = assert_nucleus_close(pol, want_pol, infos, tol=tol, what=f"{what} policy g{groups}")
+        if first is None:
+            first = pol.tobytes()
+        assert pol.tobytes() == first, f"{what}: policy bytes differ between groups"
+    return want_pol, infos
+
+
+def support_targets(logits, vr, temps, top_p, top_k, seed):
+    """Targets drawn uniformly from each row's oracle support."""
+    rng = np.random.default_rng(seed)
+    out = np.empty(logits.shape[0], dtype=np.int64)
+    for i in range(logits.shape[0]):
+        _, _, info = O.nucleus_row(logits[i], vr, float(temps[i]), float(top_p[i]), int(top_k[i]), 0,
+                                   want_mask=True)
+        idx = np.flatnonzero(info.support_mask)
+        out[i] = int(rng.choice(idx))
+    return out
+
+
+CASES = [(0.9, -1), (0.95, 50), (1.0, 10), (0.5, 3), (0.99, 128), (1e-6, -1), (1.0, 1), (0.3, 1000),
+         (1.0, 999), (0.999, -1)]
+
+
+def test_tiny_every_target_all_cases():
+    say("case: tiny nucleus, every target")
+    w = datagen.tiny()
+    logits, _ = w.generate()
+    rep = np.repeat(logits, 1000, axis=0)
+    tg = np.tile(np.arange(1000), 4)
+    n = rep.shape[0]
+    temps = np.ones(n, dtype=np.float32)
+    for p, k in CASES:
+        top_p = np.full(n, p, dtype=np.float32)
+        top_k = np.full(n, k, dtype=np.int32)
+        want_pol, _ = check(rep, 1000, temps, top_p, top_k, tg, f"tiny p={p} k={k}", groups_list=(1, 8))
+        pol, _, _ = run_nucleus(rep, 1000, temps, top_p, top_k, tg)
+        for i in range(4):
+            blk = pol[i * 1000:(i + 1) * 1000].astype(np.float64)
+            fin = np.isfinite(blk)
+            assert abs(math.fsum(np.exp(blk[fin])) - 1.0) < 3e-5
+            assert np.array_equal(fin, np.isfinite(want_pol[i * 1000:(i + 1) * 1000]))
+
+
+def _palette_rows(seed, n, vp, vr):
+    """Rows drawn from a few BF16 values: large tie classes at every boundary."""
+    rng = np.random.default_rng(seed)
+    pal = np.array([-3.0, -1.0, -0.5, 0.0, 0.25, 1.0, 1.5, 2.0, 2.5, 3.0], dtype=np.float32)
+    rows = np.full((n, vp), datagen.BF16_NEG_INF, dtype=np.uint16)
+    for i in range(n):
+        rows[i, :vr] = datagen.f32_to_bf16_bits(rng.choice(pal, size=vr))
+    return rows
+
+
+def test_tied_classes_and_parameter_mix():
+    say("case: ties and parameter mix")
+    vp, vr = 2048, 1999
+    logits = _palette_rows(5, 40, vp, vr)
+    rng = np.random.default_rng(6)
+    temps = rng.choice(np.array([0.7, 1.0, 1.3, 0.4], dtype=np.float32), 40)
+    top_p = rng.choice(np.array([0.95, 0.99, 0.5, 1.0, 0.1], dtype=np.float32), 40)
+    top_k = rng.choice(np.array([-1, 128, 1, 300, 1999, 1500], dtype=np.int32), 40)
+    targets = rng.integers(0, vr, 40)
+    check(logits, vr, temps, top_p, top_k, targets, "ties")
+    targets = support_targets(logits, vr, temps, top_p, top_k, 8)
+    check(logits, vr, temps, top_p, top_k, targets, "ties in-support")
+
+
+def test_support_limited_rows_match_enumeration():
+    """Rows with at most 12 finite real logits (the rest -inf): the oracle's
+    support on these is pinned by exhaustive subset enumeration."""
+    say("case: support-limited rows")
+    vp, vr = 1024, 1000
+    rng = np.random.default_rng(12)
+    n = 64
+    logits = np.full((n, vp), datagen.BF16_NEG_INF, dtype=np.uint16)
+    for i in range(n):
+        m = int(rng.integers(1, 13))
+        cols = rng.choice(vr, m, replace=False)
+        vals = rng.choice(np.array([0.0, 0.5, 1.0, 1.25, 2.0, -1.0], np.float32), m)
+        logits[i, cols] = datagen.f32_to_bf16_bits(vals)
+    temps = rng.choice(np.array([0.7, 1.0, 1.3], np.float32), n)
+    top_p = rng.choice(np.array([0.3, 0.6, 0.9, 1.0], np.float32), n)
+    top_k = rng.choice(np.array([-1, 1, 2, 3, 5], np.int32), n)
+    targets = support_targets(logits, vr, temps, top_p, top_k, 13)
+    check(logits, vr, temps, top_p, top_k, targets, "support-limited")
+
+
+def test_special_rows():
+    say("case: nucleus special rows")
+    vp, vr = 4096, 4000
+    rng = np.random.default_rng(21)
+    base = datagen.f32_to_bf16_bits(rng.normal(0, 2.5, vr).astype(np.float32))
+    rows, T, P, K, TG = [], [], [], [], []
+
+    def add(t, p, k, tg, row=base):
+        r = np.full(vp, datagen.BF16_NEG_INF, dtype=np.uint16)
+        r[:vr] = row
+        rows.append(r)
+        T.append(t)
+        P.append(p)
+        K.append(k)
+        TG.append(tg)
+
+    am = int(np.argmax(datagen.bf16_bits_to_f32(base)))
+    for p, k in ((0.0, -1), (1.5, -1), (float("nan"), -1), (0.9, 0), (0.9, -2), (0.9, vr + 1)):
+        add(0.7, p, k, am)                   # invalid top-p / top-k: policy NaN, reference valid
+    add(0.0, 0.9, 5, am)                     # greedy
+    add(0.0, 0.9, 5, am + 1)
+    add(0.7, 1.0, -1, 3)                     # disabled: policy == reference
+    add(0.7, 1.0, vr, 3)
+    add(0.7, 1.0, vr - 1, 3)                 # top-k keeps all but the minimum class
+    add(0.7, 0.9, -1, 3, row=np.full(vr, datagen.f32_to_bf16_bits(np.float32([1.0]))[0], np.uint16))  # all equal
+    add(float("nan"), 0.9, 5, 3)
+    add(0.7, 0.9, 5, -4)
+    logits = np.stack(rows)
+    check(logits, vr, np.array(T, np.float32), np.array(P, np.float32), np.array(K, np.int32),
+          np.array(TG, np.int64), "special")
+
+
+@pytest.fixture(scope="module")
+def qwen_logits():
+    w = datagen.nucleus()
+    say("generating the 8192 x 152576 workload")
+    logits, targets = w.generate()
+    return w, logits, targets
+
+
+def test_full_size_nucleus_sampled(qwen_logits):
+    """8192 x 152576, T = 0.7, top-p 0.95, top-k off; sampled rows get targets
+    from their oracle nucleus; reference bytes equal rlk_logp_full's."""
+    import torch
+    w, logits, targets = qwen_logits
+    rows = np.random.default_rng(3003).choice(w.n_rows, 40, replace=False)
+    tg = targets.copy()
+    tg[rows] = support_targets(logits[rows], w.vocab_real, w.temperature[rows], w.top_p[rows], w.top_k[rows],
+                               3003)
+    say("case: nucleus full size, groups 1")
+    pol, ref, full = run_nucleus(logits, w.vocab_real, w.temperature, w.top_p, w.top_k, tg)
+    assert ref.tobytes() == full.tobytes()
+    want_pol, want_ref, infos = O.nucleus_logp(logits[rows], w.vocab_real, w.temperature[rows], w.top_p[rows],
+                                               w.top_k[rows], tg[rows])
+    assert_close(ref[rows], want_ref, what="nucleus full ref")
+    n_amb = assert_nucleus_close(pol[rows], want_pol, infos, what="nucleus full policy")
+    say(f"ambiguous sampled rows: {n_amb}")
+    assert np.isfinite(pol[rows]).all()
+    del torch
+
+
+def test_per_request_sampled():
+    """64 requests x 128 rows, T in {0.7, 1.0, 1.3}, top-p in {0.95, 0.99},
+    top-k in {-1, 128}; two sampled rows per request."""
+    w = datagen.per_request()
+    say("generating per-request workload")
+    logits, targets = w.generate()
+    rng = np.random.default_rng(4004)
+    rows = np.array([r * 128 + int(rng.integers(0, 128)) for r in range(64)] +
+                    [r * 128 + int(rng.integers(0, 128)) for r in range(64)])
+    tg = targets.copy()
+    tg[rows] = support_targets(logits[rows], w.vocab_real, w.temperature[rows], w.top_p[rows], w.top_k[rows],
+                               4005)
+    for groups in (1, 4):
+        say(f"case: per-request groups {groups}")
+        pol, ref, full = run_nucleus(logits, w.vocab_real, w.temperature, w.top_p, w.top_k, tg, groups)
+        assert ref.tobytes() == full.tobytes()
+        want_pol, want_ref, infos = O.nucleus_logp(logits[rows], w.vocab_real, w.temperature[rows],
+                                                   w.top_p[rows], w.top_k[rows], tg[rows])
+        assert_close(ref[rows], want_ref, what="per-request ref")
+        n_amb = assert_nucleus_close(pol[rows], want_pol, infos, what="per-request policy")
+        say(f"ambiguous sampled rows: {n_amb}")
