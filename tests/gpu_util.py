@@ -77,6 +77,7 @@ def assert_nucleus_close(pol_gpu, pol_want, infos, tol=TOL, what=""):
     """Policy comparison with the ambiguity band: a row whose top-p decision lies
     within the band may match the oracle under either neighbouring cut."""
     pol_gpu = np.asarray(pol_gpu, dtype=np.float64)
+    tol = np.broadcast_to(np.asarray(tol, dtype=np.float64), pol_gpu.shape)
     n_amb = 0
     for i, info in enumerate(infos):
         cands = [pol_want[i]] + list(info.alternatives if info.ambiguous else [])
@@ -86,7 +87,7 @@ def assert_nucleus_close(pol_gpu, pol_want, infos, tol=TOL, what=""):
                 ok = True
             elif np.isinf(c) or np.isinf(pol_gpu[i]):
                 ok = ok or (c == pol_gpu[i])
-            elif abs(pol_gpu[i] - c) <= tol:
+            elif abs(pol_gpu[i] - c) <= tol[i]:
                 ok = True
         if info.ambiguous:
             n_amb += 1
