@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Throughput of the strict token-logprob path on one MI355X.
+
+A step is one call of the hot path over one batch: rlk_logp_full on 8192 rows
+of 152576-wide BF16 logits (151936 real columns, pads -inf), temperature 0.7,
+uniform targets - the Qwen3-8B-shaped logits of the RL-Kernel pages (page
+"Configurable H100 consistency runs": padded vocabulary 152576, float32
+temperature scaling of BF16 logits; page "H100 rollout context parallelism":
+8,192 active tokens per validation). Inputs are seeded synthetic normals
+(sigma 2.5, one +8 spike per row) generated on the host and uploaded before
+the timed region; two copies alternate so that no step reads logits the
+previous step left in the 256 MB last-level cache.
+
+Prints one JSON line. `value` is tokens/s over the K timed steps (wall clock
+between two device synchronisations); `roofline.achieved` is the algorithmic
+bytes of one launch divided by the average launch time measured with HIP
+events on the launch stream over the same region. `cpu_baseline` times the
+CPU oracle (float64 numpy, one core) on a bounded sample of the same rows.
+`secondary` reports rlk_logp_nucleus on the top-p 0.95 workload and on the
+per-request workload (64 requests x 128 rows), for information.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "logp tokens/s and logits HBM GB/s (% of peak), 8192×152576 BF16, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_logp_full_8192x152576.json")
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "invariant_token_log_fp32_amd", "csrc", "rlk_logp.hip"),
+    os.path.join(ROOT, "invariant_token_log_fp32_amd", "csrc", "logp_device.hpp"),
+]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def bytes_full(n_rows: int, vocab_real: int) -> int:
+    # real logits + int64 target + float32 temperature + float32 output, per row
+    return n_rows * (vocab_real * 2 + 8 + 4 + 4)
+
+
+def bytes_nucleus(n_rows: int, vocab_real: int) -> int:
+    # real logits (read once) + target + temperature + top-p + top-k + two outputs
+    return n_rows * (vocab_real * 2 + 8 + 4 + 4 + 4 + 8)
+
+
+def cpu_baseline(workload, logits, targets, rows: int):
+    from oracle import logp as O
+    rows = min(rows, workload.n_rows)
+    t0 = time.perf_counter()
+    for i in range(rows):
+        O.ref_logp_row(logits[i], workload.vocab_real, float(workload.temperature[i]), int(targets[i]))
+    dt = time.perf_counter() - t0
+    return {
+        "value": rows / dt,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"rows 0..{rows - 1} of the same 8192-row workload (full 151936-column rows), "
+                  f"float64 numpy reference logprob, one core, {dt:.1f} s",
+    }
+
+
+def time_calls(fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(steps):
+        fn(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, ev0.elapsed_time(ev1) / steps
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--groups", type=int, default=1, help="physical blocks per row (1, 2, 4 or 8)")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle sample size for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run one device copy of the logits (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs the hot path on a single MI355X "
+              "(rows are independent, so N GPUs would each run this same benchmark on their own rows); "
+              "run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import datagen
+    import invariant_token_log_fp32_amd as rlk
+
+    rlk.load_library()  # fails loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = datagen.full()
+    logits, targets = w.generate()
+    lg_a = torch.from_numpy(logits.view(np.int16)).to(dev)
+    lg_b = lg_a.clone()
+    bufs = (lg_a, lg_b)
+    temp = torch.full((w.n_rows,), 0.7, dtype=torch.float32, device=dev)
+    tg = torch.from_numpy(targets).to(dev)
+    out = torch.empty(w.n_rows, dtype=torch.float32, device=dev)
+    ws = None
+    need = rlk.workspace_bytes(w.n_rows, w.vocab_padded, w.vocab_real, groups=args.groups)
+    if need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        rlk.logp_full(bufs[i % 2], temp, tg, vocab_real=w.vocab_real, groups=args.groups, out=out, workspace=ws)
+
+    wall, ms_event = time_calls(step, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = w.n_rows * args.steps / wall
+    alg = bytes_full(w.n_rows, w.vocab_real)
+    achieved = alg / (ms_event * 1e-3) / 1e9
+
+    if args.calibrate_copy:
+        lg_b.copy_(lg_a)
+        torch.cuda.synchronize()
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "full-vocab logp: 8192 rows x 152576 BF16 (151936 real), T 0.7, uniform targets",
+            "n_rows": w.n_rows, "vocab_padded": w.vocab_padded, "vocab_real": w.vocab_real,
+            "temperature": 0.7, "groups": args.groups, "entry_point": "rlk_logp_full",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": stored_traffic(),
+            "algorithmic_bytes_per_launch": alg,
+            "avg_launch_ms": ms_event,
+        },
+    }
+
+    if not args.no_secondary:
+        sec = []
+        pk = torch.full((w.n_rows,), -1, dtype=torch.int32, device=dev)
+        pp = torch.full((w.n_rows,), 0.95, dtype=torch.float32, device=dev)
+        pol = torch.empty(w.n_rows, dtype=torch.float32, device=dev)
+        ref = torch.empty(w.n_rows, dtype=torch.float32, device=dev)
+        wsn = torch.empty(rlk.workspace_bytes(w.n_rows, w.vocab_padded, w.vocab_real, nucleus=True),
+                          dtype=torch.uint8, device=dev)
+
+        def nstep(i, lgs=bufs, t=temp, p=pp, k=pk, target=tg):
+            rlk.logp_nucleus(lgs[i % 2], t, p, k, target, vocab_real=w.vocab_real, policy_out=pol, ref_out=ref,
+                             workspace=wsn)
+
+        _, ms_n = time_calls(nstep, 10, 2)
+        ab = bytes_nucleus(w.n_rows, w.vocab_real)
+        sec.append({"workload": "nucleus: same logits, top-p 0.95, top-k off, T 0.7", "entry_point":
+                    "rlk_logp_nucleus", "ms_per_step": ms_n, "tokens_per_s": w.n_rows / (ms_n * 1e-3),
+                    "achieved_GBs": ab / (ms_n * 1e-3) / 1e9, "frac": ab / (ms_n * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        wr = datagen.per_request()
+        lg_r, tg_r = wr.generate()
+        lg_r = (torch.from_numpy(lg_r.view(np.int16)).to(dev),) * 2
+        prm = dict(t=torch.from_numpy(wr.temperature).to(dev), p=torch.from_numpy(wr.top_p).to(dev),
+                   k=torch.from_numpy(wr.top_k).to(dev), target=torch.from_numpy(tg_r).to(dev))
+        _, ms_r = time_calls(lambda i: nstep(i, lgs=lg_r, **prm), 10, 2)
+        sec.append({"workload": "per-request: 64 requests x 128 rows, T {0.7,1.0,1.3}, top-p {0.95,0.99}, "
+                    "top-k {-1,128}", "entry_point": "rlk_logp_nucleus", "ms_per_step": ms_r,
+                    "tokens_per_s": wr.n_rows / (ms_r * 1e-3), "achieved_GBs": ab / (ms_r * 1e-3) / 1e9,
+                    "frac": ab / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        result["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, logits, targets, args.cpu_rows)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
