@@ -111,8 +111,8 @@ def time_calls(fn, steps, warmup):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--groups", type=int, default=1, help="physical blocks per row (1, 2, 4 or 8)")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle sample size for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

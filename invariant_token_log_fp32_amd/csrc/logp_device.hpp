@@ -14,7 +14,7 @@
 //     (ncols % 8 != 0) is processed after them with its missing columns
 //     treated as -inf;
 //   * lane l of the wave owns vectors l, l+64, l+128, ...; they are consumed
-//     in chunks of U vectors per lane (chunk j = vectors (jU + u)*64 + l);
+//     in chunks of U = 8 vectors per lane (chunk j = vectors (jU + u)*64 + l);
 //   * each lane keeps 8 accumulators, one per position inside a vector, and
 //     adds its terms in vector order;
 //   * the lane total is ((a0+a1)+(a2+a3))+((a4+a5)+(a6+a7)); the wave total is

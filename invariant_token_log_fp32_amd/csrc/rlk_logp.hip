@@ -27,7 +27,7 @@
 namespace rlk {
 
 // Vectors per lane per chunk in the streaming loop.
-constexpr int kChunk = 4;
+constexpr int kChunk = 8;
 constexpr int kRowThreads = kShards * kWave;  // 512
 
 // Per-row, per-shard dispatch on the temperature (uniform across the workgroup).
