@@ -39,6 +39,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_logp_full_8192x152576.jso
 KERNEL_SOURCES = [
     os.path.join(ROOT, "invariant_token_log_fp32_amd", "csrc", "rlk_logp.hip"),
     os.path.join(ROOT, "invariant_token_log_fp32_amd", "csrc", "logp_device.hpp"),
+    os.path.join(ROOT, "invariant_token_log_fp32_amd", "csrc", "support.hpp"),
 ]
 
 
@@ -201,12 +202,12 @@ def main():
         pp = torch.full((w.n_rows,), 0.95, dtype=torch.float32, device=dev)
         pol = torch.empty(w.n_rows, dtype=torch.float32, device=dev)
         ref = torch.empty(w.n_rows, dtype=torch.float32, device=dev)
-        wsn = torch.empty(rlk.workspace_bytes(w.n_rows, w.vocab_padded, w.vocab_real, nucleus=True),
-                          dtype=torch.uint8, device=dev)
+        need_n = rlk.workspace_bytes(w.n_rows, w.vocab_padded, w.vocab_real, groups=args.groups, nucleus=True)
+        wsn = torch.empty(need_n, dtype=torch.uint8, device=dev) if need_n else None
 
         def nstep(i, lgs=bufs, t=temp, p=pp, k=pk, target=tg):
-            rlk.logp_nucleus(lgs[i % 2], t, p, k, target, vocab_real=w.vocab_real, policy_out=pol, ref_out=ref,
-                             workspace=wsn)
+            rlk.logp_nucleus(lgs[i % 2], t, p, k, target, vocab_real=w.vocab_real, groups=args.groups,
+                             policy_out=pol, ref_out=ref, workspace=wsn)
 
         _, ms_n = time_calls(nstep, 10, 2)
         ab = bytes_nucleus(w.n_rows, w.vocab_real)

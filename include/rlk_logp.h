@@ -119,7 +119,8 @@ int32_t rlk_logp_full(const uint16_t* logits, int64_t n_rows, const rlk_vocab_la
  *                   [1, vocab_real]).
  *   ref_out[i]    = byte-identical to rlk_logp_full's logp_out[i].
  *   top_p  [n_rows] float32;  top_k [n_rows] int32.
- *   workspace      rlk_logp_workspace_bytes(n_rows, layout, 1) bytes, 16-byte aligned.
+ *   workspace      rlk_logp_workspace_bytes(n_rows, layout, 1) bytes, 16-byte
+ *                  aligned; may be NULL when that size is 0 (groups == 1).
  * Greedy rows (temperature 0) put a point mass on the lowest-index maximum for
  * both outputs. The support decision is taken on integer masses, so it is the
  * same for any batch or grouping. */
@@ -128,8 +129,9 @@ int32_t rlk_logp_nucleus(const uint16_t* logits, int64_t n_rows, const rlk_vocab
                          const int64_t* target, float* policy_out, float* ref_out,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of device workspace the calls above need (0 for rlk_logp_full with
- * groups == 1). Returns 0 for an invalid layout or n_rows < 0. */
+/* Bytes of device workspace the calls above need: 0 when groups == 1, else
+ * n_rows * 128 (8 shard summaries of 16 bytes per row), for either entry
+ * point. Returns 0 for an invalid layout or n_rows < 0. */
 size_t rlk_logp_workspace_bytes(int64_t n_rows, const rlk_vocab_layout* layout, int32_t nucleus);
 
 /* Static, NUL-terminated description of a status code. */

@@ -187,12 +187,13 @@ def logp_nucleus(logits, temperature, top_p, top_k, target, *, vocab_real: int,
     lay = make_layout(vp, vocab_real, stride, groups)
     lib = load_library()
     need = int(lib.rlk_logp_workspace_bytes(n, ctypes.byref(lay), 1))
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     st = lib.rlk_logp_nucleus(
         logits.data_ptr(), n, ctypes.byref(lay), temperature.data_ptr(), top_p.data_ptr(),
         top_k.data_ptr(), target.data_ptr(), policy_out.data_ptr(), ref_out.data_ptr(),
-        workspace.data_ptr(), workspace.numel(), _stream_handle(stream, dev))
+        workspace.data_ptr() if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0, _stream_handle(stream, dev))
     if st != RLK_OK:
         raise RlkError(st, "rlk_logp_nucleus")
     return policy_out, ref_out

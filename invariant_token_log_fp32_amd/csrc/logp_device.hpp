@@ -136,8 +136,10 @@ struct ShardAcc {
     m0 = -INFINITY;
   }
 
-  template <int UU>
-  __device__ __forceinline__ void consume(const u32x4 (&v)[UU], float c) {
+  // Consumes UU vectors; hook(x, nvalid[u]) sees each vector's unpacked values
+  // right after their terms are accumulated.
+  template <int UU, typename Hook>
+  __device__ __forceinline__ void consume(const u32x4 (&v)[UU], float c, Hook& hook, const int (&nvalid)[UU]) {
     float x[UU][8];
 #pragma unroll
     for (int u = 0; u < UU; ++u) unpack8(v[u], x[u]);
@@ -162,9 +164,11 @@ struct ShardAcc {
     }
     const float nr = -r;
 #pragma unroll
-    for (int u = 0; u < UU; ++u)
+    for (int u = 0; u < UU; ++u) {
 #pragma unroll
       for (int p = 0; p < 8; ++p) acc[p] += __builtin_amdgcn_exp2f(fmaf(x[u][p], c, nr));
+      hook(x[u], nvalid[u]);
+    }
   }
 
   __device__ __forceinline__ float lane_total() const {
@@ -183,19 +187,31 @@ __device__ __forceinline__ void load_chunk(const u32x4* __restrict__ base, int f
   }
 }
 
+// Per-vector observer called by the streaming pass with each vector's 8
+// values (float32 widenings of the BF16 columns, in column order) and the
+// number of them that are real columns (8, the tail count, or 0).
+struct NoHook {
+  __device__ __forceinline__ void operator()(const float (&)[8], int) const {}
+};
+
 // One pass over the shard with the state machine above.
-template <int U, bool kExactMax>
+template <int U, bool kExactMax, typename Hook = NoHook>
 __device__ __forceinline__ void shard_pass(const u32x4* __restrict__ base, int nfull, int tail, int lane,
-                                           float c, ShardAcc<kExactMax>& st) {
+                                           float c, ShardAcc<kExactMax>& st, Hook& hook) {
   for (int first = 0; first < nfull; first += U * kWave) {
     u32x4 v[U];
     load_chunk<U>(base, first, nfull, lane, v);
-    st.template consume<U>(v, c);
+    int nvalid[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) nvalid[u] = (first + u * kWave + lane < nfull) ? 8 : 0;
+    st.template consume<U>(v, c, hook, nvalid);
   }
   if (tail) {
+    const bool owner = (lane == (nfull & (kWave - 1)));
     u32x4 v[1];
-    v[0] = (lane == (nfull & (kWave - 1))) ? mask_tail(base[nfull], tail) : neg_inf_vec();
-    st.template consume<1>(v, c);
+    v[0] = owner ? mask_tail(base[nfull], tail) : neg_inf_vec();
+    const int nvalid[1] = {owner ? tail : 0};
+    st.template consume<1>(v, c, hook, nvalid);
   }
 }
 
@@ -226,8 +242,9 @@ __device__ __forceinline__ float shard_exact_max(const u32x4* __restrict__ base,
 // Summary of the shard whose real columns are [col0, col0 + ncols) of `row`,
 // for a row with valid temperature T > 0 (c = fl32(log2(e) / T)).
 // Must be called by all 64 lanes of a wave.
-template <int U, bool kExactMax>
-__device__ ShardSummary summarize_shard(const uint16_t* __restrict__ row, int col0, int ncols, float c) {
+template <int U, bool kExactMax, typename Hook = NoHook>
+__device__ __forceinline__ ShardSummary summarize_shard(const uint16_t* __restrict__ row, int col0, int ncols, float c,
+                                                        Hook& hook) {
   const int lane = threadIdx.x & (kWave - 1);
   const u32x4* __restrict__ base = reinterpret_cast<const u32x4*>(row + col0);
   const int nfull = ncols >> 3;
@@ -235,7 +252,7 @@ __device__ ShardSummary summarize_shard(const uint16_t* __restrict__ row, int co
 
   ShardAcc<kExactMax> st;
   st.init();
-  shard_pass<U, kExactMax>(base, nfull, tail, lane, c, st);
+  shard_pass<U, kExactMax>(base, nfull, tail, lane, c, st, hook);
   float total = wave_sum(st.lane_total());
   float r = st.r;
   float m = kExactMax ? wave_max(st.mx) : st.m0;
@@ -247,7 +264,8 @@ __device__ ShardSummary summarize_shard(const uint16_t* __restrict__ row, int co
     st2.init();
     st2.r = (mexact == INFINITY) ? NAN : ref_exponent(mexact, c);
     st2.have_ref = true;
-    shard_pass<U, false>(base, nfull, tail, lane, c, st2);
+    NoHook none;
+    shard_pass<U, false>(base, nfull, tail, lane, c, st2, none);
     total = wave_sum(st2.lane_total());
     r = st2.r;
     m = mexact;
@@ -263,7 +281,7 @@ __device__ ShardSummary summarize_shard(const uint16_t* __restrict__ row, int co
 
 // Greedy (T == 0) summary: exact maximum, its lowest column, and a NaN mark
 // when the shard holds NaN or +inf.
-__device__ ShardSummary summarize_shard_greedy(const uint16_t* __restrict__ row, int col0, int ncols) {
+__device__ __forceinline__ ShardSummary summarize_shard_greedy(const uint16_t* __restrict__ row, int col0, int ncols) {
   const int lane = threadIdx.x & (kWave - 1);
   float m = -INFINITY;
   bool bad = false;

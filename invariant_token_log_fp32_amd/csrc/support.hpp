@@ -1,0 +1,801 @@
+// Top-k / top-p support and policy logprob for one row (one 512-thread workgroup).
+//
+// Passages: RL-Kernel page "Configurable H100 consistency runs": sampling
+// paragraph (top-p in (0, 1], top-k -1 or 1..real vocabulary, support over the
+// real vocabulary), mode/KL paragraph (the policy logprob keeps its actual
+// top-p/top-k support), command examples (top-k independent of top-p).
+//
+// Semantics (value thresholds, ties kept): classes are the distinct BF16
+// values of the row (-0 folded into +0), in decreasing order. top-k keeps the
+// classes down to the first one whose cumulative count reaches k; top-p then
+// keeps, among those, the classes down to the first one whose cumulative mass
+// reaches p times their total.
+//
+// Masses are integers: a token of value x weighs floor(2^(x*c - R) * 2^40) with
+// c = fl32(log2(e)/T) and R = ceil(fl32(M*c)) for the exact row maximum M; a
+// class weighs its count times that. Integer sums are exact and order-free, so
+// the support does not depend on the schedule of any atomic; the test
+// "cumulative >= p * Z" is evaluated exactly as cumulative >= ceil(p * Z).
+//
+// Fast path: every token is counted per compressed 16-bit rank (LDS u32
+// atomics) in a fixed window of 16384 ranks that covers every BF16 value from
+// -1.82e19 to 65536 with magnitude at least 2^-24 (the rank keeps the order of
+// the values; -inf tokens are counted apart, mass 0). With groups == 1 the
+// shard-waves count while they stream the row for the reference logprob, so
+// the support costs no extra pass; otherwise one pass builds it. The row
+// maximum is the top non-empty rank, class masses are count * weight, and
+// the thresholds come from prefix sums over the window.
+// General path, for rows with a token outside the window (including any
+// |x| < 2^-24): an exact-maximum pass, then a 4096-bin histogram of
+// (count, mass) over key >> 4, then the 16 keys of each boundary bin, each
+// from another pass over the row. Both paths produce the same integers and
+// therefore the same output bytes.
+#pragma once
+
+#include "logp_device.hpp"
+
+namespace rlk {
+
+constexpr int kNucThreads = 512;
+constexpr int kNucWaves = kNucThreads / kWave;
+constexpr int kBinsA = 4096;
+constexpr int kSub = 16;
+constexpr int kWin = 16384;
+constexpr int kWinPerThread = kWin / kNucThreads;  // 32
+constexpr uint32_t kWinHi = 0x6081u;               // rank of 65536.0: window slot 0
+constexpr uint32_t kTinyExp = 103;                 // biased exponent: |x| < 2^-24
+constexpr uint32_t kNegInfBits = 0xFF80u;
+
+typedef unsigned long long u64;
+
+// Monotone 16-bit key of a BF16 pattern (-0 folded into +0).
+__device__ __forceinline__ uint32_t key16(uint32_t b) {
+  b = (b == 0x8000u) ? 0u : b;
+  return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+
+// Compressed rank of a BF16 pattern with |x| >= 2^-24, finite: negative values
+// rank 0xFFFF - b (at most 0x4C7F), positive values b + 0x1901 (at least
+// 0x4C81); the order of the ranks is the order of the values.
+__device__ __forceinline__ uint32_t crank16(uint32_t b) { return (b & 0x8000u) ? (0xFFFFu - b) : (b + 0x1901u); }
+
+// Inverse of crank16.
+__device__ __forceinline__ uint32_t crank_bits(uint32_t r) { return (r < 0x4C80u) ? (0xFFFFu - r) : (r - 0x1901u); }
+
+// Window slot of a BF16 pattern (kWinHi - rank), or kWin (the trash slot) for
+// -inf, NaN, +-inf, |x| < 2^-24 and values outside the window.
+__device__ __forceinline__ uint32_t window_slot(uint32_t b) {
+  const uint32_t ex = b & 0x7F80u;
+  const bool normal = (ex - (kTinyExp << 7)) < (0x7F80u - (kTinyExp << 7));
+  const uint32_t idx = kWinHi - crank16(b);
+  return (normal && idx < static_cast<uint32_t>(kWin)) ? idx : static_cast<uint32_t>(kWin);
+}
+
+// floor(w * 2^40) for 0 <= w < 2^24, from the float's bits.
+__device__ __forceinline__ u64 fixed40(float w) {
+  const uint32_t u = __float_as_uint(w);
+  const uint32_t e = u >> 23;
+  const u64 m = static_cast<u64>((u & 0x7FFFFFu) | 0x800000u);
+  const int sh = static_cast<int>(e) - 110;
+  if (e == 0 || sh <= -24) return 0ull;
+  return sh >= 0 ? (m << sh) : (m >> (-sh));
+}
+
+__device__ __forceinline__ u64 weight(uint32_t b, float c, float nr) {
+  return fixed40(__builtin_amdgcn_exp2f(fmaf(__uint_as_float(b << 16), c, nr)));
+}
+
+// ceil(p * z) for p in (0, 1) given as a float32, exactly.
+__device__ __forceinline__ u64 ceil_mul(float p, u64 z) {
+  const uint32_t u = __float_as_uint(p);
+  const uint32_t e = u >> 23;
+  const uint32_t mant = (e == 0) ? (u & 0x7FFFFFu) : ((u & 0x7FFFFFu) | 0x800000u);
+  const int sh = (e == 0) ? 149 : (150 - static_cast<int>(e));  // p = mant * 2^-sh
+  const unsigned __int128 a = static_cast<unsigned __int128>(mant) * z;
+  if (sh >= 127) return a > 0 ? 1ull : 0ull;
+  const unsigned __int128 one = 1;
+  return static_cast<u64>((a + ((one << sh) - 1)) >> sh);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const T o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_total(T v) {
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+struct NucGeneral {
+  uint32_t cnt[kBinsA];
+  u64 mass[kBinsA];
+  uint32_t sub_cnt[kSub];
+  u64 sub_mass[kSub];
+};
+
+struct NucLds {
+  ShardSummary sm[kShards];
+  // row state, written by thread 0 before the support search
+  int search;
+  int k_active;
+  int p_active;
+  int64_t k;
+  float p;
+  float c;
+  float R;
+  // block reductions
+  uint32_t red_u32[kNucWaves][2];
+  u64 red_u64[kNucWaves];
+  int red_flag[kNucWaves];
+  // search results
+  int fast_ok;
+  int jk;            // fast: class index of the top-k boundary; general: key inside bk
+  uint32_t cnt_k;    // cumulative count through the top-k boundary
+  u64 z_k;           // mass of the top-k set
+  int kappa;         // support: fast = last kept class index, general = smallest kept key
+  uint32_t cnt_s;
+  u64 z_s;
+  // general path scan state
+  int bk;
+  uint32_t rc;
+  u64 rm;
+  int scan_bin;
+  uint32_t scan_cnt_above;
+  u64 scan_mass_above;
+  union {
+    uint32_t win[kWin + 1];  // + trash slot
+    NucGeneral gen;
+  } u;
+};
+
+// Applies f(bits) to every real column of the row (all threads of the block).
+// Thread t owns vectors t, t + 512, ...; each iteration issues kPassLoads
+// independent 128-bit loads before consuming them.
+constexpr int kPassLoads = 4;
+
+template <typename F>
+__device__ __forceinline__ void row_pass(const uint16_t* __restrict__ rowp, int64_t vocab_real, F f) {
+  const u32x4* __restrict__ base = reinterpret_cast<const u32x4*>(rowp);
+  const int nvec = static_cast<int>(vocab_real >> 3);
+  const int tail = static_cast<int>(vocab_real & 7);
+  for (int v0 = threadIdx.x; v0 < nvec; v0 += kNucThreads * kPassLoads) {
+    u32x4 w[kPassLoads];
+#pragma unroll
+    for (int u = 0; u < kPassLoads; ++u) {
+      const int vi = v0 + u * kNucThreads;
+      w[u] = (vi < nvec) ? base[vi] : neg_inf_vec();
+    }
+#pragma unroll
+    for (int u = 0; u < kPassLoads; ++u) {
+      if (v0 + u * kNucThreads < nvec) {
+        const uint32_t ws4[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          f(ws4[e] & 0xFFFFu);
+          f(ws4[e] >> 16);
+        }
+      }
+    }
+  }
+  if (tail && threadIdx.x == 0) {
+    for (int e = 0; e < tail; ++e) f(static_cast<uint32_t>(rowp[nvec * 8 + e]));
+  }
+}
+
+// As row_pass, but hands whole 16-byte vectors (4 words, 8 values in column
+// order) to fv; the partial tail vector's values go one by one to fe.
+template <typename FV, typename FE>
+__device__ __forceinline__ void row_pass_vec(const uint16_t* __restrict__ rowp, int64_t vocab_real, FV fv, FE fe) {
+  const u32x4* __restrict__ base = reinterpret_cast<const u32x4*>(rowp);
+  const int nvec = static_cast<int>(vocab_real >> 3);
+  const int tail = static_cast<int>(vocab_real & 7);
+  const int step = kNucThreads * kPassLoads;
+  const int nmain = (nvec / step) * step;
+  for (int v0 = threadIdx.x; v0 < nmain; v0 += step) {  // every load in range
+    u32x4 w[kPassLoads];
+#pragma unroll
+    for (int u = 0; u < kPassLoads; ++u) w[u] = base[v0 + u * kNucThreads];
+#pragma unroll
+    for (int u = 0; u < kPassLoads; ++u) {
+      const uint32_t ws4[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+      fv(ws4);
+    }
+  }
+  for (int v = nmain + threadIdx.x; v < nvec; v += kNucThreads) {
+    const u32x4 w = base[v];
+    const uint32_t ws4[4] = {w.x, w.y, w.z, w.w};
+    fv(ws4);
+  }
+  if (tail && threadIdx.x == 0) {
+    for (int e = 0; e < tail; ++e) fe(static_cast<uint32_t>(rowp[nvec * 8 + e]));
+  }
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+// Window slots of the two BF16 values packed in one 32-bit word, computed on
+// 16-bit integer lane pairs (low half = first value):
+//   negative b: slot = b - 0x9F7E, in the window iff slot - 0x1402 <= 0x2BFD
+//   positive b: slot = 0x4780 - b, in the window iff slot <= 0x1400
+// `outside` is nonzero iff a half lies outside the window; halves inside get
+// exactly window_slot() (checked against it on all 65536 patterns).
+__device__ __forceinline__ uint32_t window_slots2(uint32_t w, uint32_t& outside) {
+  uint32_t neg, a, b, slot, lo, d, span;
+  asm(
+      "v_pk_ashrrev_i16 %[neg], 15, %[w] op_sel_hi:[0,1]\n\t"
+      "v_pk_sub_u16 %[a], %[w], %[k1]\n\t"
+      "v_pk_sub_u16 %[b], %[k2], %[w]\n\t"
+      "v_bfi_b32 %[slot], %[neg], %[a], %[b]\n\t"
+      "v_and_b32 %[lo], %[k3], %[neg]\n\t"
+      "v_pk_sub_u16 %[d], %[slot], %[lo]\n\t"
+      "v_bfi_b32 %[span], %[neg], %[k4], %[k5]\n\t"
+      "v_pk_sub_u16 %[out], %[d], %[span] clamp"
+      : [neg] "=&v"(neg), [a] "=&v"(a), [b] "=&v"(b), [slot] "=&v"(slot), [lo] "=&v"(lo), [d] "=&v"(d),
+        [span] "=&v"(span), [out] "=&v"(outside)
+      : [w] "v"(w), [k1] "v"(0x9F7E9F7Eu), [k2] "v"(0x47804780u), [k3] "v"(0x14021402u), [k4] "v"(0x2BFD2BFDu),
+        [k5] "v"(0x14001400u));
+  return slot;
+}
+
+// Counts tokens into the window while a pass streams them. Per lane: the
+// number of -inf tokens and whether any other token fell outside the window.
+struct WindowHook {
+  uint32_t* win;
+  uint32_t ninf;
+  bool odd;
+
+  __device__ __forceinline__ explicit WindowHook(uint32_t* w) : win(w), ninf(0), odd(false) {}
+
+  __device__ __forceinline__ void outside(uint32_t b) {
+    if (b == kNegInfBits) {
+      ++ninf;
+    } else {
+      odd = true;
+    }
+  }
+
+  // x: 8 values (float32 widenings of BF16 columns); nvalid of them are real.
+  __device__ __forceinline__ void operator()(const float (&x)[8], int nvalid) {
+    if (nvalid == 8) {
+      bool any_out = false;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        // the two BF16 patterns of columns e, e + 1 as one word (low half = column e)
+        const uint32_t w = __builtin_amdgcn_perm(__float_as_uint(x[e + 1]), __float_as_uint(x[e]), 0x07060302u);
+        uint32_t out;
+        const uint32_t slots = window_slots2(w, out);
+        const bool in = (out == 0u);
+        atomicAdd(&win[in ? (slots & 0xFFFFu) : static_cast<uint32_t>(kWin)], 1u);
+        atomicAdd(&win[in ? (slots >> 16) : static_cast<uint32_t>(kWin)], 1u);
+        any_out |= !in;
+      }
+      if (any_out) {  // rare: a word with a value outside the window went to the trash slot whole
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const uint32_t b0 = __float_as_uint(x[e]) >> 16;
+          const uint32_t b1 = __float_as_uint(x[e + 1]) >> 16;
+          const uint32_t s0 = window_slot(b0);
+          const uint32_t s1 = window_slot(b1);
+          if (s0 == static_cast<uint32_t>(kWin) || s1 == static_cast<uint32_t>(kWin)) {
+            if (s0 == static_cast<uint32_t>(kWin)) {
+              outside(b0);
+            } else {
+              atomicAdd(&win[s0], 1u);
+            }
+            if (s1 == static_cast<uint32_t>(kWin)) {
+              outside(b1);
+            } else {
+              atomicAdd(&win[s1], 1u);
+            }
+          }
+        }
+      }
+    } else {
+      for (int e = 0; e < nvalid; ++e) {
+        const uint32_t b = __float_as_uint(x[e]) >> 16;
+        const uint32_t slot = window_slot(b);
+        if (slot < static_cast<uint32_t>(kWin)) {
+          atomicAdd(&win[slot], 1u);
+        } else {
+          outside(b);
+        }
+      }
+    }
+  }
+
+  // Per-wave totals into L.red_u32[wave][1] (-inf count) and L.red_flag[wave].
+  template <typename Lds>
+  __device__ __forceinline__ void publish(Lds& L) {
+    const uint32_t n = wave_total(ninf);
+    const bool any = __any(odd);
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+      L.red_u32[threadIdx.x / kWave][1] = n;
+      L.red_flag[threadIdx.x / kWave] = any;
+    }
+  }
+};
+
+template <typename Lds>
+__device__ __forceinline__ void window_clear(Lds& L) {
+  for (int i = threadIdx.x; i <= kWin; i += kNucThreads) L.u.win[i] = 0u;
+}
+
+// One pass over the row that fills the window (when the streaming pass did not).
+__device__ __forceinline__ void window_pass(NucLds& L, const uint16_t* __restrict__ rowp, int64_t vocab_real) {
+  WindowHook hook(L.u.win);
+  row_pass_vec(rowp, vocab_real,
+               [&](const uint32_t (&ws4)[4]) {
+                 u32x4 v;
+                 v.x = ws4[0]; v.y = ws4[1]; v.z = ws4[2]; v.w = ws4[3];
+                 float x[8];
+                 unpack8(v, x);
+                 hook(x, 8);
+               },
+               [&](uint32_t b) {
+                 const float x[8] = {__uint_as_float(b << 16), 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                 hook(x, 1);
+               });
+  hook.publish(L);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_min(T v) {
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d, kWave));
+  return v;
+}
+
+// Block-wide inclusive scan of (count, mass) over the 512 threads, in thread
+// order; returns the block totals through tot_c / tot_m. Uses L.red_* (two
+// barriers inside).
+__device__ __forceinline__ void block_incl_scan(NucLds& L, uint32_t& c, u64& m, uint32_t& tot_c, u64& tot_m) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  c = wave_incl_scan<uint32_t>(c, lane);
+  m = wave_incl_scan<u64>(m, lane);
+  if (lane == kWave - 1) {
+    L.red_u32[wv][0] = c;
+    L.red_u64[wv] = m;
+  }
+  __syncthreads();
+  tot_c = 0;
+  tot_m = 0;
+  for (int w = 0; w < kNucWaves; ++w) {
+    const uint32_t wc = L.red_u32[w][0];
+    const u64 wm = L.red_u64[w];
+    if (w < wv) {
+      c += wc;
+      m += wm;
+    }
+    tot_c += wc;
+    tot_m += wm;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Fast path on a filled window (L.red_* hold the hook totals). Returns
+// (block-uniformly) whether it decided the support; on success L.R is set,
+// L.kappa is the last kept class (window slot, or kWin for the -inf class),
+// L.cnt_s / L.z_s the support's count and mass, and thread 0's `tclass` the
+// target's class.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool support_fast(NucLds& L, int64_t vocab_real, uint32_t bt, int& tclass) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const float c = L.c;
+
+  uint32_t ninf_n = 0;
+  bool odd = false;
+  for (int w = 0; w < kNucWaves; ++w) {
+    ninf_n += L.red_u32[w][1];
+    odd |= (L.red_flag[w] != 0);
+  }
+  if (odd) return false;  // block-uniform
+
+  // the row maximum: first non-empty slot (thread t visits t, t + 512, ...)
+  int jtop = kWin;
+  for (int i = kWinPerThread - 1; i >= 0; --i)
+    if (L.u.win[i * kNucThreads + tid]) jtop = i * kNucThreads + tid;
+  jtop = wave_min(jtop);
+  __syncthreads();  // red_* reads above are complete before reuse
+  if (lane == 0) L.red_u32[wv][0] = static_cast<uint32_t>(jtop);
+  __syncthreads();
+  jtop = kWin;
+  for (int w = 0; w < kNucWaves; ++w) jtop = min(jtop, static_cast<int>(L.red_u32[w][0]));
+  if (jtop == kWin) return false;  // no finite token (cannot happen on a searched row)
+  const float m = __uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(jtop)) << 16);
+  const float R = ref_exponent(m, c);
+  const float nr = -R;
+
+  // count and mass of class (slot) j; a term below 2^-42 is 0 in 2^-40 fixed point
+  auto class_at = [&](int j, uint32_t& cj, u64& mj) {
+    cj = L.u.win[j];
+    mj = 0;
+    if (cj) {
+      const float t = fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(j)) << 16), c, nr);
+      if (t >= -42.0f) mj = static_cast<u64>(cj) * fixed40(__builtin_amdgcn_exp2f(t));
+    }
+  };
+
+  // totals (order-free integer sums)
+  uint32_t tc = 0;
+  u64 tm = 0;
+  for (int i = 0; i < kWinPerThread; ++i) {
+    uint32_t cj;
+    u64 mj;
+    class_at(i * kNucThreads + tid, cj, mj);
+    tc += cj;
+    tm += mj;
+  }
+  tc = wave_total(tc);
+  tm = wave_total(tm);
+  __syncthreads();
+  if (lane == 0) {
+    L.red_u32[wv][0] = tc;
+    L.red_u64[wv] = tm;
+  }
+  __syncthreads();
+  uint32_t total_c = 0;
+  u64 total_m = 0;
+  for (int w = 0; w < kNucWaves; ++w) {
+    total_c += L.red_u32[w][0];
+    total_m += L.red_u64[w];
+  }
+  __syncthreads();
+
+  // top-k boundary by count (the -inf class when the window holds fewer than k)
+  int jk = kWin;
+  uint32_t cnt_k = total_c + ninf_n;
+  u64 z_k = total_m;
+  if (L.k_active) {
+    const uint64_t k = static_cast<uint64_t>(L.k);
+    if (static_cast<uint64_t>(total_c) >= k) {
+      uint32_t carry_c = 0;
+      u64 carry_m = 0;
+      for (int r = jtop / kNucThreads; r < kWinPerThread; ++r) {  // rounds of 512 slots, from the top
+        const int j = r * kNucThreads + tid;
+        uint32_t cj;
+        u64 mj;
+        class_at(j, cj, mj);
+        uint32_t ic = cj;
+        u64 im = mj;
+        uint32_t rc;
+        u64 rm;
+        block_incl_scan(L, ic, im, rc, rm);
+        ic += carry_c;
+        im += carry_m;
+        const bool hit = static_cast<uint64_t>(ic) >= k && static_cast<uint64_t>(ic - cj) < k;
+        if (hit) {
+          L.jk = j;
+          L.cnt_k = ic;
+          L.z_k = im;
+        }
+        if (static_cast<uint64_t>(carry_c + rc) >= k) break;  // block-uniform
+        carry_c += rc;
+        carry_m += rm;
+      }
+      __syncthreads();
+      jk = L.jk;
+      cnt_k = L.cnt_k;
+      z_k = L.z_k;
+      __syncthreads();
+    }
+  }
+
+  // top-p boundary by mass inside the top-k set
+  int kappa = jk;
+  uint32_t cnt_s = cnt_k;
+  u64 z_s = z_k;
+  if (L.p_active) {
+    const u64 P = ceil_mul(L.p, z_k);
+    u64 carry_m = 0;
+    uint32_t carry_c = 0;
+    for (int r = jtop / kNucThreads; r < kWinPerThread; ++r) {
+      const int j = r * kNucThreads + tid;
+      uint32_t cj;
+      u64 mj;
+      class_at(j, cj, mj);
+      uint32_t ic = cj;
+      u64 im = mj;
+      uint32_t rc;
+      u64 rm;
+      block_incl_scan(L, ic, im, rc, rm);
+      ic += carry_c;
+      im += carry_m;
+      const bool hit = im >= P && (im - mj) < P && j <= jk;
+      if (hit) {
+        L.kappa = j;
+        L.cnt_s = ic;
+        L.z_s = im;
+      }
+      if (carry_m + rm >= P) break;  // block-uniform
+      carry_c += rc;
+      carry_m += rm;
+    }
+    __syncthreads();
+    kappa = L.kappa;
+    cnt_s = L.cnt_s;
+    z_s = L.z_s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    L.R = R;
+    L.kappa = kappa;
+    L.cnt_s = cnt_s;
+    L.z_s = z_s;
+    tclass = (bt == kNegInfBits) ? kWin : static_cast<int>(window_slot(bt));
+  }
+  __syncthreads();
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// General path (any row whose thresholds are not resolved by the fast path).
+// ---------------------------------------------------------------------------
+
+// Wave 0: scan level-A bins from the top (4095 down to 0) for the first bin
+// where the inclusive cumulative count (by_mass = 0) or mass (by_mass = 1)
+// reaches `thresh`. Bins above L.bk count fully, bin L.bk counts (L.rc, L.rm),
+// bins below L.bk count zero (when L.bk >= 0).
+__device__ __forceinline__ void general_scan(NucLds& L, bool by_mass, u64 thresh) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int bk = L.bk;
+  auto val = [&](int b, uint32_t& cc, u64& mm) {
+    if (bk < 0 || b > bk) {
+      cc = L.u.gen.cnt[b];
+      mm = L.u.gen.mass[b];
+    } else if (b == bk) {
+      cc = L.rc;
+      mm = L.rm;
+    } else {
+      cc = 0;
+      mm = 0;
+    }
+  };
+  const int hi = kBinsA - 1 - kWave * lane;
+  uint32_t tc = 0;
+  u64 tm = 0;
+  for (int i = 0; i < kWave; ++i) {
+    const int b = hi - ((i + lane) & (kWave - 1));  // rotated to spread LDS banks
+    uint32_t cc;
+    u64 mm;
+    val(b, cc, mm);
+    tc += cc;
+    tm += mm;
+  }
+  const uint32_t ic = wave_incl_scan<uint32_t>(tc, lane);
+  const u64 im = wave_incl_scan<u64>(tm, lane);
+  const bool reach = by_mass ? (im >= thresh) : (static_cast<u64>(ic) >= thresh);
+  const u64 ball = __ballot(reach);
+  const int Ln = ball ? __ffsll(static_cast<long long>(ball)) - 1 : kWave - 1;
+  const uint32_t ec = __shfl(ic - tc, Ln, kWave);
+  const u64 em = __shfl(im - tm, Ln, kWave);
+  const int b = kBinsA - 1 - kWave * Ln - lane;
+  uint32_t cc;
+  u64 mm;
+  val(b, cc, mm);
+  const uint32_t jc = wave_incl_scan<uint32_t>(cc, lane);
+  const u64 jm = wave_incl_scan<u64>(mm, lane);
+  const bool reach2 = by_mass ? (em + jm >= thresh) : (static_cast<u64>(ec + jc) >= thresh);
+  const u64 ball2 = __ballot(reach2);
+  const int J = ball2 ? __ffsll(static_cast<long long>(ball2)) - 1 : kWave - 1;
+  if (lane == J) {
+    L.scan_bin = b;
+    L.scan_cnt_above = ec + jc - cc;
+    L.scan_mass_above = em + jm - mm;
+  }
+}
+
+__device__ __forceinline__ void general_sub(NucLds& L, const uint16_t* __restrict__ rowp, int64_t vocab_real, uint32_t bin) {
+  const float c = L.c;
+  const float nr = -L.R;
+  if (threadIdx.x < kSub) {
+    L.u.gen.sub_cnt[threadIdx.x] = 0;
+    L.u.gen.sub_mass[threadIdx.x] = 0;
+  }
+  __syncthreads();
+  row_pass(rowp, vocab_real, [&](uint32_t b) {
+    const uint32_t key = key16(b);
+    if ((key >> 4) != bin) return;
+    atomicAdd(&L.u.gen.sub_cnt[key & 15u], 1u);
+    const u64 q = weight(b, c, nr);
+    if (q) atomicAdd(&L.u.gen.sub_mass[key & 15u], q);
+  });
+  __syncthreads();
+}
+
+// On return L.R is set, L.kappa is the smallest kept key16, L.cnt_s / L.z_s
+// the support's count and mass.
+__device__ __forceinline__ void support_general(NucLds& L, const uint16_t* __restrict__ rowp, int64_t vocab_real) {
+  const int tid = threadIdx.x;
+  const float c = L.c;
+  // exact row maximum -> reference exponent R
+  float mx = -INFINITY;
+  row_pass(rowp, vocab_real, [&](uint32_t b) { mx = fmaxf(mx, __uint_as_float(b << 16)); });
+  mx = wave_max(mx);
+  if ((tid & (kWave - 1)) == 0) L.red_u32[tid / kWave][0] = __float_as_uint(mx);
+  __syncthreads();
+  for (int w = 0; w < kNucWaves; ++w) mx = fmaxf(mx, __uint_as_float(L.red_u32[w][0]));
+  const float nr = -ref_exponent(mx, c);
+  if (tid == 0) L.R = -nr;
+  for (int i = tid; i < kBinsA; i += kNucThreads) {
+    L.u.gen.cnt[i] = 0;
+    L.u.gen.mass[i] = 0;
+  }
+  if (tid == 0) {
+    L.bk = -1;
+    L.rc = 0;
+    L.rm = 0;
+  }
+  __syncthreads();
+  row_pass(rowp, vocab_real, [&](uint32_t b) {
+    const uint32_t bin = key16(b) >> 4;
+    atomicAdd(&L.u.gen.cnt[bin], 1u);
+    const u64 q = weight(b, c, nr);
+    if (q) atomicAdd(&L.u.gen.mass[bin], q);
+  });
+  __syncthreads();
+
+  int kappa = 0;
+  uint32_t cnt_s = 0;
+  u64 z_k = 0;
+  if (L.k_active) {
+    if (tid < kWave) general_scan(L, false, static_cast<u64>(L.k));
+    __syncthreads();
+    const int bk = L.scan_bin;
+    const uint32_t ca = L.scan_cnt_above;
+    const u64 ma = L.scan_mass_above;
+    general_sub(L, rowp, vocab_real, static_cast<uint32_t>(bk));
+    if (tid == 0) {
+      uint32_t run = ca;
+      u64 rm = 0;
+      int j = kSub - 1;
+      for (; j >= 0; --j) {
+        run += L.u.gen.sub_cnt[j];
+        rm += L.u.gen.sub_mass[j];
+        if (static_cast<int64_t>(run) >= L.k) break;
+      }
+      j = j < 0 ? 0 : j;
+      L.bk = bk;
+      L.jk = j;
+      L.rc = run - ca;
+      L.rm = rm;
+      L.scan_cnt_above = ca;
+      L.scan_mass_above = ma;
+    }
+    __syncthreads();
+    kappa = L.bk * kSub + L.jk;
+    cnt_s = L.scan_cnt_above + L.rc;
+    z_k = L.scan_mass_above + L.rm;
+  } else {
+    if (tid < kWave) general_scan(L, false, ~0ull);  // unreachable: lands on bin 0
+    __syncthreads();
+    cnt_s = L.scan_cnt_above + L.u.gen.cnt[0];
+    z_k = L.scan_mass_above + L.u.gen.mass[0];
+    kappa = 0;
+  }
+  u64 z_s = z_k;
+  if (L.p_active) {
+    const u64 thresh = ceil_mul(L.p, z_k);
+    __syncthreads();
+    if (tid < kWave) general_scan(L, true, thresh);
+    __syncthreads();
+    const int bp = L.scan_bin;
+    const uint32_t ca = L.scan_cnt_above;
+    const u64 ma = L.scan_mass_above;
+    const bool same = L.k_active && bp == L.bk;
+    if (!same) {
+      __syncthreads();
+      general_sub(L, rowp, vocab_real, static_cast<uint32_t>(bp));
+    }
+    const int jlo = same ? L.jk : 0;
+    uint32_t run_c = ca;
+    u64 run_m = ma;
+    int j = kSub - 1;
+    for (; j > jlo; --j) {
+      run_c += L.u.gen.sub_cnt[j];
+      run_m += L.u.gen.sub_mass[j];
+      if (run_m >= thresh) break;
+    }
+    if (j == jlo) {
+      run_c += L.u.gen.sub_cnt[j];
+      run_m += L.u.gen.sub_mass[j];
+    }
+    kappa = bp * kSub + j;
+    cnt_s = run_c;
+    z_s = run_m;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    L.kappa = kappa;
+    L.cnt_s = cnt_s;
+    L.z_s = z_s;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Whole-row driver: L.sm must hold the row's 8 shard summaries; when
+// `window_built` the window and the hook totals are already filled (the
+// streaming pass counted the row). Writes ref_out[row] and policy_out[row].
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restrict__ rowp, int64_t row,
+                                            int64_t vocab_real, float t, float p, int64_t k, int64_t tg,
+                                            bool window_built, float* __restrict__ policy_out,
+                                            float* __restrict__ ref_out) {
+  const int tid = threadIdx.x;
+  float ref = NAN, zt = NAN;
+  uint32_t bt = 0;
+  if (tid == 0) {
+    const bool tok = (tg >= 0) && (tg < vocab_real);
+    if (tok) bt = rowp[tg];
+    const float xt = __uint_as_float(bt << 16);
+    const RowMerge mr = merge_row(L.sm, t, tok, tg, xt);
+    ref = mr.logp;
+    ref_out[row] = ref;
+    const bool p_ok = (p > 0.0f) && (p <= 1.0f);
+    const bool k_ok = (k == -1) || (k >= 1 && k <= vocab_real);
+    L.search = 0;
+    float pol = ref;
+    if (!mr.ok || !p_ok || !k_ok) {
+      pol = NAN;
+    } else if (t != 0.0f) {
+      const bool ka = (k != -1) && (k < vocab_real);
+      const bool pa = (p < 1.0f);
+      if (ka || pa) {
+        L.search = 1;
+        L.k_active = ka;
+        L.p_active = pa;
+        L.k = k;
+        L.p = p;
+        L.c = kLog2e / t;
+        zt = xt / t;
+      }
+    }
+    if (!L.search) policy_out[row] = pol;
+  }
+  __syncthreads();
+  if (!L.search) return;
+
+  if (!window_built) {
+    window_clear(L);
+    __syncthreads();
+    window_pass(L, rowp, vocab_real);
+    __syncthreads();
+  }
+  int tclass = 0;
+  const bool fast = support_fast(L, vocab_real, bt, tclass);
+  bool in_support;
+  if (!fast) {
+    __syncthreads();
+    support_general(L, rowp, vocab_real);
+    in_support = (tid == 0) && static_cast<int>(key16(bt)) >= L.kappa;
+  } else {
+    in_support = (tid == 0) && tclass <= L.kappa;
+  }
+  if (tid == 0) {
+    float pol;
+    if (!in_support) {
+      pol = -INFINITY;
+    } else if (static_cast<int64_t>(L.cnt_s) == vocab_real) {
+      pol = ref;
+    } else {
+      const double lse_s = (static_cast<double>(L.R) + (log2(static_cast<double>(L.z_s)) - 40.0)) * kLn2;
+      pol = static_cast<float>(static_cast<double>(zt) - lse_s);
+    }
+    policy_out[row] = pol;
+  }
+}
+
+}  // namespace rlk

@@ -85,7 +85,8 @@ def test_full_rejects_bad_arguments(lib, kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(p=None), NULL), (dict(k=None), NULL), (dict(pol=None), NULL), (dict(ref=None), NULL),
     (dict(p=P + 2), ALIGN), (dict(k=P + 1), ALIGN), (dict(pol=P + 2), ALIGN), (dict(ref=P + 2), ALIGN),
-    (dict(ws=None), WS), (dict(wsb=4 * 8 * 16 - 1), WS), (dict(ws=P + 4), ALIGN), (dict(logits=None), NULL),
+    (dict(ws=None, L=lay(groups=2)), WS), (dict(wsb=4 * 8 * 16 - 1, L=lay(groups=2)), WS),
+    (dict(ws=P + 4, L=lay(groups=2)), ALIGN), (dict(logits=None), NULL),
     (dict(L=lay(groups=5)), GROUPS), (dict(n=-3), SHAPE), (dict(L=lay(vr=2000)), SHAPE),
 ])
 def test_nucleus_rejects_bad_arguments(lib, kw, code):
@@ -96,12 +97,15 @@ def test_workspace_sizes(lib):
     assert rlk.workspace_bytes(8192, 152576, 151936) == 0
     for g in (2, 4, 8):
         assert rlk.workspace_bytes(8192, 152576, 151936, groups=g) == 8192 * 8 * 16
-    assert rlk.workspace_bytes(8192, 152576, 151936, nucleus=True) == 8192 * 8 * 16
+    assert rlk.workspace_bytes(8192, 152576, 151936, nucleus=True) == 0
+    assert rlk.workspace_bytes(8192, 152576, 151936, groups=4, nucleus=True) == 8192 * 8 * 16
     assert rlk.workspace_bytes(-1, 152576, 151936) == 0
     assert rlk.workspace_bytes(10, 152576, 151936, groups=3) == 0
     L = lay()
     assert lib.rlk_logp_workspace_bytes(5, None, 0) == 0
-    assert lib.rlk_logp_workspace_bytes(5, ctypes.byref(L), 1) == 5 * 128
+    assert lib.rlk_logp_workspace_bytes(5, ctypes.byref(L), 1) == 0
+    L2 = lay(groups=2)
+    assert lib.rlk_logp_workspace_bytes(5, ctypes.byref(L2), 1) == 5 * 128
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
