@@ -48,7 +48,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Summary of one shard of one row.
 //   value rows:  r = reference exponent (integer-valued), l = sum of 2^(x*c - r),
-//                m = exact maximum when requested (else the first-chunk maximum).
+//                m = maximum of the first chunk holding a value above -inf (the
+//                exact shard maximum when the shard was recomputed).
 //   greedy rows: r = 0, l = 0 (NaN if the shard holds NaN or +inf), m = exact
 //                maximum, first = lowest column holding m (-1 if none).
 struct alignas(16) ShardSummary {
@@ -119,12 +120,10 @@ __device__ __forceinline__ u32x4 neg_inf_vec() {
 }
 
 // Wave-level streaming state for one shard.
-template <bool kExactMax>
 struct ShardAcc {
   float acc[8];
   float r;         // reference exponent (wave-uniform)
   bool have_ref;   // wave-uniform
-  float mx;        // lane running exact maximum (kExactMax)
   float m0;        // wave maximum of the chunk that fixed r
 
   __device__ __forceinline__ void init() {
@@ -132,7 +131,6 @@ struct ShardAcc {
     for (int p = 0; p < 8; ++p) acc[p] = 0.0f;
     r = 0.0f;
     have_ref = false;
-    mx = -INFINITY;
     m0 = -INFINITY;
   }
 
@@ -143,12 +141,6 @@ struct ShardAcc {
     float x[UU][8];
 #pragma unroll
     for (int u = 0; u < UU; ++u) unpack8(v[u], x[u]);
-    if (kExactMax) {
-#pragma unroll
-      for (int u = 0; u < UU; ++u)
-#pragma unroll
-        for (int p = 0; p < 8; ++p) mx = fmaxf(mx, x[u][p]);
-    }
     if (!have_ref) {  // wave-uniform branch, taken until a value above -inf appears
       float cm = -INFINITY;
 #pragma unroll
@@ -195,9 +187,9 @@ struct NoHook {
 };
 
 // One pass over the shard with the state machine above.
-template <int U, bool kExactMax, typename Hook = NoHook>
+template <int U, typename Hook = NoHook>
 __device__ __forceinline__ void shard_pass(const u32x4* __restrict__ base, int nfull, int tail, int lane,
-                                           float c, ShardAcc<kExactMax>& st, Hook& hook) {
+                                           float c, ShardAcc& st, Hook& hook) {
   for (int first = 0; first < nfull; first += U * kWave) {
     u32x4 v[U];
     load_chunk<U>(base, first, nfull, lane, v);
@@ -242,7 +234,7 @@ __device__ __forceinline__ float shard_exact_max(const u32x4* __restrict__ base,
 // Summary of the shard whose real columns are [col0, col0 + ncols) of `row`,
 // for a row with valid temperature T > 0 (c = fl32(log2(e) / T)).
 // Must be called by all 64 lanes of a wave.
-template <int U, bool kExactMax, typename Hook = NoHook>
+template <int U, typename Hook = NoHook>
 __device__ __forceinline__ ShardSummary summarize_shard(const uint16_t* __restrict__ row, int col0, int ncols, float c,
                                                         Hook& hook) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -250,22 +242,22 @@ __device__ __forceinline__ ShardSummary summarize_shard(const uint16_t* __restri
   const int nfull = ncols >> 3;
   const int tail = ncols & 7;
 
-  ShardAcc<kExactMax> st;
+  ShardAcc st;
   st.init();
-  shard_pass<U, kExactMax>(base, nfull, tail, lane, c, st, hook);
+  shard_pass<U>(base, nfull, tail, lane, c, st, hook);
   float total = wave_sum(st.lane_total());
   float r = st.r;
-  float m = kExactMax ? wave_max(st.mx) : st.m0;
+  float m = st.m0;
 
   if (!(total < kRestartBound)) {
     // Two-pass recompute: reference from the exact shard maximum.
     const float mexact = shard_exact_max<U>(base, nfull, tail, lane);
-    ShardAcc<false> st2;
+    ShardAcc st2;
     st2.init();
     st2.r = (mexact == INFINITY) ? NAN : ref_exponent(mexact, c);
     st2.have_ref = true;
     NoHook none;
-    shard_pass<U, false>(base, nfull, tail, lane, c, st2, none);
+    shard_pass<U>(base, nfull, tail, lane, c, st2, none);
     total = wave_sum(st2.lane_total());
     r = st2.r;
     m = mexact;

@@ -15,7 +15,7 @@
 //                 support from the exact integer histogram and writes the
 //                 policy logprob.
 //   k_nucleus     groups > 1: the same per-row support search on summaries
-//                 that k_summaries<true> stored in the workspace.
+//                 that k_summaries stored in the workspace.
 // Passages: RL-Kernel page "Configurable H100 consistency runs" (sampling,
 // topology and mode/KL paragraphs; top-k independent of top-p in the command
 // examples) and page "Reproduce and profile the Qwen3-8B TP4/CP2 experiment",
@@ -36,7 +36,7 @@ constexpr int kChunk = 8;
 constexpr int kRowThreads = kShards * kWave;  // 512
 
 // Per-row, per-shard dispatch on the temperature (uniform across the workgroup).
-template <bool kExactMax, typename Hook = NoHook>
+template <typename Hook = NoHook>
 __device__ __forceinline__ ShardSummary summarize_row_shard(const uint16_t* __restrict__ rowp, int shard,
                                                             int shard_width, int64_t vocab_real, float t,
                                                             Hook& hook) {
@@ -56,7 +56,7 @@ __device__ __forceinline__ ShardSummary summarize_row_shard(const uint16_t* __re
   if (ncols == 0) return s;
   if (t == 0.0f) return summarize_shard_greedy(rowp, static_cast<int>(col0), ncols);
   const float c = kLog2e / t;  // IEEE float32 division
-  return summarize_shard<kChunk, kExactMax>(rowp, static_cast<int>(col0), ncols, c, hook);
+  return summarize_shard<kChunk>(rowp, static_cast<int>(col0), ncols, c, hook);
 }
 
 __device__ __forceinline__ float load_target_logit(const uint16_t* __restrict__ rowp, int64_t tg) {
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kRowThreads) void k_full_g1(const uint16_t* __restr
     if (tok) xt = load_target_logit(rowp, tg);
   }
   NoHook none;
-  const ShardSummary s = summarize_row_shard<false>(rowp, wave, shard_width, vocab_real, t, none);
+  const ShardSummary s = summarize_row_shard(rowp, wave, shard_width, vocab_real, t, none);
   if ((threadIdx.x & (kWave - 1)) == 0) sm[wave] = s;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -93,7 +93,6 @@ __global__ __launch_bounds__(kRowThreads) void k_full_g1(const uint16_t* __restr
   }
 }
 
-template <bool kExactMax>
 __global__ __launch_bounds__(kRowThreads) void k_summaries(const uint16_t* __restrict__ logits, int64_t row_stride,
                                                            int shard_width, int64_t vocab_real,
                                                            const float* __restrict__ temperature, int groups,
@@ -105,7 +104,7 @@ __global__ __launch_bounds__(kRowThreads) void k_summaries(const uint16_t* __res
   const uint16_t* __restrict__ rowp = logits + row * row_stride;
   const float t = temperature[row];
   NoHook none;
-  const ShardSummary s = summarize_row_shard<kExactMax>(rowp, shard, shard_width, vocab_real, t, none);
+  const ShardSummary s = summarize_row_shard(rowp, shard, shard_width, vocab_real, t, none);
   if ((threadIdx.x & (kWave - 1)) == 0) ws[row * kShards + shard] = s;
 }
 
@@ -144,15 +143,23 @@ __global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(4, 
   const int wave = threadIdx.x / kWave;
   const uint16_t* __restrict__ rowp = logits + row * row_stride;
   const float t = temperature[row];
-  // the shard-waves build the key histogram while they stream the row
-  window_clear(L);
+  const float p = top_p[row];
+  const int64_t k = top_k[row];
+  if (search_needed(t, p, k, vocab_real)) {
+    // the shard-waves build the key histogram while they stream the row
+    window_clear(L);
+    __syncthreads();
+    WindowHook hook(L.u.win);
+    const ShardSummary s = summarize_row_shard(rowp, wave, shard_width, vocab_real, t, hook);
+    if ((threadIdx.x & (kWave - 1)) == 0) L.sm[wave] = s;
+    hook.publish(L);
+  } else {
+    NoHook none;
+    const ShardSummary s = summarize_row_shard(rowp, wave, shard_width, vocab_real, t, none);
+    if ((threadIdx.x & (kWave - 1)) == 0) L.sm[wave] = s;
+  }
   __syncthreads();
-  WindowHook hook(L.u.win);
-  const ShardSummary s = summarize_row_shard<false>(rowp, wave, shard_width, vocab_real, t, hook);
-  if ((threadIdx.x & (kWave - 1)) == 0) L.sm[wave] = s;
-  hook.publish(L);
-  __syncthreads();
-  nucleus_row(L, rowp, row, vocab_real, t, top_p[row], top_k[row], target[row], true, policy_out, ref_out);
+  nucleus_row(L, rowp, row, vocab_real, t, p, k, target[row], true, policy_out, ref_out);
 }
 
 __global__ __launch_bounds__(kNucThreads) void k_nucleus(const uint16_t* __restrict__ logits, int64_t row_stride,
@@ -246,7 +253,7 @@ int32_t rlk_logp_full(const uint16_t* logits, int64_t n_rows, const rlk_vocab_la
     return launched();
   }
   ShardSummary* ws = static_cast<ShardSummary*>(workspace);
-  k_summaries<false><<<dim3(static_cast<unsigned>(n_rows * G)), dim3(kShards / G * kWave), 0, stream>>>(
+  k_summaries<<<dim3(static_cast<unsigned>(n_rows * G)), dim3(kShards / G * kWave), 0, stream>>>(
       logits, layout->row_stride, S, layout->vocab_real, temperature, G, ws);
   if ((st = launched()) != RLK_OK) return st;
   const unsigned blocks = static_cast<unsigned>((n_rows + 255) / 256);
@@ -280,7 +287,7 @@ int32_t rlk_logp_nucleus(const uint16_t* logits, int64_t n_rows, const rlk_vocab
     return launched();
   }
   ShardSummary* ws = static_cast<ShardSummary*>(workspace);
-  k_summaries<false><<<dim3(static_cast<unsigned>(n_rows * G)), dim3(kShards / G * kWave), 0, stream>>>(
+  k_summaries<<<dim3(static_cast<unsigned>(n_rows * G)), dim3(kShards / G * kWave), 0, stream>>>(
       logits, layout->row_stride, S, layout->vocab_real, temperature, G, ws);
   if ((st = launched()) != RLK_OK) return st;
   k_nucleus<<<dim3(static_cast<unsigned>(n_rows)), dim3(kNucThreads), 0, stream>>>(

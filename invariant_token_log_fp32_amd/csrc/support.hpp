@@ -428,30 +428,27 @@ __device__ __forceinline__ bool support_fast(NucLds& L, int64_t vocab_real, uint
     }
   };
 
-  // totals (order-free integer sums)
-  uint32_t tc = 0;
+  // totals: every real token is in the window or is -inf; masses are summed
+  // in 512-slot rounds from the top and stop once a round starts below
+  // 2^-42 (slots are in decreasing value order, so every later term is 0)
+  const uint32_t total_c = static_cast<uint32_t>(vocab_real) - ninf_n;
   u64 tm = 0;
-  for (int i = 0; i < kWinPerThread; ++i) {
+  for (int r = jtop / kNucThreads; r < kWinPerThread; ++r) {
+    const int jfirst = r * kNucThreads;
+    if (jfirst > jtop &&
+        fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(jfirst)) << 16), c, nr) < -42.0f)
+      break;  // block-uniform
     uint32_t cj;
     u64 mj;
-    class_at(i * kNucThreads + tid, cj, mj);
-    tc += cj;
+    class_at(jfirst + tid, cj, mj);
     tm += mj;
   }
-  tc = wave_total(tc);
   tm = wave_total(tm);
   __syncthreads();
-  if (lane == 0) {
-    L.red_u32[wv][0] = tc;
-    L.red_u64[wv] = tm;
-  }
+  if (lane == 0) L.red_u64[wv] = tm;
   __syncthreads();
-  uint32_t total_c = 0;
   u64 total_m = 0;
-  for (int w = 0; w < kNucWaves; ++w) {
-    total_c += L.red_u32[w][0];
-    total_m += L.red_u64[w];
-  }
+  for (int w = 0; w < kNucWaves; ++w) total_m += L.red_u64[w];
   __syncthreads();
 
   // top-k boundary by count (the -inf class when the window holds fewer than k)
@@ -725,6 +722,15 @@ __device__ __forceinline__ void support_general(NucLds& L, const uint16_t* __res
   __syncthreads();
 }
 
+// Whether a row's policy needs a support search (parameters valid, T > 0, and
+// top-k or top-p active); other rows' policy is the reference or NaN.
+__device__ __forceinline__ bool search_needed(float t, float p, int64_t k, int64_t vocab_real) {
+  const bool p_ok = (p > 0.0f) && (p <= 1.0f);
+  const bool k_ok = (k == -1) || (k >= 1 && k <= vocab_real);
+  const bool active = (k != -1 && k < vocab_real) || (p < 1.0f);
+  return temperature_valid(t) && t != 0.0f && p_ok && k_ok && active;
+}
+
 // ---------------------------------------------------------------------------
 // Whole-row driver: L.sm must hold the row's 8 shard summaries; when
 // `window_built` the window and the hook totals are already filled (the
@@ -750,18 +756,14 @@ __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restric
     float pol = ref;
     if (!mr.ok || !p_ok || !k_ok) {
       pol = NAN;
-    } else if (t != 0.0f) {
-      const bool ka = (k != -1) && (k < vocab_real);
-      const bool pa = (p < 1.0f);
-      if (ka || pa) {
-        L.search = 1;
-        L.k_active = ka;
-        L.p_active = pa;
-        L.k = k;
-        L.p = p;
-        L.c = kLog2e / t;
-        zt = xt / t;
-      }
+    } else if (search_needed(t, p, k, vocab_real)) {
+      L.search = 1;
+      L.k_active = (k != -1) && (k < vocab_real);
+      L.p_active = (p < 1.0f);
+      L.k = k;
+      L.p = p;
+      L.c = kLog2e / t;
+      zt = xt / t;
     }
     if (!L.search) policy_out[row] = pol;
   }
