@@ -224,6 +224,25 @@ def main():
                     "top-k {-1,128}", "entry_point": "rlk_logp_nucleus", "ms_per_step": ms_r,
                     "tokens_per_s": wr.n_rows / (ms_r * 1e-3), "achieved_GBs": ab / (ms_r * 1e-3) / 1e9,
                     "frac": ab / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        # vocabulary-parallel form: 8 ranks, each with its own 8192 x 19072 slice
+        G = 8
+        cols = w.vocab_padded // G
+        slices = [lg_a[:, r * cols:(r + 1) * cols].contiguous() for r in range(G)]
+        summ = torch.empty(rlk.summary_bytes(w.n_rows, w.vocab_padded, w.vocab_real, groups=G) * G,
+                           dtype=torch.uint8, device=dev)
+        per = summ.numel() // G
+        _, ms_ranks = time_calls(lambda i: [rlk.logp_shard_summaries(
+            slices[r], temp, tg, rank=r, groups=G, vocab_real=w.vocab_real, vocab_padded=w.vocab_padded,
+            out=summ[r * per:(r + 1) * per]) for r in range(G)], 10, 2)
+        _, ms_merge = time_calls(lambda i: rlk.logp_merge(
+            summ, temp, tg, n_rows=w.n_rows, groups=G, vocab_real=w.vocab_real, vocab_padded=w.vocab_padded,
+            out=out), 20, 2)
+        rank_bytes = alg / G
+        sec.append({"workload": "vocabulary-parallel: 8 ranks x (8192 x 19072 slice) shard summaries, then merge",
+                    "entry_point": "rlk_logp_shard_summaries + rlk_logp_merge",
+                    "ms_per_rank": ms_ranks / G, "ms_merge": ms_merge,
+                    "rank_achieved_GBs": rank_bytes / (ms_ranks / G * 1e-3) / 1e9,
+                    "frac": rank_bytes / (ms_ranks / G * 1e-3) / 1e9 / HBM_PEAK_GBS})
         result["secondary"] = sec
 
     if not args.no_cpu_baseline:

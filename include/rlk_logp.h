@@ -129,9 +129,50 @@ int32_t rlk_logp_nucleus(const uint16_t* logits, int64_t n_rows, const rlk_vocab
                          const int64_t* target, float* policy_out, float* ref_out,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of device workspace the calls above need: 0 when groups == 1, else
- * n_rows * 128 (8 shard summaries of 16 bytes per row), for either entry
- * point. Returns 0 for an invalid layout or n_rows < 0. */
+/* Vocabulary-parallel form [REPRO-CANON], [CFG-TOPOLOGY]: with `groups` = G
+ * ranks, rank r holds the columns [r*C, (r+1)*C) of every row, C = 8/G shards
+ * of width vocab_padded/8 (the canonical partition does not depend on G).
+ *
+ * rlk_logp_shard_summaries: rank `rank` reduces its slice to its 8/G shard
+ * summaries.
+ *   logits_slice  [n_rows * slice_stride] BF16 bits, 16-byte aligned; row i's
+ *                 column r*C + j is logits_slice[i * slice_stride + j]
+ *   slice_stride  >= C and a multiple of 8
+ *   temperature, target  as for rlk_logp_full (target is a global column)
+ *   summaries_out rlk_logp_summary_bytes(n_rows, layout) bytes, 16-byte
+ *                 aligned: n_rows * (8/G) records of 16 bytes, record
+ *                 (i, j) at index i * (8/G) + j for local shard j. A record is
+ *                 {float r; float l; float m; int32 aux}: for a row with
+ *                 T > 0, l = sum of 2^(x*log2(e)/T - r) over the shard's real
+ *                 columns in a fixed order, r an integer-valued reference
+ *                 exponent, aux = the target's BF16 bits if the target column
+ *                 lies in this shard, else -1; for T == 0, m = the shard's
+ *                 maximum and aux = its lowest global column.
+ *   layout->row_stride is not used (it must still be valid).
+ * rlk_logp_merge: given every rank's summaries concatenated in rank order
+ * (what an all-gather of summaries_out produces: rank r's block at offset
+ * r * rlk_logp_summary_bytes(); summaries_bytes >= n_rows * 128), merges each
+ * row's 8 summaries left to right and writes the same logp_out / lse_out
+ * bytes as rlk_logp_full on the whole rows, for every G.
+ * Both return RLK_OK or a negative status (rank outside [0, G) or a bad
+ * slice_stride is RLK_ERR_SHAPE; a short summary buffer RLK_ERR_WORKSPACE);
+ * n_rows == 0 enqueues nothing. */
+int32_t rlk_logp_shard_summaries(const uint16_t* logits_slice, int64_t n_rows, const rlk_vocab_layout* layout,
+                                 int32_t rank, int64_t slice_stride, const float* temperature,
+                                 const int64_t* target, void* summaries_out, size_t summaries_bytes,
+                                 hipStream_t stream);
+
+int32_t rlk_logp_merge(const void* summaries, size_t summaries_bytes, int64_t n_rows,
+                       const rlk_vocab_layout* layout, const float* temperature, const int64_t* target,
+                       float* logp_out, float* lse_out, hipStream_t stream);
+
+/* Bytes of one rank's summaries: n_rows * (8/groups) * 16. 0 for an invalid
+ * layout or n_rows < 0. */
+size_t rlk_logp_summary_bytes(int64_t n_rows, const rlk_vocab_layout* layout);
+
+/* Bytes of device workspace rlk_logp_full / rlk_logp_nucleus need: 0 when
+ * groups == 1, else n_rows * 128 (8 shard summaries of 16 bytes per row), for
+ * either entry point. Returns 0 for an invalid layout or n_rows < 0. */
 size_t rlk_logp_workspace_bytes(int64_t n_rows, const rlk_vocab_layout* layout, int32_t nucleus);
 
 /* Static, NUL-terminated description of a status code. */

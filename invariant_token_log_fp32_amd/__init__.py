@@ -17,7 +17,7 @@ from typing import Optional, Tuple, Union
 
 __all__ = [
     "LIB_PATH", "HEADER_PATH", "VocabLayout", "load_library", "status_string", "workspace_bytes",
-    "logp_full", "logp_nucleus", "RlkError", "N_SHARDS",
+    "summary_bytes", "logp_full", "logp_nucleus", "logp_shard_summaries", "logp_merge", "RlkError", "N_SHARDS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +71,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rlk_logp_workspace_bytes.restype = sz
     lib.rlk_status_string.argtypes = [i32]
     lib.rlk_status_string.restype = ctypes.c_char_p
+    lib.rlk_logp_shard_summaries.argtypes = [vp, i64, lay, i32, i64, vp, vp, vp, sz, vp]
+    lib.rlk_logp_shard_summaries.restype = i32
+    lib.rlk_logp_merge.argtypes = [vp, sz, i64, lay, vp, vp, vp, vp, vp]
+    lib.rlk_logp_merge.restype = i32
+    lib.rlk_logp_summary_bytes.argtypes = [i64, lay]
+    lib.rlk_logp_summary_bytes.restype = sz
     _lib = lib
     return lib
 
@@ -93,6 +99,12 @@ def workspace_bytes(n_rows: int, vocab_padded: int, vocab_real: int, row_stride:
                     groups: int = 1, nucleus: bool = False) -> int:
     lay = make_layout(vocab_padded, vocab_real, row_stride or vocab_padded, groups)
     return int(load_library().rlk_logp_workspace_bytes(int(n_rows), ctypes.byref(lay), 1 if nucleus else 0))
+
+
+def summary_bytes(n_rows: int, vocab_padded: int, vocab_real: int, groups: int = 1) -> int:
+    """Bytes of one rank's shard summaries (rlk_logp_summary_bytes)."""
+    lay = make_layout(vocab_padded, vocab_real, vocab_padded, groups)
+    return int(load_library().rlk_logp_summary_bytes(int(n_rows), ctypes.byref(lay)))
 
 
 # ---------------------------------------------------------------------------
@@ -197,3 +209,48 @@ def logp_nucleus(logits, temperature, top_p, top_k, target, *, vocab_real: int,
     if st != RLK_OK:
         raise RlkError(st, "rlk_logp_nucleus")
     return policy_out, ref_out
+
+
+def logp_shard_summaries(logits_slice, temperature, target, *, rank: int, groups: int, vocab_real: int,
+                         vocab_padded: int, out=None, stream=None):
+    """One rank's shard summaries (rlk_logp_shard_summaries). ``logits_slice``
+    is [n_rows, >= vocab_padded/groups] BF16 bits holding that rank's columns.
+    Returns a uint8 tensor of rlk_logp_summary_bytes() bytes."""
+    torch = _torch()
+    stride = _check_logits(logits_slice)
+    n = logits_slice.shape[0]
+    dev = logits_slice.device
+    temperature = _per_row(temperature, n, torch.float32, dev, "temperature")
+    target = _per_row(target, n, torch.int64, dev, "target")
+    lay = make_layout(vocab_padded, vocab_real, vocab_padded, groups)
+    lib = load_library()
+    need = int(lib.rlk_logp_summary_bytes(n, ctypes.byref(lay)))
+    if out is None:
+        out = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = lib.rlk_logp_shard_summaries(
+        logits_slice.data_ptr(), n, ctypes.byref(lay), int(rank), int(stride), temperature.data_ptr(),
+        target.data_ptr(), out.data_ptr(), out.numel(), _stream_handle(stream, dev))
+    if st != RLK_OK:
+        raise RlkError(st, "rlk_logp_shard_summaries")
+    return out
+
+
+def logp_merge(summaries, temperature, target, *, n_rows: int, groups: int, vocab_real: int, vocab_padded: int,
+               return_lse: bool = False, out=None, lse_out=None, stream=None):
+    """Merge the rank-ordered concatenation of every rank's summaries
+    (rlk_logp_merge); the result equals logp_full on the whole rows."""
+    torch = _torch()
+    dev = summaries.device
+    temperature = _per_row(temperature, n_rows, torch.float32, dev, "temperature")
+    target = _per_row(target, n_rows, torch.int64, dev, "target")
+    out = out if out is not None else torch.empty(n_rows, dtype=torch.float32, device=dev)
+    if return_lse and lse_out is None:
+        lse_out = torch.empty(n_rows, dtype=torch.float32, device=dev)
+    lay = make_layout(vocab_padded, vocab_real, vocab_padded, groups)
+    nbytes = summaries.numel() * summaries.element_size()
+    st = load_library().rlk_logp_merge(
+        summaries.data_ptr(), nbytes, int(n_rows), ctypes.byref(lay), temperature.data_ptr(), target.data_ptr(),
+        out.data_ptr(), lse_out.data_ptr() if lse_out is not None else None, _stream_handle(stream, dev))
+    if st != RLK_OK:
+        raise RlkError(st, "rlk_logp_merge")
+    return (out, lse_out) if return_lse else out

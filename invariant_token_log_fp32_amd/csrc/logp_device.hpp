@@ -46,17 +46,20 @@ constexpr float kRestartBound = 0x1p100f;
 // loaded with one 128-bit global load and a non-temporal hint).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Summary of one shard of one row.
+// Summary of one shard of one row (16 bytes; also the record that ranks of a
+// vocabulary-parallel layout exchange).
 //   value rows:  r = reference exponent (integer-valued), l = sum of 2^(x*c - r),
 //                m = maximum of the first chunk holding a value above -inf (the
-//                exact shard maximum when the shard was recomputed).
+//                exact shard maximum when the shard was recomputed),
+//                aux = BF16 bits of the target's logit when the target column
+//                lies in this shard's real columns, else -1.
 //   greedy rows: r = 0, l = 0 (NaN if the shard holds NaN or +inf), m = exact
-//                maximum, first = lowest column holding m (-1 if none).
+//                maximum, aux = lowest (global) column holding m, -1 if none.
 struct alignas(16) ShardSummary {
   float r;
   float l;
   float m;
-  int32_t first;
+  int32_t aux;
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -235,10 +238,10 @@ __device__ __forceinline__ float shard_exact_max(const u32x4* __restrict__ base,
 // for a row with valid temperature T > 0 (c = fl32(log2(e) / T)).
 // Must be called by all 64 lanes of a wave.
 template <int U, typename Hook = NoHook>
-__device__ __forceinline__ ShardSummary summarize_shard(const uint16_t* __restrict__ row, int col0, int ncols, float c,
+__device__ __forceinline__ ShardSummary summarize_shard(const uint16_t* __restrict__ shard, int ncols, float c,
                                                         Hook& hook) {
   const int lane = threadIdx.x & (kWave - 1);
-  const u32x4* __restrict__ base = reinterpret_cast<const u32x4*>(row + col0);
+  const u32x4* __restrict__ base = reinterpret_cast<const u32x4*>(shard);
   const int nfull = ncols >> 3;
   const int tail = ncols & 7;
 
@@ -267,25 +270,27 @@ __device__ __forceinline__ ShardSummary summarize_shard(const uint16_t* __restri
   s.r = r;
   s.l = total;
   s.m = m;
-  s.first = -1;
+  s.aux = -1;
   return s;
 }
 
 // Greedy (T == 0) summary: exact maximum, its lowest column, and a NaN mark
 // when the shard holds NaN or +inf.
-__device__ __forceinline__ ShardSummary summarize_shard_greedy(const uint16_t* __restrict__ row, int col0, int ncols) {
+// `shard` points at the shard's first column, whose global index is col0.
+__device__ __forceinline__ ShardSummary summarize_shard_greedy(const uint16_t* __restrict__ shard, int col0,
+                                                              int ncols) {
   const int lane = threadIdx.x & (kWave - 1);
   float m = -INFINITY;
   bool bad = false;
   for (int j = lane; j < ncols; j += kWave) {
-    const float x = __uint_as_float(static_cast<uint32_t>(row[col0 + j]) << 16);
+    const float x = __uint_as_float(static_cast<uint32_t>(shard[j]) << 16);
     bad |= (x != x) || (x == INFINITY);
     m = fmaxf(m, x);
   }
   m = wave_max(m);
   int first = INT32_MAX;
   for (int j = lane; j < ncols; j += kWave) {
-    const float x = __uint_as_float(static_cast<uint32_t>(row[col0 + j]) << 16);
+    const float x = __uint_as_float(static_cast<uint32_t>(shard[j]) << 16);
     if (x == m) { first = min(first, col0 + j); break; }
   }
   first = wave_min_i32(first);
@@ -294,7 +299,7 @@ __device__ __forceinline__ ShardSummary summarize_shard_greedy(const uint16_t* _
   s.r = 0.0f;
   s.l = any_bad ? NAN : 0.0f;
   s.m = m;
-  s.first = (first == INT32_MAX) ? -1 : first;
+  s.aux = (first == INT32_MAX) ? -1 : first;
   return s;
 }
 
@@ -307,9 +312,10 @@ struct RowMerge {
 };
 
 // Fixed-order merge of the 8 summaries of a row (shard 0 first), then the
-// target's logprob. `xt` is the target's logit (float32 from BF16).
+// target's logprob; the target's logit comes from the aux field of the shard
+// holding it (shard_width = columns per shard).
 __device__ __forceinline__ RowMerge merge_row(const ShardSummary* __restrict__ s, float t, bool target_ok, int64_t target,
-                                              float xt) {
+                                              int shard_width) {
   RowMerge out;
   out.logp = NAN;
   out.lse = NAN;
@@ -328,7 +334,7 @@ __device__ __forceinline__ RowMerge merge_row(const ShardSummary* __restrict__ s
     int first = -1;
 #pragma unroll
     for (int k = kShards - 1; k >= 0; --k)  // lowest shard holding the maximum wins
-      first = (s[k].m == m) ? s[k].first : first;
+      first = (s[k].m == m) ? s[k].aux : first;
     out.logp = (static_cast<int64_t>(first) == target) ? 0.0f : -INFINITY;
     out.ok = true;
     return out;
@@ -347,8 +353,14 @@ __device__ __forceinline__ RowMerge merge_row(const ShardSummary* __restrict__ s
     if (s[k].r != s[k].r || l != l) acc = NAN;
   }
   if (!(acc > 0.0) || !(acc < INFINITY) || !(rmax > -INFINITY) || !(rmax < INFINITY)) return out;
+  const int ts = static_cast<int>(target / shard_width);
+  int tbits = -1;
+#pragma unroll
+  for (int k = 0; k < kShards; ++k) tbits = (k == ts) ? s[k].aux : tbits;
+  if (tbits < 0) return out;  // the shard holding the target did not report it
   const double lse2 = static_cast<double>(rmax) + log2(acc);
   const double lse = lse2 * kLn2;
+  const float xt = __uint_as_float(static_cast<uint32_t>(tbits) << 16);
   const float zt = xt / t;  // IEEE float32 division, rounded to nearest
   out.lse2 = lse2;
   out.lse = static_cast<float>(lse);

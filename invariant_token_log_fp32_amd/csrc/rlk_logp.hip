@@ -1,26 +1,28 @@
 // Strict token-logprob kernels for gfx950 and the C-ABI declared in include/rlk_logp.h.
 //
 // Kernels:
-//   k_full_g1     one workgroup (8 waves) per row: wave s summarises shard s,
-//                 the summaries meet in LDS, thread 0 merges them and writes
-//                 the reference logprob (the headline path, one launch).
-//   k_summaries   groups > 1 or the support path: workgroup (row, g) runs the
-//                 8/groups consecutive shards that a physical rank would own
-//                 and stores their summaries in the workspace.
-//   k_merge_full  one thread per row: the same merge as k_full_g1.
-//   k_nucleus_g1  groups == 1 support path in one launch: one workgroup per
-//                 row runs the 8 shard-waves, which also count every token
-//                 into an LDS histogram of compressed BF16 ranks, merges the
-//                 summaries (reference logprob), finds the top-k/top-p
-//                 support from the exact integer histogram and writes the
-//                 policy logprob.
-//   k_nucleus     groups > 1: the same per-row support search on summaries
-//                 that k_summaries stored in the workspace.
+//   k_full_g1          one workgroup (8 waves) per row: wave s summarises
+//                      shard s, the summaries meet in LDS, thread 0 merges
+//                      them and writes the reference logprob (one launch).
+//   k_rank_summaries   workgroup (row, rank) runs the 8/groups consecutive
+//                      shard-waves a rank of a vocabulary-parallel layout owns
+//                      and stores their 16-byte summaries rank-major; used by
+//                      groups > 1 and by rlk_logp_shard_summaries on a slice.
+//   k_merge            one thread per row: the same fixed-order merge over the
+//                      rank-major summaries (groups > 1, rlk_logp_merge).
+//   k_nucleus_g1       groups == 1 support path in one launch: the shard-waves
+//                      also count every token into an LDS histogram of
+//                      compressed BF16 ranks; then the merge (reference
+//                      logprob), the top-k/top-p support from the exact
+//                      integer histogram, and the policy logprob.
+//   k_nucleus          groups > 1: the same per-row support search on the
+//                      summaries k_rank_summaries stored.
 // Passages: RL-Kernel page "Configurable H100 consistency runs" (sampling,
 // topology and mode/KL paragraphs; top-k independent of top-p in the command
 // examples) and page "Reproduce and profile the Qwen3-8B TP4/CP2 experiment",
 // section "How non-default CUDA topology reuses TP4/CP2" (per-virtual-shard
-// summaries merged in fixed global-vocabulary order).
+// summaries merged in fixed global-vocabulary order; a coarser physical rank
+// owns several virtual shards).
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -35,32 +37,31 @@ namespace rlk {
 constexpr int kChunk = 8;
 constexpr int kRowThreads = kShards * kWave;  // 512
 
-// Per-row, per-shard dispatch on the temperature (uniform across the workgroup).
+// Summary of the shard whose first column (global index col0) is at `shard`,
+// for a row with temperature t and target column tg. Uniform across the wave;
+// dispatches on the temperature (uniform across the workgroup).
 template <typename Hook = NoHook>
-__device__ __forceinline__ ShardSummary summarize_row_shard(const uint16_t* __restrict__ rowp, int shard,
+__device__ __forceinline__ ShardSummary summarize_row_shard(const uint16_t* __restrict__ shard, int64_t col0,
                                                             int shard_width, int64_t vocab_real, float t,
-                                                            Hook& hook) {
+                                                            int64_t tg, Hook& hook) {
   ShardSummary s;
   s.r = 0.0f;
   s.l = 0.0f;
   s.m = -INFINITY;
-  s.first = -1;
+  s.aux = -1;
   if (!temperature_valid(t)) {
     s.l = NAN;
     return s;
   }
-  const int64_t col0 = static_cast<int64_t>(shard) * shard_width;
   int64_t ncols64 = vocab_real - col0;
   ncols64 = ncols64 < 0 ? 0 : (ncols64 > shard_width ? shard_width : ncols64);
   const int ncols = static_cast<int>(ncols64);
   if (ncols == 0) return s;
-  if (t == 0.0f) return summarize_shard_greedy(rowp, static_cast<int>(col0), ncols);
+  if (t == 0.0f) return summarize_shard_greedy(shard, static_cast<int>(col0), ncols);
   const float c = kLog2e / t;  // IEEE float32 division
-  return summarize_shard<kChunk>(rowp, static_cast<int>(col0), ncols, c, hook);
-}
-
-__device__ __forceinline__ float load_target_logit(const uint16_t* __restrict__ rowp, int64_t tg) {
-  return __uint_as_float(static_cast<uint32_t>(rowp[tg]) << 16);
+  s = summarize_shard<kChunk>(shard, ncols, c, hook);
+  if (tg >= col0 && tg < col0 + ncols) s.aux = static_cast<int32_t>(shard[tg - col0]);
+  return s;
 }
 
 __global__ __launch_bounds__(kRowThreads) void k_full_g1(const uint16_t* __restrict__ logits, int64_t row_stride,
@@ -71,58 +72,65 @@ __global__ __launch_bounds__(kRowThreads) void k_full_g1(const uint16_t* __restr
   __shared__ ShardSummary sm[kShards];
   const int64_t row = blockIdx.x;
   const int wave = threadIdx.x / kWave;
+  const int64_t col0 = static_cast<int64_t>(wave) * shard_width;
   const uint16_t* __restrict__ rowp = logits + row * row_stride;
   const float t = temperature[row];
-
-  int64_t tg = -1;
-  bool tok = false;
-  float xt = 0.0f;
-  if (threadIdx.x == 0) {
-    tg = target[row];
-    tok = (tg >= 0) && (tg < vocab_real);
-    if (tok) xt = load_target_logit(rowp, tg);
-  }
+  const int64_t tg = target[row];
   NoHook none;
-  const ShardSummary s = summarize_row_shard(rowp, wave, shard_width, vocab_real, t, none);
+  const ShardSummary s = summarize_row_shard(rowp + col0, col0, shard_width, vocab_real, t, tg, none);
   if ((threadIdx.x & (kWave - 1)) == 0) sm[wave] = s;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const RowMerge mr = merge_row(sm, t, tok, tg, xt);
+    const bool tok = (tg >= 0) && (tg < vocab_real);
+    const RowMerge mr = merge_row(sm, t, tok, tg, shard_width);
     logp_out[row] = mr.logp;
     if (lse_out) lse_out[row] = mr.lse;
   }
 }
 
-__global__ __launch_bounds__(kRowThreads) void k_summaries(const uint16_t* __restrict__ logits, int64_t row_stride,
-                                                           int shard_width, int64_t vocab_real,
-                                                           const float* __restrict__ temperature, int groups,
-                                                           ShardSummary* __restrict__ ws) {
-  const int waves_per_group = kShards / groups;
-  const int64_t row = blockIdx.x / groups;
-  const int g = blockIdx.x % groups;
-  const int shard = g * waves_per_group + static_cast<int>(threadIdx.x / kWave);
-  const uint16_t* __restrict__ rowp = logits + row * row_stride;
-  const float t = temperature[row];
+// Workgroup b handles row b / ranks_in_grid and rank rank0 + b % ranks_in_grid,
+// whose slice of the row starts at base + (b % ranks_in_grid) * rank_col_step +
+// row * slice_stride and holds shards [rank * spr, rank * spr + spr) (spr =
+// 8 / groups = waves per workgroup). Writes out[((b % ranks_in_grid) * n_rows +
+// row) * spr + wave].
+__global__ __launch_bounds__(kRowThreads) void k_rank_summaries(const uint16_t* __restrict__ base,
+                                                                int64_t slice_stride, int64_t rank_col_step,
+                                                                int rank0, int ranks_in_grid, int spr,
+                                                                int shard_width, int64_t vocab_real, int64_t n_rows,
+                                                                const float* __restrict__ temperature,
+                                                                const int64_t* __restrict__ target,
+                                                                ShardSummary* __restrict__ out) {
+  const int64_t row = blockIdx.x / ranks_in_grid;
+  const int rr = static_cast<int>(blockIdx.x % ranks_in_grid);
+  const int wave = static_cast<int>(threadIdx.x / kWave);
+  const int shard = (rank0 + rr) * spr + wave;
+  const int64_t col0 = static_cast<int64_t>(shard) * shard_width;
+  const uint16_t* __restrict__ sp =
+      base + rr * rank_col_step + row * slice_stride + static_cast<int64_t>(wave) * shard_width;
   NoHook none;
-  const ShardSummary s = summarize_row_shard(rowp, shard, shard_width, vocab_real, t, none);
-  if ((threadIdx.x & (kWave - 1)) == 0) ws[row * kShards + shard] = s;
+  const ShardSummary s = summarize_row_shard(sp, col0, shard_width, vocab_real, temperature[row], target[row], none);
+  if ((threadIdx.x & (kWave - 1)) == 0) out[(static_cast<int64_t>(rr) * n_rows + row) * spr + wave] = s;
 }
 
-__global__ __launch_bounds__(256) void k_merge_full(const uint16_t* __restrict__ logits, int64_t row_stride,
-                                                    int64_t vocab_real, const float* __restrict__ temperature,
-                                                    const int64_t* __restrict__ target,
-                                                    const ShardSummary* __restrict__ ws, int64_t n_rows,
-                                                    float* __restrict__ logp_out, float* __restrict__ lse_out) {
+// Loads the 8 summaries of a row from the rank-major layout.
+__device__ __forceinline__ void load_row_summaries(const ShardSummary* __restrict__ ws, int64_t row, int64_t n_rows,
+                                                   int spr, ShardSummary* s) {
+#pragma unroll
+  for (int k = 0; k < kShards; ++k) s[k] = ws[(static_cast<int64_t>(k / spr) * n_rows + row) * spr + (k % spr)];
+}
+
+__global__ __launch_bounds__(256) void k_merge(const ShardSummary* __restrict__ ws, int64_t n_rows, int spr,
+                                               int shard_width, int64_t vocab_real,
+                                               const float* __restrict__ temperature,
+                                               const int64_t* __restrict__ target, float* __restrict__ logp_out,
+                                               float* __restrict__ lse_out) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (row >= n_rows) return;
   ShardSummary s[kShards];
-#pragma unroll
-  for (int k = 0; k < kShards; ++k) s[k] = ws[row * kShards + k];
-  const float t = temperature[row];
+  load_row_summaries(ws, row, n_rows, spr, s);
   const int64_t tg = target[row];
   const bool tok = (tg >= 0) && (tg < vocab_real);
-  const float xt = tok ? load_target_logit(logits + row * row_stride, tg) : 0.0f;
-  const RowMerge mr = merge_row(s, t, tok, tg, xt);
+  const RowMerge mr = merge_row(s, temperature[row], tok, tg, shard_width);
   logp_out[row] = mr.logp;
   if (lse_out) lse_out[row] = mr.lse;
 }
@@ -130,40 +138,39 @@ __global__ __launch_bounds__(256) void k_merge_full(const uint16_t* __restrict__
 // ----------------------------------------------------------------------------
 // Support path (top-k then top-p): see support.hpp.
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_nucleus_g1(const uint16_t* __restrict__ logits, int64_t row_stride,
-                                                            int shard_width, int64_t vocab_real,
-                                                            const float* __restrict__ temperature,
-                                                            const float* __restrict__ top_p,
-                                                            const int32_t* __restrict__ top_k,
-                                                            const int64_t* __restrict__ target,
-                                                            float* __restrict__ policy_out,
-                                                            float* __restrict__ ref_out) {
+__global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_nucleus_g1(
+    const uint16_t* __restrict__ logits, int64_t row_stride, int shard_width, int64_t vocab_real,
+    const float* __restrict__ temperature, const float* __restrict__ top_p, const int32_t* __restrict__ top_k,
+    const int64_t* __restrict__ target, float* __restrict__ policy_out, float* __restrict__ ref_out) {
   __shared__ NucLds L;
   const int64_t row = blockIdx.x;
   const int wave = threadIdx.x / kWave;
+  const int64_t col0 = static_cast<int64_t>(wave) * shard_width;
   const uint16_t* __restrict__ rowp = logits + row * row_stride;
   const float t = temperature[row];
   const float p = top_p[row];
   const int64_t k = top_k[row];
+  const int64_t tg = target[row];
   if (search_needed(t, p, k, vocab_real)) {
     // the shard-waves build the key histogram while they stream the row
     window_clear(L);
     __syncthreads();
     WindowHook hook(L.u.win);
-    const ShardSummary s = summarize_row_shard(rowp, wave, shard_width, vocab_real, t, hook);
+    const ShardSummary s = summarize_row_shard(rowp + col0, col0, shard_width, vocab_real, t, tg, hook);
     if ((threadIdx.x & (kWave - 1)) == 0) L.sm[wave] = s;
     hook.publish(L);
   } else {
     NoHook none;
-    const ShardSummary s = summarize_row_shard(rowp, wave, shard_width, vocab_real, t, none);
+    const ShardSummary s = summarize_row_shard(rowp + col0, col0, shard_width, vocab_real, t, tg, none);
     if ((threadIdx.x & (kWave - 1)) == 0) L.sm[wave] = s;
   }
   __syncthreads();
-  nucleus_row(L, rowp, row, vocab_real, t, p, k, target[row], true, policy_out, ref_out);
+  nucleus_row(L, rowp, row, vocab_real, shard_width, t, p, k, tg, true, policy_out, ref_out);
 }
 
 __global__ __launch_bounds__(kNucThreads) void k_nucleus(const uint16_t* __restrict__ logits, int64_t row_stride,
-                                                         int64_t vocab_real, const float* __restrict__ temperature,
+                                                         int64_t n_rows, int spr, int shard_width, int64_t vocab_real,
+                                                         const float* __restrict__ temperature,
                                                          const float* __restrict__ top_p,
                                                          const int32_t* __restrict__ top_k,
                                                          const int64_t* __restrict__ target,
@@ -171,10 +178,13 @@ __global__ __launch_bounds__(kNucThreads) void k_nucleus(const uint16_t* __restr
                                                          float* __restrict__ policy_out, float* __restrict__ ref_out) {
   __shared__ NucLds L;
   const int64_t row = blockIdx.x;
-  if (threadIdx.x < kShards) L.sm[threadIdx.x] = ws[row * kShards + threadIdx.x];
+  if (threadIdx.x < kShards) {
+    const int k = threadIdx.x;
+    L.sm[k] = ws[(static_cast<int64_t>(k / spr) * n_rows + row) * spr + (k % spr)];
+  }
   __syncthreads();
-  nucleus_row(L, logits + row * row_stride, row, vocab_real, temperature[row], top_p[row], top_k[row], target[row],
-              false, policy_out, ref_out);
+  nucleus_row(L, logits + row * row_stride, row, vocab_real, shard_width, temperature[row], top_p[row], top_k[row],
+              target[row], false, policy_out, ref_out);
 }
 
 // ----------------------------------------------------------------------------
@@ -200,12 +210,27 @@ static int32_t check_layout(int64_t n_rows, const rlk_vocab_layout* L) {
   return RLK_OK;
 }
 
+static size_t summary_bytes_all(int64_t n_rows) { return static_cast<size_t>(n_rows) * kShards * sizeof(ShardSummary); }
+
 static size_t workspace_bytes(int64_t n_rows, const rlk_vocab_layout* L, bool /*nucleus*/) {
   if (L->groups == 1) return 0;
-  return static_cast<size_t>(n_rows) * kShards * sizeof(ShardSummary);
+  return summary_bytes_all(n_rows);
 }
 
 static int32_t launched() { return hipGetLastError() == hipSuccess ? RLK_OK : RLK_ERR_HIP; }
+
+// groups > 1: every rank's summaries of the full rows, rank-major, into ws.
+static int32_t launch_all_ranks(const uint16_t* logits, int64_t n_rows, const rlk_vocab_layout* L,
+                                const float* temperature, const int64_t* target, ShardSummary* ws,
+                                hipStream_t stream) {
+  const int S = static_cast<int>(L->vocab_padded / kShards);
+  const int G = L->groups;
+  const int spr = kShards / G;
+  k_rank_summaries<<<dim3(static_cast<unsigned>(n_rows * G)), dim3(spr * kWave), 0, stream>>>(
+      logits, L->row_stride, static_cast<int64_t>(spr) * S, 0, G, spr, S, L->vocab_real, n_rows, temperature, target,
+      ws);
+  return launched();
+}
 
 }  // namespace rlk
 
@@ -215,10 +240,10 @@ const char* rlk_status_string(int32_t status) {
   switch (status) {
     case RLK_OK: return "ok";
     case RLK_ERR_NULL: return "a required pointer is NULL";
-    case RLK_ERR_ALIGN: return "misaligned pointer (logits and workspace need 16 bytes)";
-    case RLK_ERR_SHAPE: return "n_rows or a layout field is out of range";
+    case RLK_ERR_ALIGN: return "misaligned pointer (logits, slices, summaries and workspace need 16 bytes)";
+    case RLK_ERR_SHAPE: return "n_rows, rank or a layout field is out of range";
     case RLK_ERR_GROUPS: return "groups must be 1, 2, 4 or 8";
-    case RLK_ERR_WORKSPACE: return "workspace missing or too small";
+    case RLK_ERR_WORKSPACE: return "workspace or summary buffer missing or too small";
     case RLK_ERR_HIP: return "HIP runtime error while launching";
     default: return "unknown status";
   }
@@ -227,6 +252,11 @@ const char* rlk_status_string(int32_t status) {
 size_t rlk_logp_workspace_bytes(int64_t n_rows, const rlk_vocab_layout* layout, int32_t nucleus) {
   if (rlk::check_layout(n_rows, layout) != RLK_OK) return 0;
   return rlk::workspace_bytes(n_rows, layout, nucleus != 0);
+}
+
+size_t rlk_logp_summary_bytes(int64_t n_rows, const rlk_vocab_layout* layout) {
+  if (rlk::check_layout(n_rows, layout) != RLK_OK) return 0;
+  return rlk::summary_bytes_all(n_rows) / static_cast<size_t>(layout->groups);
 }
 
 int32_t rlk_logp_full(const uint16_t* logits, int64_t n_rows, const rlk_vocab_layout* layout,
@@ -253,12 +283,10 @@ int32_t rlk_logp_full(const uint16_t* logits, int64_t n_rows, const rlk_vocab_la
     return launched();
   }
   ShardSummary* ws = static_cast<ShardSummary*>(workspace);
-  k_summaries<<<dim3(static_cast<unsigned>(n_rows * G)), dim3(kShards / G * kWave), 0, stream>>>(
-      logits, layout->row_stride, S, layout->vocab_real, temperature, G, ws);
-  if ((st = launched()) != RLK_OK) return st;
+  if ((st = launch_all_ranks(logits, n_rows, layout, temperature, target, ws, stream)) != RLK_OK) return st;
   const unsigned blocks = static_cast<unsigned>((n_rows + 255) / 256);
-  k_merge_full<<<dim3(blocks), dim3(256), 0, stream>>>(logits, layout->row_stride, layout->vocab_real,
-                                                       temperature, target, ws, n_rows, logp_out, lse_out);
+  k_merge<<<dim3(blocks), dim3(256), 0, stream>>>(ws, n_rows, kShards / G, S, layout->vocab_real, temperature, target,
+                                                  logp_out, lse_out);
   return launched();
 }
 
@@ -287,11 +315,54 @@ int32_t rlk_logp_nucleus(const uint16_t* logits, int64_t n_rows, const rlk_vocab
     return launched();
   }
   ShardSummary* ws = static_cast<ShardSummary*>(workspace);
-  k_summaries<<<dim3(static_cast<unsigned>(n_rows * G)), dim3(kShards / G * kWave), 0, stream>>>(
-      logits, layout->row_stride, S, layout->vocab_real, temperature, G, ws);
-  if ((st = launched()) != RLK_OK) return st;
+  if ((st = launch_all_ranks(logits, n_rows, layout, temperature, target, ws, stream)) != RLK_OK) return st;
   k_nucleus<<<dim3(static_cast<unsigned>(n_rows)), dim3(kNucThreads), 0, stream>>>(
-      logits, layout->row_stride, layout->vocab_real, temperature, top_p, top_k, target, ws, policy_out, ref_out);
+      logits, layout->row_stride, n_rows, kShards / G, S, layout->vocab_real, temperature, top_p, top_k, target, ws,
+      policy_out, ref_out);
+  return launched();
+}
+
+int32_t rlk_logp_shard_summaries(const uint16_t* logits_slice, int64_t n_rows, const rlk_vocab_layout* layout,
+                                 int32_t rank, int64_t slice_stride, const float* temperature,
+                                 const int64_t* target, void* summaries_out, size_t summaries_bytes,
+                                 hipStream_t stream) {
+  using namespace rlk;
+  int32_t st = check_layout(n_rows, layout);
+  if (st != RLK_OK) return st;
+  const int G = layout->groups;
+  const int spr = kShards / G;
+  const int64_t S = layout->vocab_padded / kShards;
+  if (rank < 0 || rank >= G) return RLK_ERR_SHAPE;
+  if (slice_stride < spr * S || slice_stride % 8 != 0) return RLK_ERR_SHAPE;
+  if (n_rows > 0 && slice_stride > INT64_MAX / 2 / n_rows) return RLK_ERR_SHAPE;
+  if (n_rows == 0) return RLK_OK;
+  if (!logits_slice || !temperature || !target || !summaries_out) return RLK_ERR_NULL;
+  if (!aligned(logits_slice, 16) || !aligned(temperature, 4) || !aligned(target, 8) || !aligned(summaries_out, 16))
+    return RLK_ERR_ALIGN;
+  if (summaries_bytes < summary_bytes_all(n_rows) / static_cast<size_t>(G)) return RLK_ERR_WORKSPACE;
+  k_rank_summaries<<<dim3(static_cast<unsigned>(n_rows)), dim3(spr * kWave), 0, stream>>>(
+      logits_slice, slice_stride, 0, rank, 1, spr, static_cast<int>(S), layout->vocab_real, n_rows, temperature,
+      target, static_cast<ShardSummary*>(summaries_out));
+  return launched();
+}
+
+int32_t rlk_logp_merge(const void* summaries, size_t summaries_bytes, int64_t n_rows,
+                       const rlk_vocab_layout* layout, const float* temperature, const int64_t* target,
+                       float* logp_out, float* lse_out, hipStream_t stream) {
+  using namespace rlk;
+  int32_t st = check_layout(n_rows, layout);
+  if (st != RLK_OK) return st;
+  if (n_rows == 0) return RLK_OK;
+  if (!summaries || !temperature || !target || !logp_out) return RLK_ERR_NULL;
+  if (!aligned(summaries, 16) || !aligned(temperature, 4) || !aligned(target, 8) || !aligned(logp_out, 4) ||
+      (lse_out && !aligned(lse_out, 4)))
+    return RLK_ERR_ALIGN;
+  if (summaries_bytes < summary_bytes_all(n_rows)) return RLK_ERR_WORKSPACE;
+  const int S = static_cast<int>(layout->vocab_padded / kShards);
+  const unsigned blocks = static_cast<unsigned>((n_rows + 255) / 256);
+  k_merge<<<dim3(blocks), dim3(256), 0, stream>>>(static_cast<const ShardSummary*>(summaries), n_rows,
+                                                  kShards / layout->groups, S, layout->vocab_real, temperature, target,
+                                                  logp_out, lse_out);
   return launched();
 }
 

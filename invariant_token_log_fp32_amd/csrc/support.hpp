@@ -737,8 +737,8 @@ __device__ __forceinline__ bool search_needed(float t, float p, int64_t k, int64
 // streaming pass counted the row). Writes ref_out[row] and policy_out[row].
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restrict__ rowp, int64_t row,
-                                            int64_t vocab_real, float t, float p, int64_t k, int64_t tg,
-                                            bool window_built, float* __restrict__ policy_out,
+                                            int64_t vocab_real, int shard_width, float t, float p, int64_t k,
+                                            int64_t tg, bool window_built, float* __restrict__ policy_out,
                                             float* __restrict__ ref_out) {
   const int tid = threadIdx.x;
   float ref = NAN, zt = NAN;
@@ -747,7 +747,7 @@ __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restric
     const bool tok = (tg >= 0) && (tg < vocab_real);
     if (tok) bt = rowp[tg];
     const float xt = __uint_as_float(bt << 16);
-    const RowMerge mr = merge_row(L.sm, t, tok, tg, xt);
+    const RowMerge mr = merge_row(L.sm, t, tok, tg, shard_width);
     ref = mr.logp;
     ref_out[row] = ref;
     const bool p_ok = (p > 0.0f) && (p <= 1.0f);

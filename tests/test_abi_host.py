@@ -41,7 +41,8 @@ def nuc(lib, logits=P, n=4, L=None, t=P + 0x100, p=P + 0x140, k=P + 0x180, tg=P 
 
 def test_every_declared_function_is_exported(lib):
     names = rlk.declared_functions()
-    assert set(names) == {"rlk_logp_full", "rlk_logp_nucleus", "rlk_logp_workspace_bytes", "rlk_status_string"}
+    assert set(names) == {"rlk_logp_full", "rlk_logp_nucleus", "rlk_logp_workspace_bytes", "rlk_status_string",
+                          "rlk_logp_shard_summaries", "rlk_logp_merge", "rlk_logp_summary_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -118,3 +119,41 @@ def test_binding_fails_loudly_without_library(tmp_path):
             mod.load_library(str(tmp_path / "nope.so"))
         finally:
             mod._lib = saved
+
+
+def shard(lib, logits=P, n=4, L=None, rank=0, stride=1024, t=P + 0x100, tg=P + 0x200, out=P + 0x1000, ob=1 << 20):
+    L = L if L is not None else lay()
+    return lib.rlk_logp_shard_summaries(logits, n, ctypes.byref(L) if L is not False else None, rank, stride, t, tg,
+                                        out, ob, None)
+
+
+def merge(lib, summ=P + 0x1000, sb=1 << 20, n=4, L=None, t=P + 0x100, tg=P + 0x200, out=P + 0x300, lse=None):
+    L = L if L is not None else lay()
+    return lib.rlk_logp_merge(summ, sb, n, ctypes.byref(L) if L is not False else None, t, tg, out, lse, None)
+
+
+def test_shard_api_zero_rows_and_sizes(lib):
+    assert shard(lib, n=0, logits=None, t=None, tg=None, out=None, ob=0) == OK
+    assert merge(lib, n=0, summ=None, sb=0, t=None, tg=None, out=None) == OK
+    for g in (1, 2, 4, 8):
+        assert rlk.summary_bytes(8192, 152576, 151936, groups=g) == 8192 * (8 // g) * 16
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), NULL), (dict(t=None), NULL), (dict(tg=None), NULL), (dict(out=None), NULL),
+    (dict(L=False), NULL), (dict(logits=P + 8), ALIGN), (dict(out=P + 8), ALIGN), (dict(tg=P + 4), ALIGN),
+    (dict(rank=-1), SHAPE), (dict(rank=1), SHAPE), (dict(L=lay(groups=2), rank=2), SHAPE),
+    (dict(stride=1020), SHAPE), (dict(L=lay(groups=4), stride=250), SHAPE), (dict(L=lay(groups=4), stride=252), SHAPE),
+    (dict(ob=4 * 8 * 16 - 1), WS), (dict(L=lay(groups=2), ob=4 * 4 * 16 - 1), WS),
+    (dict(L=lay(groups=6)), GROUPS), (dict(n=-1), SHAPE),
+])
+def test_shard_summaries_rejects_bad_arguments(lib, kw, code):
+    assert shard(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(summ=None), NULL), (dict(t=None), NULL), (dict(out=None), NULL), (dict(summ=P + 8), ALIGN),
+    (dict(lse=P + 2), ALIGN), (dict(sb=4 * 128 - 1), WS), (dict(L=lay(groups=3)), GROUPS), (dict(n=-2), SHAPE),
+])
+def test_merge_rejects_bad_arguments(lib, kw, code):
+    assert merge(lib, **kw) == code
