@@ -35,6 +35,18 @@ What it computes, per row i of BF16 logits ``x[i, j]`` (j < vocab_real):
 5. Greedy (T == 0): a point mass on the lowest-index argmax of x; both
    outputs are 0 for that token and -inf for every other one.
 
+6. Gradient (the training side consumes logprob gradients; page "H100
+   canonical CP backward validation", "Change"): for upstream gradients
+   g_ref, g_pol of one row,
+   d/dx_j = (1/T) * ( [j == t] * (g_ref + g_pol') - g_ref * p_j
+                      - g_pol' * [j in S] * q_j )
+   with p = softmax(z) over the real vocabulary, q the softmax restricted to
+   the support S, and g_pol' = g_pol when t is in S, else 0 (the policy
+   logprob is the constant -inf there). The support is piecewise constant in
+   x, so its boundaries carry no gradient. Pad columns get 0; a row with
+   g_ref = g_pol = 0 or T = 0 (greedy: piecewise-constant logprob) gets 0; any
+   other row whose forward is NaN gets NaN on its real columns.
+
 Rows with an invalid temperature (NaN, +-inf, negative) or target (outside
 [0, vocab_real)), or whose real logits contain NaN or +inf, or are all -inf,
 give NaN for both outputs. An invalid top-p (outside (0, 1]) or top-k
@@ -121,6 +133,8 @@ class NucleusInfo:
     alternatives: List[float] = field(default_factory=list)  # pol for neighbouring top-p cuts
     ambiguous: bool = False
     support_mask: Optional[np.ndarray] = None
+    lse_support: float = NAN   # log of the support's sum of exp(z_j)
+    threshold: float = NAN     # smallest kept BF16 logit value; -inf when the support is the whole real vocabulary
 
 
 def _classes(z: np.ndarray):
@@ -178,6 +192,8 @@ def nucleus_row(bits_row, vocab_real: int, temperature: float, top_p: float, top
     info.support_size = int(counts[: r_star + 1].sum())
     if want_mask:
         info.support_mask = inv <= r_star
+    info.lse_support = m + math.log(math.fsum(w[: r_star + 1].tolist()))
+    info.threshold = NEG_INF if r_star == last else float(x[inv <= r_star].min())
 
     def pol_for(r_cut: int) -> float:
         if r_cut == last:
@@ -227,3 +243,40 @@ def nucleus_logp(logits: np.ndarray, vocab_real: int, temperature, top_p, top_k,
                                            float(top_p[i]), int(top_k[i]), int(target[i]), band)
         infos.append(info)
     return pol, ref, infos
+
+
+def grad_row(bits_row, vocab_padded: int, vocab_real: int, temperature: float, target: int,
+             g_ref: float, g_pol: float = 0.0, top_p: float = 1.0, top_k: int = -1) -> np.ndarray:
+    """float64 gradient of g_ref * ref + g_pol * policy with respect to the row's
+    logits (columns [0, vocab_padded)); see item 6 of the module docstring."""
+    g = np.zeros(vocab_padded)
+    g_ref = float(g_ref)
+    g_pol = float(g_pol)
+    if g_ref == 0.0 and g_pol == 0.0:
+        return g
+    x, err = _row_prelude(bits_row, vocab_real, temperature, target)
+    if err is not None:
+        g[:vocab_real] = NAN
+        return g
+    t = float(np.float32(temperature))
+    if t == 0.0:
+        return g
+    z = scale_fp32(x, t)
+    m = float(z.max())
+    e = np.exp(z - m)
+    zsum = math.fsum(e.tolist())
+    p = e / zsum
+    pol, _, info = nucleus_row(bits_row, vocab_real, temperature, top_p, top_k, target, want_mask=True)
+    if g_pol != 0.0 and math.isnan(pol):
+        g[:vocab_real] = NAN
+        return g
+    gp = g_pol if (g_pol != 0.0 and np.isfinite(pol)) else 0.0
+    out = -g_ref * p
+    if gp != 0.0:
+        mask = info.support_mask if info.support_mask is not None else np.ones(vocab_real, dtype=bool)
+        es = np.where(mask, e, 0.0)
+        q = es / math.fsum(es.tolist())
+        out = out - gp * q
+    out[int(target)] += g_ref + gp
+    g[:vocab_real] = out / t
+    return g

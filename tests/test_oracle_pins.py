@@ -422,3 +422,164 @@ def test_golden_snapshot_is_current():
             pol, ref2, info = O.nucleus_row(logits[i], 1000, 1.0, c["top_p"], c["top_k"], c["target"])
             assert pol == c["policy_logp"] and ref2 == c["ref_logp"]
             assert info.support_size == c["support_size"]
+
+
+# --------------------------------------------------------------------------- support record (threshold, lse)
+
+def test_support_threshold_and_lse_match_subset_enumeration():
+    rng = np.random.default_rng(77)
+    checked = 0
+    for case in range(150):
+        V = int(rng.integers(2, 9))
+        row = bf16(rng.normal(0, 2, size=V).astype(np.float32))
+        temperature = float(rng.choice([0.7, 1.0, 1.3]))
+        p = float(np.float32(rng.choice([rng.uniform(0.05, 0.999), 1.0])))
+        k = int(rng.choice([-1, int(rng.integers(1, V + 1))]))
+        x = [float(v) for v in f32(row)]
+        z = [float(v) for v in O.scale_fp32(f32(row), temperature)]
+        keep, margin = _brute_support(z, p, k)
+        if margin is not None and margin < 1e-12:
+            continue
+        _, _, info = O.nucleus_row(row, V, temperature, p, k, 0)
+        want_thr = float("-inf") if len(keep) == V else min(x[j] for j in keep)
+        assert info.threshold == want_thr
+        with mpmath.workdps(40):
+            want = float(mpmath.log(mpmath.fsum(mpmath.exp(mpmath.mpf(z[j])) for j in keep)))
+        assert abs(info.lse_support - want) < 1e-12
+        checked += 1
+    assert checked > 100
+
+
+# --------------------------------------------------------------------------- gradient
+
+def _forward_mp(z, t_idx, keep, g_ref, g_pol, scale=None):
+    """g_ref * ref + g_pol * pol at 50 digits, for a fixed support `keep`
+    (the policy term is dropped when the target is outside it: pol is the
+    constant -inf there). `scale` divides z first (x-space evaluation)."""
+    zz = [mpmath.mpf(v) if scale is None else mpmath.mpf(v) / mpmath.mpf(scale) for v in z]
+    lse = mpmath.log(mpmath.fsum(mpmath.exp(v) for v in zz))
+    f = g_ref * (zz[t_idx] - lse)
+    if g_pol != 0 and t_idx in keep:
+        lse_s = mpmath.log(mpmath.fsum(mpmath.exp(zz[j]) for j in keep))
+        f += g_pol * (zz[t_idx] - lse_s)
+    return f
+
+
+def _grad_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    for case in range(n):
+        V = int(rng.integers(2, 9))
+        vals = rng.normal(0, 2, size=V).astype(np.float32)
+        if case % 5 == 0:
+            vals[int(rng.integers(V))] = -np.inf if V > 1 else vals[0]
+        row = bf16(vals)
+        if not np.isfinite(f32(row)).any():
+            continue
+        temperature = float(rng.choice([0.7, 1.0, 1.3]))
+        p = float(np.float32(rng.choice([rng.uniform(0.05, 0.999), 1.0])))
+        k = int(rng.choice([-1, int(rng.integers(1, V + 1))]))
+        t_idx = int(rng.choice(np.flatnonzero(np.isfinite(f32(row)))))  # -inf targets: test_grad_sums_to_zero...
+        g_ref = float(rng.choice([0.0, 1.0, -0.37]))
+        g_pol = float(rng.choice([0.0, 0.8, -1.9]))
+        if g_ref == 0.0 and g_pol == 0.0:
+            g_ref = 1.0
+        yield row, V, temperature, p, k, t_idx, g_ref, g_pol
+
+
+def test_grad_matches_50_digit_central_differences():
+    """d/dz_j of the forward at the float32 point z = fl32(x/T), by central
+    differences at 50 digits with the support held fixed (it is piecewise
+    constant), times dz/dx = 1/T."""
+    checked = 0
+    h = mpmath.mpf("1e-20")
+    for row, V, temperature, p, k, t_idx, g_ref, g_pol in _grad_cases(31, 160):
+        z = [float(v) for v in O.scale_fp32(f32(row), temperature)]
+        keep, margin = _brute_support([v if np.isfinite(v) else -1e300 for v in z], p, k)
+        if margin is not None and margin < 1e-12:
+            continue
+        got = O.grad_row(row, V + 3, V, temperature, t_idx, g_ref, g_pol, p, k)
+        assert np.all(got[V:] == 0.0)
+        with mpmath.workdps(50):
+            for j in range(V):
+                zp = list(z); zp[j] = mpmath.mpf(z[j]) + h
+                zm = list(z); zm[j] = mpmath.mpf(z[j]) - h
+                d = (_forward_mp(zp, t_idx, keep, g_ref, g_pol) - _forward_mp(zm, t_idx, keep, g_ref, g_pol)) / (2 * h)
+                want = float(d) / float(np.float32(temperature))
+                assert abs(got[j] - want) < 1e-12 * (1 + abs(want)), (row, temperature, p, k, t_idx, j, got[j], want)
+        checked += 1
+    assert checked > 100
+
+
+def test_grad_in_x_space_carries_the_temperature_factor():
+    """Differences of the forward in x itself (z = x/T at 50 digits, no float32
+    rounding): agrees with the gradient up to the float32 rounding of z."""
+    h = mpmath.mpf("1e-20")
+    rng = np.random.default_rng(5)
+    for _ in range(30):
+        V = 6
+        row = bf16(rng.normal(0, 2, size=V).astype(np.float32))
+        x = [float(v) for v in f32(row)]
+        for temperature in (0.5, 1.7):
+            t_idx = int(rng.integers(V))
+            got = O.grad_row(row, V, V, temperature, t_idx, 1.0, 0.0)
+            with mpmath.workdps(50):
+                for j in range(V):
+                    xp = list(x); xp[j] = mpmath.mpf(x[j]) + h
+                    xm = list(x); xm[j] = mpmath.mpf(x[j]) - h
+                    T = float(np.float32(temperature))
+                    d = (_forward_mp(xp, t_idx, set(), 1.0, 0.0, T) - _forward_mp(xm, t_idx, set(), 1.0, 0.0, T)) / (2 * h)
+                    assert abs(got[j] - float(d)) < 1e-6 * (1 + abs(float(d)))
+
+
+def test_grad_matches_torch_autograd_on_tiny_rows():
+    import torch
+    w = datagen.tiny()
+    logits, targets = w.generate()
+    for i in range(w.n_rows):
+        for p, k, g_ref, g_pol in ((1.0, -1, 1.0, 0.0), (0.9, -1, 0.3, -1.2), (0.95, 50, -0.5, 2.0), (1.0, 20, 0.0, 1.0)):
+            t_idx = int(targets[i]) if i % 2 else int(np.argmax(f32(logits[i][:1000])))
+            pol, _, info = O.nucleus_row(logits[i], 1000, 1.0, p, k, t_idx, want_mask=True)
+            z = torch.tensor(O.scale_fp32(f32(logits[i][:1000]), 1.0), dtype=torch.float64, requires_grad=True)
+            f = g_ref * torch.log_softmax(z, 0)[t_idx]
+            if np.isfinite(pol):
+                mask = torch.from_numpy(info.support_mask)
+                f = f + g_pol * (z[t_idx] - torch.logsumexp(z[mask], 0))
+            f.backward()
+            got = O.grad_row(logits[i], 1024, 1000, 1.0, t_idx, g_ref, g_pol, p, k)
+            assert np.allclose(got[:1000], z.grad.numpy(), rtol=1e-12, atol=1e-15)
+            assert np.all(got[1000:] == 0.0)
+
+
+def test_grad_sums_to_zero_and_special_rows():
+    w = datagen.tiny()
+    logits, targets = w.generate()
+    row, tg = logits[1], int(targets[1])
+    for p, k in ((1.0, -1), (0.9, -1), (0.5, 7)):
+        g = O.grad_row(row, 1024, 1000, 0.7, tg, 0.6, -1.4, p, k)
+        assert abs(math.fsum(g.tolist())) < 1e-12 and np.all(np.isfinite(g))
+    # zero upstream gradients: exact zeros, even for an invalid row
+    assert np.all(O.grad_row(row, 1024, 1000, float("nan"), tg, 0.0, 0.0) == 0.0)
+    # greedy rows: the logprob is piecewise constant
+    assert np.all(O.grad_row(row, 1024, 1000, 0.0, tg, 1.0, 1.0, 0.9, 5) == 0.0)
+    # invalid rows: NaN on the real columns, zeros on the pads
+    for t, target in ((float("nan"), tg), (-1.0, tg), (1.0, 1000), (1.0, -1)):
+        g = O.grad_row(row, 1024, 1000, t, target, 1.0)
+        assert np.all(np.isnan(g[:1000])) and np.all(g[1000:] == 0.0)
+    bad = row.copy(); bad[3] = 0x7FC0
+    assert np.all(np.isnan(O.grad_row(bad, 1024, 1000, 1.0, tg, 0.0, 1.0)[:1000]))
+    # invalid top-p: NaN only when the policy term is asked for
+    assert np.all(np.isnan(O.grad_row(row, 1024, 1000, 1.0, tg, 1.0, 1.0, 1.5, -1)[:1000]))
+    assert np.array_equal(O.grad_row(row, 1024, 1000, 1.0, tg, 1.0, 0.0, 1.5, -1), O.grad_row(row, 1024, 1000, 1.0, tg, 1.0))
+    # target outside the support: the policy term vanishes
+    _, _, info = O.nucleus_row(row, 1000, 1.0, 0.5, 3, 0, want_mask=True)
+    outside = int(np.flatnonzero(~info.support_mask)[0])
+    assert np.array_equal(O.grad_row(row, 1024, 1000, 1.0, outside, 0.7, 5.0, 0.5, 3),
+                          O.grad_row(row, 1024, 1000, 1.0, outside, 0.7, 0.0))
+    # a -inf target: its logprob is -inf but d/dx_t = (1 - p_t) / T = 1 / T, the rest -p_j / T (sum 0)
+    neg = row.copy(); neg[9] = datagen.BF16_NEG_INF
+    g = O.grad_row(neg, 1024, 1000, 2.0, 9, 1.0)
+    assert g[9] == 0.5 and abs(math.fsum(g.tolist())) < 1e-12
+    # disabled support: the policy term equals the reference term
+    a = O.grad_row(row, 1024, 1000, 1.3, tg, 0.25, 0.5)
+    b = O.grad_row(row, 1024, 1000, 1.3, tg, 0.75, 0.0)
+    assert np.allclose(a, b, rtol=1e-14, atol=1e-18)
