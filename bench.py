@@ -16,8 +16,10 @@ between two device synchronisations); `roofline.achieved` is the algorithmic
 bytes of one launch divided by the average launch time measured with HIP
 events on the launch stream over the same region. `cpu_baseline` times the
 CPU oracle (float64 numpy, one core) on a bounded sample of the same rows.
-`secondary` reports rlk_logp_nucleus on the top-p 0.95 workload and on the
-per-request workload (64 requests x 128 rows), for information.
+`secondary` reports rlk_logp_nucleus on the top-p 0.95 workload, the
+backward (rlk_logp_backward) on it, rlk_logp_nucleus on the per-request
+workload (64 requests x 128 rows) and the vocabulary-parallel form, for
+information.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -40,6 +42,7 @@ KERNEL_SOURCES = [
     os.path.join(ROOT, "invariant_token_log_fp32_amd", "csrc", "rlk_logp.hip"),
     os.path.join(ROOT, "invariant_token_log_fp32_amd", "csrc", "logp_device.hpp"),
     os.path.join(ROOT, "invariant_token_log_fp32_amd", "csrc", "support.hpp"),
+    os.path.join(ROOT, "invariant_token_log_fp32_amd", "csrc", "backward.hpp"),
 ]
 
 
@@ -72,6 +75,12 @@ def bytes_full(n_rows: int, vocab_real: int) -> int:
 def bytes_nucleus(n_rows: int, vocab_real: int) -> int:
     # real logits (read once) + target + temperature + top-p + top-k + two outputs
     return n_rows * (vocab_real * 2 + 8 + 4 + 4 + 4 + 8)
+
+
+def bytes_backward(n_rows: int, vocab_real: int, vocab_padded: int, policy: bool) -> int:
+    # real logits read once + gradient row written once (pads included) + per-row
+    # temperature, target, ref, lse, upstream gradient (+ policy, support record, upstream gradient)
+    return n_rows * (vocab_real * 2 + vocab_padded * 2 + 4 + 8 + 4 + 4 + 4 + (24 if policy else 0))
 
 
 def cpu_baseline(workload, logits, targets, rows: int):
@@ -214,6 +223,27 @@ def main():
         sec.append({"workload": "nucleus: same logits, top-p 0.95, top-k off, T 0.7", "entry_point":
                     "rlk_logp_nucleus", "ms_per_step": ms_n, "tokens_per_s": w.n_rows / (ms_n * 1e-3),
                     "achieved_GBs": ab / (ms_n * 1e-3) / 1e9, "frac": ab / (ms_n * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        # backward of both terms (and of the reference term alone) from the nucleus forward's statistics
+        lse = torch.empty(w.n_rows, dtype=torch.float32, device=dev)
+        state = torch.empty((w.n_rows, 4), dtype=torch.int32, device=dev)
+        rlk.logp_nucleus(lg_a, temp, pp, pk, tg, vocab_real=w.vocab_real, return_state=True, policy_out=pol,
+                         ref_out=ref, lse_out=lse, state_out=state, workspace=wsn)
+        gen = torch.Generator(device=dev).manual_seed(7)
+        g_r = torch.randn(w.n_rows, generator=gen, device=dev)
+        g_p = torch.randn(w.n_rows, generator=gen, device=dev)
+        grad = torch.empty((w.n_rows, w.vocab_padded), dtype=torch.bfloat16, device=dev)
+        for policy in (True, False):
+            kw = dict(policy_logp=pol, support_state=state, grad_policy=g_p) if policy else {}
+            _, ms_b = time_calls(lambda i: rlk.logp_backward(
+                bufs[0], temp, tg, vocab_real=w.vocab_real, ref_logp=ref, lse=lse, grad_ref=g_r, out=grad, **kw),
+                20, 5)
+            bb = bytes_backward(w.n_rows, w.vocab_real, w.vocab_padded, policy)
+            sec.append({"workload": "backward: same logits, " + ("reference + top-p 0.95 policy terms" if policy
+                        else "reference term only") + ", BF16 gradient 8192 x 152576",
+                        "entry_point": "rlk_logp_backward", "ms_per_step": ms_b,
+                        "tokens_per_s": w.n_rows / (ms_b * 1e-3), "algorithmic_bytes_per_launch": bb,
+                        "achieved_GBs": bb / (ms_b * 1e-3) / 1e9, "frac": bb / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        del grad
         wr = datagen.per_request()
         lg_r, tg_r = wr.generate()
         lg_r = (torch.from_numpy(lg_r.view(np.int16)).to(dev),) * 2

@@ -67,7 +67,7 @@ enum {
   RLK_OK = 0,
   RLK_ERR_NULL = -1,      /* a required pointer is NULL */
   RLK_ERR_ALIGN = -2,     /* logits/workspace not 16-byte aligned, or another array misaligned */
-  RLK_ERR_SHAPE = -3,     /* n_rows or a layout field out of range */
+  RLK_ERR_SHAPE = -3,     /* n_rows (0 .. 2^22) or a layout field out of range */
   RLK_ERR_GROUPS = -4,    /* groups is not 1, 2, 4 or 8 */
   RLK_ERR_WORKSPACE = -5, /* workspace missing or smaller than rlk_logp_workspace_bytes() */
   RLK_ERR_HIP = -6        /* the HIP runtime reported an error when launching */
@@ -105,6 +105,22 @@ int32_t rlk_logp_full(const uint16_t* logits, int64_t n_rows, const rlk_vocab_la
                       float* logp_out, float* lse_out,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Per-row record of the support decision, written by rlk_logp_nucleus and read
+ * by rlk_logp_backward [CFG-KL]. */
+typedef struct rlk_support_state {
+  float lse_support; /* log of the sum of exp(z_j) over the support (natural log);
+                        equal to lse when the support is the whole real vocabulary;
+                        NaN for greedy and invalid rows */
+  float threshold;   /* smallest kept BF16 logit value: column j < vocab_real is in
+                        the support iff x_j >= threshold; -inf when the support is
+                        the whole real vocabulary */
+  int32_t status;    /* 1: the target is in the support (policy logprob finite or
+                        -inf only through a -inf target logit); 0: the target is
+                        outside it (policy -inf); -1: invalid top_p / top_k (policy
+                        NaN); -2: invalid row (reference NaN) */
+  int32_t reserved;  /* 0 */
+} rlk_support_state;
+
 /* Policy logprob over the top-k-then-top-p support, and the full-vocabulary
  * reference logprob used for KL [CFG-SAMPLING], [CFG-KL], [CFG-CMDS].
  * Support of row i: top-k (when top_k[i] != -1 and < vocab_real) keeps every
@@ -118,6 +134,9 @@ int32_t rlk_logp_full(const uint16_t* logits, int64_t n_rows, const rlk_vocab_la
  *                   (outside (0, 1]) or top_k (not -1 and not in
  *                   [1, vocab_real]).
  *   ref_out[i]    = byte-identical to rlk_logp_full's logp_out[i].
+ *   lse_out        [n_rows] float32, byte-identical to rlk_logp_full's
+ *                  lse_out, or NULL.
+ *   support_out    [n_rows] rlk_support_state (16 bytes each), or NULL.
  *   top_p  [n_rows] float32;  top_k [n_rows] int32.
  *   workspace      rlk_logp_workspace_bytes(n_rows, layout, 1) bytes, 16-byte
  *                  aligned; may be NULL when that size is 0 (groups == 1).
@@ -127,7 +146,48 @@ int32_t rlk_logp_full(const uint16_t* logits, int64_t n_rows, const rlk_vocab_la
 int32_t rlk_logp_nucleus(const uint16_t* logits, int64_t n_rows, const rlk_vocab_layout* layout,
                          const float* temperature, const float* top_p, const int32_t* top_k,
                          const int64_t* target, float* policy_out, float* ref_out,
+                         float* lse_out, rlk_support_state* support_out,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Gradient of sum_i (grad_ref[i] * ref_i + grad_policy[i] * policy_i) with
+ * respect to the BF16 logits, as BF16 (round to nearest even), for training
+ * on these logprobs (page "H100 canonical CP backward validation", Change
+ * section: the training step back-propagates through the logprob; [CFG-KL]
+ * for the two terms). For a row with temperature T > 0 and target t:
+ *   d/dx_j = ( [j == t] * (g_r + g_p) - g_r * p_j - g_p * [x_j >= thr] * q_j ) / T
+ * with p_j = exp(z_j - lse), q_j = exp(z_j - lse_support), g_r = grad_ref[i],
+ * g_p = grad_policy[i] when the target is in the support (status 1) and 0
+ * when it is outside (the policy logprob is the constant -inf there). The
+ * support is piecewise constant in the logits and contributes no term. The
+ * target column is formed as (g_r * -expm1(ref) + g_p * -expm1(policy)) / T,
+ * which keeps 1 - p_t accurate when p_t is near 1.
+ *   logits        as for the forward call that produced the row statistics
+ *   temperature, target  as for the forward call
+ *   ref_logp, lse [n_rows] float32: logp_out and lse_out of rlk_logp_full
+ *                 (or ref_out and lse_out of rlk_logp_nucleus) on these rows
+ *   grad_ref      [n_rows] float32 upstream gradient of ref_i, or NULL (no
+ *                 reference term; ref_logp and lse may then be NULL)
+ *   policy_logp, support  [n_rows] policy_out and support_out of
+ *                 rlk_logp_nucleus on these rows
+ *   grad_policy   [n_rows] float32 upstream gradient of policy_i, or NULL (no
+ *                 policy term; policy_logp and support may then be NULL)
+ *   grad_logits   [n_rows * grad_stride] BF16 bits, 16-byte aligned; columns
+ *                 [0, vocab_padded) of each row are written (pad columns get
+ *                 0), columns beyond are left untouched
+ *   grad_stride   >= vocab_padded and a multiple of 8
+ * Row rules, in order: both upstream gradients 0 -> zeros; an invalid row
+ * (invalid temperature or target, ref NaN, or status -2) -> NaN on the real
+ * columns; T == 0 (greedy: piecewise-constant logprob) -> zeros; a nonzero
+ * grad_policy with status -1 -> NaN on the real columns. The pad columns are
+ * always 0. Each output depends only on its own row's inputs, so the bytes do
+ * not change with the batch or `groups` (which is not used here).
+ * At least one of grad_ref / grad_policy must be given (else RLK_ERR_NULL).
+ * Returns RLK_OK or a negative status; n_rows == 0 enqueues nothing. */
+int32_t rlk_logp_backward(const uint16_t* logits, int64_t n_rows, const rlk_vocab_layout* layout,
+                          const float* temperature, const int64_t* target,
+                          const float* ref_logp, const float* lse, const float* grad_ref,
+                          const float* policy_logp, const rlk_support_state* support, const float* grad_policy,
+                          uint16_t* grad_logits, int64_t grad_stride, hipStream_t stream);
 
 /* Vocabulary-parallel form [REPRO-CANON], [CFG-TOPOLOGY]: with `groups` = G
  * ranks, rank r holds the columns [r*C, (r+1)*C) of every row, C = 8/G shards

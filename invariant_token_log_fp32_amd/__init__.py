@@ -17,7 +17,8 @@ from typing import Optional, Tuple, Union
 
 __all__ = [
     "LIB_PATH", "HEADER_PATH", "VocabLayout", "load_library", "status_string", "workspace_bytes",
-    "summary_bytes", "logp_full", "logp_nucleus", "logp_shard_summaries", "logp_merge", "RlkError", "N_SHARDS",
+    "summary_bytes", "logp_full", "logp_nucleus", "logp_shard_summaries", "logp_merge", "logp_backward",
+    "support_state_fields", "RlkError", "N_SHARDS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -65,7 +66,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lay = ctypes.POINTER(VocabLayout)
     lib.rlk_logp_full.argtypes = [vp, i64, lay, vp, vp, vp, vp, vp, sz, vp]
     lib.rlk_logp_full.restype = i32
-    lib.rlk_logp_nucleus.argtypes = [vp, i64, lay, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.rlk_logp_nucleus.argtypes = [vp, i64, lay, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.rlk_logp_nucleus.restype = i32
     lib.rlk_logp_workspace_bytes.argtypes = [i64, lay, i32]
     lib.rlk_logp_workspace_bytes.restype = sz
@@ -77,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rlk_logp_merge.restype = i32
     lib.rlk_logp_summary_bytes.argtypes = [i64, lay]
     lib.rlk_logp_summary_bytes.restype = sz
+    lib.rlk_logp_backward.argtypes = [vp, i64, lay, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
+    lib.rlk_logp_backward.restype = i32
     _lib = lib
     return lib
 
@@ -180,11 +183,14 @@ def logp_full(logits, temperature: Union[float, "torch.Tensor"], target, *, voca
 
 
 def logp_nucleus(logits, temperature, top_p, top_k, target, *, vocab_real: int,
-                 vocab_padded: Optional[int] = None, groups: int = 1, policy_out=None, ref_out=None,
-                 workspace=None, stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+                 vocab_padded: Optional[int] = None, groups: int = 1, return_state: bool = False,
+                 policy_out=None, ref_out=None, lse_out=None, state_out=None, workspace=None, stream=None):
     """Policy logprob over the top-k-then-top-p support and the full-vocabulary
     reference logprob (rlk_logp_nucleus). ``top_p`` float or float32 [n_rows],
-    ``top_k`` int or int32 [n_rows]. Returns (policy, reference)."""
+    ``top_k`` int or int32 [n_rows]. Returns (policy, reference), or with
+    ``return_state`` (policy, reference, lse, state) where ``state`` is the
+    int32 [n_rows, 4] view of the rlk_support_state records (see
+    ``support_state_fields``)."""
     torch = _torch()
     stride = _check_logits(logits)
     n = logits.shape[0]
@@ -196,6 +202,9 @@ def logp_nucleus(logits, temperature, top_p, top_k, target, *, vocab_real: int,
     target = _per_row(target, n, torch.int64, dev, "target")
     policy_out = policy_out if policy_out is not None else torch.empty(n, dtype=torch.float32, device=dev)
     ref_out = ref_out if ref_out is not None else torch.empty(n, dtype=torch.float32, device=dev)
+    if return_state:
+        lse_out = lse_out if lse_out is not None else torch.empty(n, dtype=torch.float32, device=dev)
+        state_out = state_out if state_out is not None else torch.empty((n, 4), dtype=torch.int32, device=dev)
     lay = make_layout(vp, vocab_real, stride, groups)
     lib = load_library()
     need = int(lib.rlk_logp_workspace_bytes(n, ctypes.byref(lay), 1))
@@ -204,11 +213,65 @@ def logp_nucleus(logits, temperature, top_p, top_k, target, *, vocab_real: int,
     st = lib.rlk_logp_nucleus(
         logits.data_ptr(), n, ctypes.byref(lay), temperature.data_ptr(), top_p.data_ptr(),
         top_k.data_ptr(), target.data_ptr(), policy_out.data_ptr(), ref_out.data_ptr(),
+        lse_out.data_ptr() if lse_out is not None else None,
+        state_out.data_ptr() if state_out is not None else None,
         workspace.data_ptr() if workspace is not None else None,
         workspace.numel() if workspace is not None else 0, _stream_handle(stream, dev))
     if st != RLK_OK:
         raise RlkError(st, "rlk_logp_nucleus")
+    if return_state:
+        return policy_out, ref_out, lse_out, state_out
     return policy_out, ref_out
+
+
+def support_state_fields(state):
+    """(lse_support float32, threshold float32, status int32) columns of an
+    int32 [n_rows, 4] tensor of rlk_support_state records."""
+    torch = _torch()
+    return state[:, 0].view(torch.float32), state[:, 1].view(torch.float32), state[:, 2]
+
+
+def logp_backward(logits, temperature, target, *, vocab_real: int, vocab_padded: Optional[int] = None,
+                  ref_logp=None, lse=None, grad_ref=None, policy_logp=None, support_state=None, grad_policy=None,
+                  out=None, stream=None):
+    """BF16 gradient of sum_i (grad_ref[i] * ref_i + grad_policy[i] * policy_i)
+    with respect to the logits (rlk_logp_backward). ``ref_logp``/``lse`` come
+    from logp_full (or logp_nucleus with ``return_state``), ``policy_logp`` and
+    ``support_state`` from logp_nucleus; a term whose upstream gradient is None
+    is absent. Upstream gradients are floats or float32 [n_rows] tensors.
+    Returns a bfloat16 [n_rows, vocab_padded] tensor (or fills ``out``, a 2-D
+    BF16-bits tensor whose first vocab_padded columns are written)."""
+    torch = _torch()
+    stride = _check_logits(logits)
+    n = logits.shape[0]
+    dev = logits.device
+    vp = int(vocab_padded if vocab_padded is not None else logits.shape[1])
+    temperature = _per_row(temperature, n, torch.float32, dev, "temperature")
+    target = _per_row(target, n, torch.int64, dev, "target")
+    if grad_ref is not None:
+        grad_ref = _per_row(grad_ref, n, torch.float32, dev, "grad_ref")
+        ref_logp = _per_row(ref_logp, n, torch.float32, dev, "ref_logp")
+        lse = _per_row(lse, n, torch.float32, dev, "lse")
+    if grad_policy is not None:
+        grad_policy = _per_row(grad_policy, n, torch.float32, dev, "grad_policy")
+        policy_logp = _per_row(policy_logp, n, torch.float32, dev, "policy_logp")
+        if support_state.dtype != torch.int32 or support_state.shape != (n, 4) or not support_state.is_contiguous():
+            raise ValueError(f"support_state must be a contiguous int32 tensor of shape ({n}, 4)")
+    if out is None:
+        out = torch.empty((n, vp), dtype=torch.bfloat16, device=dev)
+    out_stride = _check_logits(out)
+    lay = make_layout(vp, vocab_real, stride, 1)
+
+    def ptr(t):
+        return t.data_ptr() if t is not None else None
+
+    st = load_library().rlk_logp_backward(
+        logits.data_ptr(), n, ctypes.byref(lay), temperature.data_ptr(), target.data_ptr(),
+        ptr(ref_logp), ptr(lse), ptr(grad_ref), ptr(policy_logp), ptr(support_state), ptr(grad_policy),
+        out.data_ptr(), int(out_stride), _stream_handle(stream, dev))
+    if st != RLK_OK:
+        raise RlkError(st, "rlk_logp_backward")
+    return out
 
 
 def logp_shard_summaries(logits_slice, temperature, target, *, rank: int, groups: int, vocab_real: int,

@@ -17,6 +17,10 @@
 //                      integer histogram, and the policy logprob.
 //   k_nucleus          groups > 1: the same per-row support search on the
 //                      summaries k_rank_summaries stored.
+//   k_backward         gradient of the reference and policy logprobs with
+//                      respect to the BF16 logits, from the forward's per-row
+//                      statistics; 1024-thread workgroups over (row, column
+//                      chunk) items in row-major order (backward.hpp).
 // Passages: RL-Kernel page "Configurable H100 consistency runs" (sampling,
 // topology and mode/KL paragraphs; top-k independent of top-p in the command
 // examples) and page "Reproduce and profile the Qwen3-8B TP4/CP2 experiment",
@@ -27,6 +31,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "backward.hpp"
 #include "logp_device.hpp"
 #include "rlk_logp.h"
 #include "support.hpp"
@@ -141,7 +146,8 @@ __global__ __launch_bounds__(256) void k_merge(const ShardSummary* __restrict__ 
 __global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_nucleus_g1(
     const uint16_t* __restrict__ logits, int64_t row_stride, int shard_width, int64_t vocab_real,
     const float* __restrict__ temperature, const float* __restrict__ top_p, const int32_t* __restrict__ top_k,
-    const int64_t* __restrict__ target, float* __restrict__ policy_out, float* __restrict__ ref_out) {
+    const int64_t* __restrict__ target, float* __restrict__ policy_out, float* __restrict__ ref_out,
+    float* __restrict__ lse_out, rlk_support_state* __restrict__ state_out) {
   __shared__ NucLds L;
   const int64_t row = blockIdx.x;
   const int wave = threadIdx.x / kWave;
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(4, 
     if ((threadIdx.x & (kWave - 1)) == 0) L.sm[wave] = s;
   }
   __syncthreads();
-  nucleus_row(L, rowp, row, vocab_real, shard_width, t, p, k, tg, true, policy_out, ref_out);
+  nucleus_row(L, rowp, row, vocab_real, shard_width, t, p, k, tg, true, policy_out, ref_out, lse_out, state_out);
 }
 
 __global__ __launch_bounds__(kNucThreads) void k_nucleus(const uint16_t* __restrict__ logits, int64_t row_stride,
@@ -175,7 +181,9 @@ __global__ __launch_bounds__(kNucThreads) void k_nucleus(const uint16_t* __restr
                                                          const int32_t* __restrict__ top_k,
                                                          const int64_t* __restrict__ target,
                                                          const ShardSummary* __restrict__ ws,
-                                                         float* __restrict__ policy_out, float* __restrict__ ref_out) {
+                                                         float* __restrict__ policy_out, float* __restrict__ ref_out,
+                                                         float* __restrict__ lse_out,
+                                                         rlk_support_state* __restrict__ state_out) {
   __shared__ NucLds L;
   const int64_t row = blockIdx.x;
   if (threadIdx.x < kShards) {
@@ -184,19 +192,94 @@ __global__ __launch_bounds__(kNucThreads) void k_nucleus(const uint16_t* __restr
   }
   __syncthreads();
   nucleus_row(L, logits + row * row_stride, row, vocab_real, shard_width, temperature[row], top_p[row], top_k[row],
-              target[row], false, policy_out, ref_out);
+              target[row], false, policy_out, ref_out, lse_out, state_out);
+}
+
+// ----------------------------------------------------------------------------
+// Backward: see backward.hpp. Row rules in order: both upstream gradients 0
+// -> zeros; invalid row -> NaN (real columns); greedy -> zeros; a policy
+// gradient with invalid top-p/top-k -> NaN; else the gradient.
+// ----------------------------------------------------------------------------
+// Per-row set-up of the gradient; returns 0 to compute, 1 for zeros, 2 for NaN.
+__device__ __forceinline__ int backward_row(int64_t row, int64_t vocab_real, const float* __restrict__ temperature,
+                                            const int64_t* __restrict__ target, const float* __restrict__ ref_logp,
+                                            const float* __restrict__ lse, const float* __restrict__ grad_ref,
+                                            const float* __restrict__ policy_logp,
+                                            const rlk_support_state* __restrict__ support,
+                                            const float* __restrict__ grad_pol, BwdRow& R, bool& policy) {
+  const float t = temperature[row];
+  const int64_t tg = target[row];
+  const float gr = grad_ref ? grad_ref[row] : 0.0f;
+  const float gp = grad_pol ? grad_pol[row] : 0.0f;
+  if (gr == 0.0f && gp == 0.0f) return 1;
+  const float ref = grad_ref ? ref_logp[row] : 0.0f;
+  const int status = grad_pol ? support[row].status : 1;
+  const bool invalid = !temperature_valid(t) || tg < 0 || tg >= vocab_real || (ref != ref) || status == -2;
+  if (invalid) return 2;
+  if (t == 0.0f) return 1;
+  if (gp != 0.0f && status == -1) return 2;
+  R.c = kLog2e / t;
+  R.a_r = grad_ref ? static_cast<float>(-static_cast<double>(lse[row]) * 1.4426950408889634) : 0.0f;
+  R.s_r = -gr / t;
+  const float gpe = (status == 1) ? gp : 0.0f;
+  R.s_p = -gpe / t;
+  R.a_p = 0.0f;
+  R.thr = INFINITY;
+  float tpol = 0.0f;
+  if (gpe != 0.0f) {
+    const rlk_support_state st = support[row];
+    R.a_p = static_cast<float>(-static_cast<double>(st.lse_support) * 1.4426950408889634);
+    R.thr = st.threshold;
+    tpol = gpe * -expm1f(policy_logp[row]);
+  }
+  const float tref = (gr != 0.0f) ? gr * -expm1f(ref) : 0.0f;
+  R.g_t = (tref + tpol) / t;
+  R.vt = tg / 8;
+  R.et = static_cast<int>(tg % 8);
+  policy = gpe != 0.0f;
+  return 0;
+}
+
+__global__ __launch_bounds__(kBwdThreads) void k_backward(
+    const uint16_t* __restrict__ logits, int64_t row_stride, int64_t vocab_real, int64_t vocab_padded,
+    const float* __restrict__ temperature, const int64_t* __restrict__ target, const float* __restrict__ ref_logp,
+    const float* __restrict__ lse, const float* __restrict__ grad_ref, const float* __restrict__ policy_logp,
+    const rlk_support_state* __restrict__ support, const float* __restrict__ grad_pol,
+    uint16_t* __restrict__ grad_out, int64_t grad_stride, int64_t chunks, int64_t n_items) {
+  const int64_t nv = vocab_padded / 8;
+  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {  // uniform across the workgroup
+    const int64_t row = item / chunks;
+    const int64_t v0 = (item % chunks) * kBwdChunk;
+    const int64_t v1 = (v0 + kBwdChunk < nv) ? v0 + kBwdChunk : nv;
+    uint16_t* __restrict__ outp = grad_out + row * grad_stride;
+    BwdRow R;
+    bool policy = false;
+    const int mode = backward_row(row, vocab_real, temperature, target, ref_logp, lse, grad_ref, policy_logp,
+                                  support, grad_pol, R, policy);
+    if (mode == 1) {
+      fill_chunk(outp, vocab_real, v0, v1, 0u);
+    } else if (mode == 2) {
+      fill_chunk(outp, vocab_real, v0, v1, 0x7FC07FC0u);
+    } else if (policy) {
+      grad_chunk<true>(logits + row * row_stride, outp, vocab_real, v0, v1, R);
+    } else {
+      grad_chunk<false>(logits + row * row_stride, outp, vocab_real, v0, v1, R);
+    }
+  }
 }
 
 // ----------------------------------------------------------------------------
 // Host side
 // ----------------------------------------------------------------------------
 constexpr int64_t kMaxVocab = int64_t(1) << 30;
+constexpr int64_t kMaxRows = int64_t(1) << 22;       // one workgroup per row: rows * 1024 threads < 2^32
+constexpr int64_t kMaxBwdBlocks = int64_t(1) << 21;  // backward grid cap; larger jobs loop over items
 
 static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 static int32_t check_layout(int64_t n_rows, const rlk_vocab_layout* L) {
   if (L == nullptr) return RLK_ERR_NULL;
-  if (n_rows < 0) return RLK_ERR_SHAPE;
+  if (n_rows < 0 || n_rows > kMaxRows) return RLK_ERR_SHAPE;
   if (L->n_shards != kShards) return RLK_ERR_SHAPE;
   if (L->vocab_padded < 8 * kShards || L->vocab_padded > kMaxVocab) return RLK_ERR_SHAPE;
   if (L->vocab_padded % (8 * kShards) != 0) return RLK_ERR_SHAPE;
@@ -292,15 +375,16 @@ int32_t rlk_logp_full(const uint16_t* logits, int64_t n_rows, const rlk_vocab_la
 
 int32_t rlk_logp_nucleus(const uint16_t* logits, int64_t n_rows, const rlk_vocab_layout* layout,
                          const float* temperature, const float* top_p, const int32_t* top_k, const int64_t* target,
-                         float* policy_out, float* ref_out, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+                         float* policy_out, float* ref_out, float* lse_out, rlk_support_state* support_out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
   using namespace rlk;
   int32_t st = check_layout(n_rows, layout);
   if (st != RLK_OK) return st;
   if (n_rows == 0) return RLK_OK;  // nothing to read or write: pointers may be NULL
   if (!logits || !temperature || !top_p || !top_k || !target || !policy_out || !ref_out) return RLK_ERR_NULL;
   if (!aligned(logits, 16) || !aligned(temperature, 4) || !aligned(top_p, 4) || !aligned(top_k, 4) ||
-      !aligned(target, 8) || !aligned(policy_out, 4) || !aligned(ref_out, 4))
+      !aligned(target, 8) || !aligned(policy_out, 4) || !aligned(ref_out, 4) || (lse_out && !aligned(lse_out, 4)) ||
+      (support_out && !aligned(support_out, 16)))
     return RLK_ERR_ALIGN;
   const size_t need = rlk::workspace_bytes(n_rows, layout, true);
   if (need > 0) {
@@ -311,14 +395,15 @@ int32_t rlk_logp_nucleus(const uint16_t* logits, int64_t n_rows, const rlk_vocab
   const int G = layout->groups;
   if (G == 1) {
     k_nucleus_g1<<<dim3(static_cast<unsigned>(n_rows)), dim3(kNucThreads), 0, stream>>>(
-        logits, layout->row_stride, S, layout->vocab_real, temperature, top_p, top_k, target, policy_out, ref_out);
+        logits, layout->row_stride, S, layout->vocab_real, temperature, top_p, top_k, target, policy_out, ref_out,
+        lse_out, support_out);
     return launched();
   }
   ShardSummary* ws = static_cast<ShardSummary*>(workspace);
   if ((st = launch_all_ranks(logits, n_rows, layout, temperature, target, ws, stream)) != RLK_OK) return st;
   k_nucleus<<<dim3(static_cast<unsigned>(n_rows)), dim3(kNucThreads), 0, stream>>>(
       logits, layout->row_stride, n_rows, kShards / G, S, layout->vocab_real, temperature, top_p, top_k, target, ws,
-      policy_out, ref_out);
+      policy_out, ref_out, lse_out, support_out);
   return launched();
 }
 
@@ -363,6 +448,34 @@ int32_t rlk_logp_merge(const void* summaries, size_t summaries_bytes, int64_t n_
   k_merge<<<dim3(blocks), dim3(256), 0, stream>>>(static_cast<const ShardSummary*>(summaries), n_rows,
                                                   kShards / layout->groups, S, layout->vocab_real, temperature, target,
                                                   logp_out, lse_out);
+  return launched();
+}
+
+int32_t rlk_logp_backward(const uint16_t* logits, int64_t n_rows, const rlk_vocab_layout* layout,
+                          const float* temperature, const int64_t* target, const float* ref_logp, const float* lse,
+                          const float* grad_ref, const float* policy_logp, const rlk_support_state* support,
+                          const float* grad_policy, uint16_t* grad_logits, int64_t grad_stride, hipStream_t stream) {
+  using namespace rlk;
+  int32_t st = check_layout(n_rows, layout);
+  if (st != RLK_OK) return st;
+  if (grad_stride < layout->vocab_padded || grad_stride % 8 != 0) return RLK_ERR_SHAPE;
+  if (n_rows > 0 && grad_stride > INT64_MAX / 2 / n_rows) return RLK_ERR_SHAPE;
+  if (n_rows == 0) return RLK_OK;
+  if (!logits || !temperature || !target || !grad_logits) return RLK_ERR_NULL;
+  if (!grad_ref && !grad_policy) return RLK_ERR_NULL;
+  if (grad_ref && (!ref_logp || !lse)) return RLK_ERR_NULL;
+  if (grad_policy && (!policy_logp || !support)) return RLK_ERR_NULL;
+  if (!aligned(logits, 16) || !aligned(grad_logits, 16) || !aligned(temperature, 4) || !aligned(target, 8) ||
+      (grad_ref && (!aligned(grad_ref, 4) || !aligned(ref_logp, 4) || !aligned(lse, 4))) ||
+      (grad_policy && (!aligned(grad_policy, 4) || !aligned(policy_logp, 4) || !aligned(support, 16))))
+    return RLK_ERR_ALIGN;
+  const int64_t chunks = (layout->vocab_padded / 8 + kBwdChunk - 1) / kBwdChunk;
+  const int64_t n_items = n_rows * chunks;
+  const int64_t grid = n_items < kMaxBwdBlocks ? n_items : kMaxBwdBlocks;
+  k_backward<<<dim3(static_cast<unsigned>(grid)), dim3(kBwdThreads), 0, stream>>>(
+      logits, layout->row_stride, layout->vocab_real, layout->vocab_padded, temperature, target,
+      grad_ref ? ref_logp : nullptr, grad_ref ? lse : nullptr, grad_ref, grad_policy ? policy_logp : nullptr,
+      grad_policy ? support : nullptr, grad_policy, grad_logits, grad_stride, chunks, n_items);
   return launched();
 }
 

@@ -33,6 +33,7 @@
 #pragma once
 
 #include "logp_device.hpp"
+#include "rlk_logp.h"
 
 namespace rlk {
 
@@ -61,6 +62,17 @@ __device__ __forceinline__ uint32_t crank16(uint32_t b) { return (b & 0x8000u) ?
 
 // Inverse of crank16.
 __device__ __forceinline__ uint32_t crank_bits(uint32_t r) { return (r < 0x4C80u) ? (0xFFFFu - r) : (r - 0x1901u); }
+
+// BF16 value of window slot j (j < kWin).
+__device__ __forceinline__ float slot_value(int j) {
+  return __uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(j)) << 16);
+}
+
+// BF16 value of a key16 (the +0 key for the folded zeros).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  const uint32_t b = (key & 0x8000u) ? (key & 0x7FFFu) : (~key & 0xFFFFu);
+  return __uint_as_float(b << 16);
+}
 
 // Window slot of a BF16 pattern (kWinHi - rank), or kWin (the trash slot) for
 // -inf, NaN, +-inf, |x| < 2^-24 and values outside the window.
@@ -734,14 +746,16 @@ __device__ __forceinline__ bool search_needed(float t, float p, int64_t k, int64
 // ---------------------------------------------------------------------------
 // Whole-row driver: L.sm must hold the row's 8 shard summaries; when
 // `window_built` the window and the hook totals are already filled (the
-// streaming pass counted the row). Writes ref_out[row] and policy_out[row].
+// streaming pass counted the row). Writes ref_out[row], policy_out[row] and,
+// when given, lse_out[row] and state_out[row].
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restrict__ rowp, int64_t row,
                                             int64_t vocab_real, int shard_width, float t, float p, int64_t k,
                                             int64_t tg, bool window_built, float* __restrict__ policy_out,
-                                            float* __restrict__ ref_out) {
+                                            float* __restrict__ ref_out, float* __restrict__ lse_out,
+                                            rlk_support_state* __restrict__ state_out) {
   const int tid = threadIdx.x;
-  float ref = NAN, zt = NAN;
+  float ref = NAN, zt = NAN, lse = NAN;
   uint32_t bt = 0;
   if (tid == 0) {
     const bool tok = (tg >= 0) && (tg < vocab_real);
@@ -749,13 +763,24 @@ __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restric
     const float xt = __uint_as_float(bt << 16);
     const RowMerge mr = merge_row(L.sm, t, tok, tg, shard_width);
     ref = mr.logp;
+    lse = mr.lse;
     ref_out[row] = ref;
+    if (lse_out) lse_out[row] = lse;
     const bool p_ok = (p > 0.0f) && (p <= 1.0f);
     const bool k_ok = (k == -1) || (k >= 1 && k <= vocab_real);
     L.search = 0;
     float pol = ref;
-    if (!mr.ok || !p_ok || !k_ok) {
+    rlk_support_state st;
+    st.lse_support = lse;
+    st.threshold = -INFINITY;
+    st.status = 1;
+    st.reserved = 0;
+    if (!mr.ok) {
       pol = NAN;
+      st.status = -2;
+    } else if (!p_ok || !k_ok) {
+      pol = NAN;
+      st.status = -1;
     } else if (search_needed(t, p, k, vocab_real)) {
       L.search = 1;
       L.k_active = (k != -1) && (k < vocab_real);
@@ -765,7 +790,10 @@ __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restric
       L.c = kLog2e / t;
       zt = xt / t;
     }
-    if (!L.search) policy_out[row] = pol;
+    if (!L.search) {
+      policy_out[row] = pol;
+      if (state_out) state_out[row] = st;
+    }
   }
   __syncthreads();
   if (!L.search) return;
@@ -787,16 +815,27 @@ __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restric
     in_support = (tid == 0) && tclass <= L.kappa;
   }
   if (tid == 0) {
+    const bool whole = static_cast<int64_t>(L.cnt_s) == vocab_real;
+    const double lse_s = (static_cast<double>(L.R) + (log2(static_cast<double>(L.z_s)) - 40.0)) * kLn2;
     float pol;
     if (!in_support) {
       pol = -INFINITY;
-    } else if (static_cast<int64_t>(L.cnt_s) == vocab_real) {
+    } else if (whole) {
       pol = ref;
     } else {
-      const double lse_s = (static_cast<double>(L.R) + (log2(static_cast<double>(L.z_s)) - 40.0)) * kLn2;
       pol = static_cast<float>(static_cast<double>(zt) - lse_s);
     }
     policy_out[row] = pol;
+    if (state_out) {
+      rlk_support_state st;
+      st.lse_support = whole ? lse : static_cast<float>(lse_s);
+      st.threshold = whole ? -INFINITY
+                           : (fast ? (L.kappa >= kWin ? -INFINITY : slot_value(L.kappa))
+                                   : key_value(static_cast<uint32_t>(L.kappa)));
+      st.status = in_support ? 1 : 0;
+      st.reserved = 0;
+      state_out[row] = st;
+    }
   }
 }
 

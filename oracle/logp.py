@@ -270,10 +270,10 @@ def grad_row(bits_row, vocab_padded: int, vocab_real: int, temperature: float, t
     if g_pol != 0.0 and math.isnan(pol):
         g[:vocab_real] = NAN
         return g
-    gp = g_pol if (g_pol != 0.0 and np.isfinite(pol)) else 0.0
+    mask = info.support_mask
+    gp = g_pol if (g_pol != 0.0 and mask[int(target)]) else 0.0
     out = -g_ref * p
     if gp != 0.0:
-        mask = info.support_mask if info.support_mask is not None else np.ones(vocab_real, dtype=bool)
         es = np.where(mask, e, 0.0)
         q = es / math.fsum(es.tolist())
         out = out - gp * q

@@ -33,16 +33,24 @@ def full(lib, logits=P, n=4, L=None, t=P + 0x100, tg=P + 0x200, out=P + 0x300, l
 
 
 def nuc(lib, logits=P, n=4, L=None, t=P + 0x100, p=P + 0x140, k=P + 0x180, tg=P + 0x200, pol=P + 0x300,
-        ref=P + 0x400, ws=P + 0x1000, wsb=1 << 20):
+        ref=P + 0x400, lse=None, state=None, ws=P + 0x1000, wsb=1 << 20):
     L = L if L is not None else lay()
     return lib.rlk_logp_nucleus(logits, n, ctypes.byref(L) if L is not False else None, t, p, k, tg, pol, ref,
-                                ws, wsb, None)
+                                lse, state, ws, wsb, None)
+
+
+def bwd(lib, logits=P, n=4, L=None, t=P + 0x100, tg=P + 0x200, ref=P + 0x300, lse=P + 0x340, gr=P + 0x380,
+        pol=P + 0x400, state=P + 0x500, gp=P + 0x600, out=P + 0x10000, stride=1024):
+    L = L if L is not None else lay()
+    return lib.rlk_logp_backward(logits, n, ctypes.byref(L) if L is not False else None, t, tg, ref, lse, gr,
+                                 pol, state, gp, out, stride, None)
 
 
 def test_every_declared_function_is_exported(lib):
     names = rlk.declared_functions()
     assert set(names) == {"rlk_logp_full", "rlk_logp_nucleus", "rlk_logp_workspace_bytes", "rlk_status_string",
-                          "rlk_logp_shard_summaries", "rlk_logp_merge", "rlk_logp_summary_bytes"}
+                          "rlk_logp_shard_summaries", "rlk_logp_merge", "rlk_logp_summary_bytes",
+                          "rlk_logp_backward"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -70,7 +78,7 @@ def test_zero_rows_is_ok_without_launch(lib):
     (dict(L=False), NULL),
     (dict(logits=P + 2), ALIGN), (dict(logits=P + 8), ALIGN), (dict(t=P + 2), ALIGN), (dict(tg=P + 4), ALIGN),
     (dict(out=P + 1), ALIGN), (dict(lse=P + 3), ALIGN),
-    (dict(n=-1), SHAPE),
+    (dict(n=-1), SHAPE), (dict(n=(1 << 22) + 1), SHAPE),
     (dict(L=lay(shards=4)), SHAPE), (dict(L=lay(vp=1000, vr=1000)), SHAPE), (dict(L=lay(vp=32, vr=32)), SHAPE),
     (dict(L=lay(vr=0)), SHAPE), (dict(L=lay(vr=1025)), SHAPE), (dict(L=lay(stride=1020)), SHAPE),
     (dict(L=lay(stride=1028)), SHAPE), (dict(L=lay(vp=(1 << 30) + 64, vr=10)), SHAPE),
@@ -89,9 +97,34 @@ def test_full_rejects_bad_arguments(lib, kw, code):
     (dict(ws=None, L=lay(groups=2)), WS), (dict(wsb=4 * 8 * 16 - 1, L=lay(groups=2)), WS),
     (dict(ws=P + 4, L=lay(groups=2)), ALIGN), (dict(logits=None), NULL),
     (dict(L=lay(groups=5)), GROUPS), (dict(n=-3), SHAPE), (dict(L=lay(vr=2000)), SHAPE),
+    (dict(lse=P + 0x502), ALIGN), (dict(state=P + 0x508), ALIGN),
 ])
 def test_nucleus_rejects_bad_arguments(lib, kw, code):
     assert nuc(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), NULL), (dict(t=None), NULL), (dict(tg=None), NULL), (dict(out=None), NULL),
+    (dict(L=False), NULL), (dict(gr=None, gp=None), NULL),
+    (dict(ref=None), NULL), (dict(lse=None), NULL), (dict(pol=None), NULL), (dict(state=None), NULL),
+    (dict(logits=P + 8), ALIGN), (dict(out=P + 0x10008), ALIGN), (dict(t=P + 0x102), ALIGN),
+    (dict(tg=P + 0x204), ALIGN), (dict(ref=P + 0x301), ALIGN), (dict(lse=P + 0x342), ALIGN),
+    (dict(gr=P + 0x381), ALIGN), (dict(pol=P + 0x402), ALIGN), (dict(state=P + 0x508), ALIGN),
+    (dict(gp=P + 0x601), ALIGN),
+    (dict(stride=1016), SHAPE), (dict(stride=1028), SHAPE), (dict(n=-1), SHAPE),
+    (dict(L=lay(vr=0)), SHAPE), (dict(L=lay(groups=3)), GROUPS),
+    (dict(n=1 << 20, stride=1 << 44), SHAPE), (dict(n=(1 << 22) + 1), SHAPE),
+])
+def test_backward_rejects_bad_arguments(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_backward_optional_terms_and_zero_rows(lib):
+    # a term whose upstream gradient is NULL needs none of its statistics
+    assert bwd(lib, n=0) == OK
+    assert bwd(lib, n=0, logits=None, t=None, tg=None, ref=None, lse=None, gr=None, pol=None, state=None,
+               gp=None, out=None) == OK
+    assert bwd(lib, n=0, stride=1000) == SHAPE
 
 
 def test_workspace_sizes(lib):

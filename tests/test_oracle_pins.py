@@ -579,6 +579,11 @@ def test_grad_sums_to_zero_and_special_rows():
     neg = row.copy(); neg[9] = datagen.BF16_NEG_INF
     g = O.grad_row(neg, 1024, 1000, 2.0, 9, 1.0)
     assert g[9] == 0.5 and abs(math.fsum(g.tolist())) < 1e-12
+    # ... and the same holds for the policy term when the support is the whole
+    # vocabulary (the -inf target is then inside it), while a restricted
+    # support leaves the -inf target outside: no policy term
+    assert np.array_equal(O.grad_row(neg, 1024, 1000, 2.0, 9, 0.0, 1.0), g)
+    assert np.all(O.grad_row(neg, 1024, 1000, 2.0, 9, 0.0, 1.0, 0.9) == 0.0)
     # disabled support: the policy term equals the reference term
     a = O.grad_row(row, 1024, 1000, 1.3, tg, 0.25, 0.5)
     b = O.grad_row(row, 1024, 1000, 1.3, tg, 0.75, 0.0)
