@@ -223,3 +223,24 @@ def small(seed: int, n_rows: int, vocab_padded: int, vocab_real: int, sigma: flo
                     row_stride or vocab_padded, sigma, spike,
                     arr(temperature, np.float32), arr(top_p, np.float32), arr(top_k, np.int32),
                     [(seed, i) for i in range(n_rows)], pad_fill=PAD_FILLS[pad])
+
+
+# --------------------------------------------------------------------------- gradient-norm inputs
+
+NORM_MICROBENCH_N = 10_000_000  # page "H100 canonical CP backward validation", Timing and scope
+
+
+def grad_values(seed: int, n: int, sigma: float = 1e-3, zero_frac: float = 0.0, chunk: int = 1 << 20) -> np.ndarray:
+    """BF16-derived float32 gradient-like values: bf16_rne(sigma * N(0, 1)) widened
+    to float32, with a fraction ``zero_frac`` of exact zeros. Chunk c of
+    ``chunk`` values comes from ``SeedSequence([seed, c])`` so that any
+    prefix is cheap to regenerate."""
+    out = np.empty(n, dtype=np.float32)
+    for c, lo in enumerate(range(0, n, chunk)):
+        hi = min(n, lo + chunk)
+        g = _rng((seed, c))
+        v = (g.standard_normal(hi - lo, dtype=np.float32) * np.float32(sigma)).astype(np.float32)
+        if zero_frac > 0:
+            v[g.random(hi - lo) < zero_frac] = 0.0
+        out[lo:hi] = bf16_bits_to_f32(f32_to_bf16_bits(v))
+    return out
