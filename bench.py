@@ -43,7 +43,7 @@ KERNEL_SOURCES = [
     os.path.join(ROOT, "invariant_token_log_fp32_amd", "csrc", "logp_device.hpp"),
     os.path.join(ROOT, "invariant_token_log_fp32_amd", "csrc", "support.hpp"),
     os.path.join(ROOT, "invariant_token_log_fp32_amd", "csrc", "backward.hpp"),
-]
+]  # sources of the kernels whose counters the traffic records hold
 
 
 def kernel_source_hash() -> str:
@@ -273,6 +273,28 @@ def main():
                     "ms_per_rank": ms_ranks / G, "ms_merge": ms_merge,
                     "rank_achieved_GBs": rank_bytes / (ms_ranks / G * 1e-3) / 1e9,
                     "frac": rank_bytes / (ms_ranks / G * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        # order-independent gradient L2 norm: the pages' 10M-element microbenchmark, and 2^28 values
+        xn = torch.from_numpy(datagen.grad_values(7, datagen.NORM_MICROBENCH_N)).to(dev)
+        nb = torch.zeros(rlk.NORM_BIN_WORDS, dtype=torch.int64, device=dev)  # rlk_l2norm leaves it zeroed
+        so = torch.empty(1, dtype=torch.float64, device=dev)
+        no = torch.empty(1, dtype=torch.float32, device=dev)
+        _, ms_norm = time_calls(lambda i: rlk.l2norm(xn, workspace=nb, sumsq_out=so, norm_out=no), 200, 20)
+        acc_bins = torch.zeros(rlk.NORM_BIN_WORDS, dtype=torch.int64, device=dev)
+        _, ms_acc = time_calls(lambda i: rlk.l2norm_accumulate(xn, acc_bins), 200, 20)
+        nbytes = xn.numel() * 4
+        sec.append({"workload": "l2norm: 10M BF16-derived fp32 gradient values (accumulate + finalize launches)",
+                    "entry_point": "rlk_l2norm", "ms_per_step": ms_norm, "accumulate_ms": ms_acc,
+                    "achieved_GBs": nbytes / (ms_norm * 1e-3) / 1e9,
+                    "frac": nbytes / (ms_norm * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        del xn
+        xl = (torch.randn(1 << 28, generator=torch.Generator(device=dev).manual_seed(3), device=dev)
+              .to(torch.bfloat16).to(torch.float32))
+        _, ms_big = time_calls(lambda i: rlk.l2norm(xl, workspace=nb, sumsq_out=so, norm_out=no), 50, 5)
+        nbytes = xl.numel() * 4
+        sec.append({"workload": "l2norm: 2^28 BF16-derived fp32 values (1 GiB)", "entry_point": "rlk_l2norm",
+                    "ms_per_step": ms_big, "achieved_GBs": nbytes / (ms_big * 1e-3) / 1e9,
+                    "frac": nbytes / (ms_big * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        del xl
         result["secondary"] = sec
 
     if not args.no_cpu_baseline:

@@ -18,13 +18,16 @@ from typing import Optional, Tuple, Union
 __all__ = [
     "LIB_PATH", "HEADER_PATH", "VocabLayout", "load_library", "status_string", "workspace_bytes",
     "summary_bytes", "logp_full", "logp_nucleus", "logp_shard_summaries", "logp_merge", "logp_backward",
-    "support_state_fields", "RlkError", "N_SHARDS",
+    "support_state_fields", "l2norm", "l2norm_zero", "l2norm_accumulate", "l2norm_finalize", "NORM_BIN_WORDS",
+    "RlkError", "N_SHARDS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librlk_logp.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "rlk_logp.h")
+HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(_PKG), "include", "rlk_norm.h")]
 N_SHARDS = 8
+NORM_BIN_WORDS = 264  # uint64 words of rlk_norm_bins
 
 RLK_OK = 0
 STATUS_NAMES = {
@@ -80,14 +83,25 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rlk_logp_summary_bytes.restype = sz
     lib.rlk_logp_backward.argtypes = [vp, i64, lay, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, vp]
     lib.rlk_logp_backward.restype = i32
+    lib.rlk_l2norm_zero.argtypes = [vp, vp]
+    lib.rlk_l2norm_zero.restype = i32
+    lib.rlk_l2norm_accumulate.argtypes = [vp, i64, vp, vp]
+    lib.rlk_l2norm_accumulate.restype = i32
+    lib.rlk_l2norm_finalize.argtypes = [vp, vp, vp, vp]
+    lib.rlk_l2norm_finalize.restype = i32
+    lib.rlk_l2norm.argtypes = [vp, i64, vp, vp, vp, vp]
+    lib.rlk_l2norm.restype = i32
     _lib = lib
     return lib
 
 
-def declared_functions(header: str = HEADER_PATH):
-    """Names of the functions that include/rlk_logp.h declares."""
-    text = open(header).read()
-    return sorted(set(re.findall(r"^\s*(?:int32_t|size_t|const char\*)\s+(rlk_\w+)\s*\(", text, re.M)))
+def declared_functions(headers=None):
+    """Names of the functions that the headers under include/ declare."""
+    names = set()
+    for h in (headers or HEADER_PATHS):
+        text = open(h).read()
+        names |= set(re.findall(r"^\s*(?:int32_t|size_t|const char\*)\s+(rlk_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def status_string(status: int) -> str:
@@ -317,3 +331,82 @@ def logp_merge(summaries, temperature, target, *, n_rows: int, groups: int, voca
     if st != RLK_OK:
         raise RlkError(st, "rlk_logp_merge")
     return (out, lse_out) if return_lse else out
+
+
+# ---------------------------------------------------------------------------
+# gradient L2 norm (include/rlk_norm.h)
+# ---------------------------------------------------------------------------
+
+def _bins_tensor(bins, device):
+    torch = _torch()
+    if bins is None:
+        return torch.empty(NORM_BIN_WORDS, dtype=torch.int64, device=device)
+    if bins.dtype not in (torch.int64, torch.uint64) or bins.numel() != NORM_BIN_WORDS or not bins.is_contiguous():
+        raise ValueError(f"bins must be a contiguous 64-bit tensor of {NORM_BIN_WORDS} words")
+    return bins
+
+
+def _f32_flat(x):
+    torch = _torch()
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("values must be a contiguous float32 device tensor")
+    return x
+
+
+def l2norm_zero(bins, stream=None):
+    """Clear an accumulator (rlk_l2norm_zero)."""
+    st = load_library().rlk_l2norm_zero(bins.data_ptr(), _stream_handle(stream, bins.device))
+    if st != RLK_OK:
+        raise RlkError(st, "rlk_l2norm_zero")
+    return bins
+
+
+def l2norm_accumulate(x, bins, stream=None):
+    """Add the float32 squares of ``x`` to ``bins`` (rlk_l2norm_accumulate)."""
+    x = _f32_flat(x)
+    st = load_library().rlk_l2norm_accumulate(x.data_ptr() if x.numel() else None, x.numel(), bins.data_ptr(),
+                                              _stream_handle(stream, bins.device))
+    if st != RLK_OK:
+        raise RlkError(st, "rlk_l2norm_accumulate")
+    return bins
+
+
+def l2norm_finalize(bins, sumsq_out=None, norm_out=None, stream=None):
+    """(sum of squares float64 [1], norm float32 [1]) from ``bins`` (rlk_l2norm_finalize)."""
+    torch = _torch()
+    dev = bins.device
+    sumsq_out = sumsq_out if sumsq_out is not None else torch.empty(1, dtype=torch.float64, device=dev)
+    norm_out = norm_out if norm_out is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    st = load_library().rlk_l2norm_finalize(bins.data_ptr(), sumsq_out.data_ptr(), norm_out.data_ptr(),
+                                            _stream_handle(stream, dev))
+    if st != RLK_OK:
+        raise RlkError(st, "rlk_l2norm_finalize")
+    return sumsq_out, norm_out
+
+
+def l2norm(xs, *, workspace=None, sumsq_out=None, norm_out=None, stream=None):
+    """Order-independent L2 norm of one float32 device tensor (rlk_l2norm, one
+    launch) or of a list of them (zero + one accumulate per tensor +
+    finalize). Returns (sum of squares float64 [1], norm float32 [1]).
+    ``workspace`` (264 int64 words) must be all-zero when given for a single
+    tensor; rlk_l2norm leaves it all-zero."""
+    torch = _torch()
+    if isinstance(xs, (list, tuple)):
+        if not xs:
+            raise ValueError("l2norm needs at least one tensor")
+        bins = _bins_tensor(workspace, xs[0].device)
+        l2norm_zero(bins, stream)
+        for x in xs:
+            l2norm_accumulate(x, bins, stream)
+        return l2norm_finalize(bins, sumsq_out, norm_out, stream)
+    x = _f32_flat(xs)
+    dev = x.device
+    ws = workspace if workspace is not None else torch.zeros(NORM_BIN_WORDS, dtype=torch.int64, device=dev)
+    ws = _bins_tensor(ws, dev)
+    sumsq_out = sumsq_out if sumsq_out is not None else torch.empty(1, dtype=torch.float64, device=dev)
+    norm_out = norm_out if norm_out is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    st = load_library().rlk_l2norm(x.data_ptr() if x.numel() else None, x.numel(), ws.data_ptr(),
+                                   sumsq_out.data_ptr(), norm_out.data_ptr(), _stream_handle(stream, dev))
+    if st != RLK_OK:
+        raise RlkError(st, "rlk_l2norm")
+    return sumsq_out, norm_out

@@ -1,6 +1,7 @@
 """Ahead-of-time build of the HIP library for gfx950.
 
-Produces ``librlk_logp.so`` next to this file from ``csrc/rlk_logp.hip``:
+Produces ``librlk_logp.so`` next to this file from ``csrc/rlk_logp.hip``
+(token logprobs, their backward) and ``csrc/rlk_norm.hip`` (gradient L2 norm):
     python -m invariant_token_log_fp32_amd.build
 """
 from __future__ import annotations
@@ -12,7 +13,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "rlk_logp.hip")
+SRCS = [os.path.join(PKG, "csrc", "rlk_logp.hip"), os.path.join(PKG, "csrc", "rlk_norm.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librlk_logp.so")
 ARCH = "gfx950"
@@ -40,7 +41,7 @@ def hipcc() -> str:
 
 def build(extra_flags=(), out: str = LIB, verbose: bool = False) -> str:
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-I", os.path.join(PKG, "csrc"), "-o", tmp, SRC]
+    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-I", os.path.join(PKG, "csrc"), "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -20,7 +20,9 @@ What it computes for a set of float32 values x_i (one or several tensors):
    for every biased exponent e of s_i in 0..254, bin[e] = sum of the 24-bit
    integer significands m_i (hidden bit included for e >= 1), so that
    s_i = m_i * 2^(max(e, 1) - 150) exactly. A square that is NaN counts in
-   n_nan, one that is +inf (overflow or infinite x) in n_inf.
+   n_nan, one that is +inf (overflow or infinite x) in n_inf. This is the
+   canonical spread of the words; any words with the same value
+   sum_e bin[e] * 2^(max(e, 1) - 150) encode the same sum.
 3. Sum of squares: the exact sum S of the s_i, rounded once to float64 (round
    to nearest even); NaN if any square is NaN, else +inf if any is +inf.
 4. Norm: fl32(sqrt(fl64(S))) with IEEE square roots.

@@ -50,7 +50,8 @@ def test_every_declared_function_is_exported(lib):
     names = rlk.declared_functions()
     assert set(names) == {"rlk_logp_full", "rlk_logp_nucleus", "rlk_logp_workspace_bytes", "rlk_status_string",
                           "rlk_logp_shard_summaries", "rlk_logp_merge", "rlk_logp_summary_bytes",
-                          "rlk_logp_backward"}
+                          "rlk_logp_backward", "rlk_l2norm", "rlk_l2norm_zero", "rlk_l2norm_accumulate",
+                          "rlk_l2norm_finalize"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -190,3 +191,28 @@ def test_shard_summaries_rejects_bad_arguments(lib, kw, code):
 ])
 def test_merge_rejects_bad_arguments(lib, kw, code):
     assert merge(lib, **kw) == code
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda L: L.rlk_l2norm_zero(None, None), NULL),
+    (lambda L: L.rlk_l2norm_zero(P + 4, None), ALIGN),
+    (lambda L: L.rlk_l2norm_accumulate(P, -1, P + 0x1000, None), SHAPE),
+    (lambda L: L.rlk_l2norm_accumulate(P, 1 << 39, P + 0x1000, None), SHAPE),
+    (lambda L: L.rlk_l2norm_accumulate(None, 0, None, None), OK),
+    (lambda L: L.rlk_l2norm_accumulate(None, 5, P + 0x1000, None), NULL),
+    (lambda L: L.rlk_l2norm_accumulate(P, 5, None, None), NULL),
+    (lambda L: L.rlk_l2norm_accumulate(P + 2, 5, P + 0x1000, None), ALIGN),
+    (lambda L: L.rlk_l2norm_accumulate(P, 5, P + 0x1004, None), ALIGN),
+    (lambda L: L.rlk_l2norm_finalize(None, P, P + 0x100, None), NULL),
+    (lambda L: L.rlk_l2norm_finalize(P + 0x1000, None, None, None), NULL),
+    (lambda L: L.rlk_l2norm_finalize(P + 0x1000, P + 4, None, None), ALIGN),
+    (lambda L: L.rlk_l2norm_finalize(P + 0x1000, None, P + 2, None), ALIGN),
+    (lambda L: L.rlk_l2norm(P, -1, P + 0x1000, P, P + 0x100, None), SHAPE),
+    (lambda L: L.rlk_l2norm(P, 5, None, P, P + 0x100, None), NULL),
+    (lambda L: L.rlk_l2norm(P, 5, P + 0x1000, None, None, None), NULL),
+    (lambda L: L.rlk_l2norm(None, 5, P + 0x1000, P, P + 0x100, None), NULL),
+    (lambda L: L.rlk_l2norm(P + 1, 5, P + 0x1000, P, P + 0x100, None), ALIGN),
+    (lambda L: L.rlk_l2norm(P, 5, P + 0x1000, P + 4, None, None), ALIGN),
+])
+def test_l2norm_rejects_bad_arguments(lib, call, code):
+    assert call(lib) == code
