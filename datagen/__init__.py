@@ -244,3 +244,67 @@ def grad_values(seed: int, n: int, sigma: float = 1e-3, zero_frac: float = 0.0, 
             v[g.random(hi - lo) < zero_frac] = 0.0
         out[lo:hi] = bf16_bits_to_f32(f32_to_bf16_bits(v))
     return out
+
+
+# --------------------------------------------------------------------------- LM-head inputs
+
+QWEN3_D_MODEL = 4096  # Qwen3-8B hidden size
+
+
+def linear_inputs(seed: int, n_rows: int, d_model: int, vocab_real: int, sigma_h: float = 1.0,
+                  logit_sigma: float = 2.5, threads: Optional[int] = None):
+    """BF16 hidden states ~ N(0, sigma_h^2) [n_rows, d_model] and a BF16 vocabulary
+    projection ~ N(0, (logit_sigma / sqrt(d_model))^2) [vocab_real, d_model], so
+    that the logits are roughly N(0, logit_sigma^2). Each block of 256 rows of
+    each matrix comes from its own stream (seed, 0 or 1, block)."""
+    hid = np.empty((n_rows, d_model), dtype=np.uint16)
+    wt = np.empty((vocab_real, d_model), dtype=np.uint16)
+    sw = logit_sigma / np.sqrt(d_model)
+    step = 256
+
+    def fill(kind, blk):
+        dst, sig, n = (hid, sigma_h, n_rows) if kind == 0 else (wt, sw, vocab_real)
+        lo, hi = blk * step, min(n, (blk + 1) * step)
+        g = _rng((seed, kind, blk))
+        v = g.standard_normal((hi - lo, d_model), dtype=np.float32) * np.float32(sig)
+        dst[lo:hi] = f32_to_bf16_bits(v.astype(np.float32))
+
+    jobs = [(0, b) for b in range((n_rows + step - 1) // step)] + \
+           [(1, b) for b in range((vocab_real + step - 1) // step)]
+    with _cf.ThreadPoolExecutor(max_workers=threads or min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(lambda j: fill(*j), jobs))
+    return hid, wt
+
+
+def linear_exact_inputs(seed: int, n_rows: int, d_model: int, vocab_real: int, nnz: int = 80,
+                        threads: Optional[int] = None):
+    """Exactly summable BF16 inputs: hidden entries in {-3..3} / 4, and each
+    vocabulary row with at most ``nnz`` entries of +-1/4 (``nnz`` uniform column
+    draws; a repeated column keeps one entry; the rest 0). Every product is a
+    multiple of 1/16, every partial sum of a row's dot product is such a
+    multiple below 2^24/16 in magnitude (exact in float32 in any order), and
+    every logit is a multiple of 1/16 of magnitude <= 3*nnz/16, which BF16
+    holds exactly when 3*nnz <= 256. Each block of 256 rows comes from its own
+    stream (seed, 10 or 11, block)."""
+    hid = np.empty((n_rows, d_model), dtype=np.uint16)
+    wt = np.zeros((vocab_real, d_model), dtype=np.uint16)
+    hv = f32_to_bf16_bits(np.arange(-3, 4, dtype=np.float32) / 4)       # index v+3 -> bits of v/4
+    qv = f32_to_bf16_bits(np.array([-0.25, 0.25], dtype=np.float32))
+    step = 256
+
+    def fill(kind, blk):
+        n = n_rows if kind == 0 else vocab_real
+        lo, hi = blk * step, min(n, (blk + 1) * step)
+        g = _rng((seed, 10 + kind, blk))
+        if kind == 0:
+            hid[lo:hi] = hv[g.integers(0, 7, (hi - lo, d_model))]
+        else:
+            cols = g.integers(0, d_model, (hi - lo, nnz))
+            vals = qv[g.integers(0, 2, (hi - lo, nnz))]
+            wt[np.arange(lo, hi)[:, None], cols] = vals
+
+    jobs = [(0, b) for b in range((n_rows + step - 1) // step)] + \
+           [(1, b) for b in range((vocab_real + step - 1) // step)]
+    with _cf.ThreadPoolExecutor(max_workers=threads or min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(lambda j: fill(*j), jobs))
+    return hid, wt
