@@ -19,13 +19,14 @@ __all__ = [
     "LIB_PATH", "HEADER_PATH", "VocabLayout", "load_library", "status_string", "workspace_bytes",
     "summary_bytes", "logp_full", "logp_nucleus", "logp_shard_summaries", "logp_merge", "logp_backward",
     "support_state_fields", "l2norm", "l2norm_zero", "l2norm_accumulate", "l2norm_finalize", "NORM_BIN_WORDS",
+    "linear", "linear_logp", "linear_logp_workspace_bytes",
     "RlkError", "N_SHARDS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librlk_logp.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "rlk_logp.h")
-HEADER_PATHS = [HEADER_PATH, os.path.join(os.path.dirname(_PKG), "include", "rlk_norm.h")]
+HEADER_PATHS = [HEADER_PATH] + [os.path.join(os.path.dirname(_PKG), "include", n) for n in ("rlk_norm.h", "rlk_linear.h")]
 N_SHARDS = 8
 NORM_BIN_WORDS = 264  # uint64 words of rlk_norm_bins
 
@@ -91,6 +92,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rlk_l2norm_finalize.restype = i32
     lib.rlk_l2norm.argtypes = [vp, i64, vp, vp, vp, vp]
     lib.rlk_l2norm.restype = i32
+    lib.rlk_linear.argtypes = [vp, i64, i64, i64, vp, i64, lay, vp, vp]
+    lib.rlk_linear.restype = i32
+    lib.rlk_linear_logp.argtypes = [vp, i64, i64, i64, vp, i64, lay, vp, vp, vp, vp, vp, sz, vp]
+    lib.rlk_linear_logp.restype = i32
+    lib.rlk_linear_logp_workspace_bytes.argtypes = [i64, lay]
+    lib.rlk_linear_logp_workspace_bytes.restype = sz
     _lib = lib
     return lib
 
@@ -410,3 +417,71 @@ def l2norm(xs, *, workspace=None, sumsq_out=None, norm_out=None, stream=None):
     if st != RLK_OK:
         raise RlkError(st, "rlk_l2norm")
     return sumsq_out, norm_out
+
+
+# ---------------------------------------------------------------------------
+# LM-head linear and fused linear + logprob (include/rlk_linear.h)
+# ---------------------------------------------------------------------------
+
+def _bf16_matrix(x, name):
+    torch = _torch()
+    if x.dim() != 2 or x.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D device tensor of BF16 bits with contiguous rows")
+    return x.stride(0) if x.shape[0] > 1 else max(x.stride(0), x.shape[1])
+
+
+def linear_logp_workspace_bytes(n_rows: int, vocab_padded: int, vocab_real: int) -> int:
+    lay = make_layout(vocab_padded, vocab_real, vocab_padded)
+    return int(load_library().rlk_linear_logp_workspace_bytes(int(n_rows), ctypes.byref(lay)))
+
+
+def linear(hidden, weight, *, vocab_padded: int, out=None, stream=None):
+    """BF16 logits bf16(hidden . weight^T) [n_rows, vocab_padded], pads -inf (rlk_linear).
+    ``weight`` holds the vocab_real rows of the projection."""
+    torch = _torch()
+    ldh = _bf16_matrix(hidden, "hidden")
+    ldw = _bf16_matrix(weight, "weight")
+    n, d = hidden.shape
+    vr = weight.shape[0]
+    if weight.shape[1] != d:
+        raise ValueError("hidden and weight must have the same d_model")
+    if out is None:
+        out = torch.empty((n, vocab_padded), dtype=torch.bfloat16, device=hidden.device)
+    ldo = _check_logits(out)
+    lay = make_layout(vocab_padded, vr, ldo)
+    st = load_library().rlk_linear(hidden.data_ptr(), n, d, ldh, weight.data_ptr(), ldw, ctypes.byref(lay),
+                                   out.data_ptr(), _stream_handle(stream, hidden.device))
+    if st != RLK_OK:
+        raise RlkError(st, "rlk_linear")
+    return out
+
+
+def linear_logp(hidden, weight, temperature, target, *, vocab_padded: int, return_lse: bool = False, out=None,
+                lse_out=None, workspace=None, stream=None):
+    """Reference logprob of ``target`` from bf16(hidden . weight^T) without writing
+    the logits (rlk_linear_logp)."""
+    torch = _torch()
+    ldh = _bf16_matrix(hidden, "hidden")
+    ldw = _bf16_matrix(weight, "weight")
+    n, d = hidden.shape
+    vr = weight.shape[0]
+    dev = hidden.device
+    if weight.shape[1] != d:
+        raise ValueError("hidden and weight must have the same d_model")
+    temperature = _per_row(temperature, n, torch.float32, dev, "temperature")
+    target = _per_row(target, n, torch.int64, dev, "target")
+    out = out if out is not None else torch.empty(n, dtype=torch.float32, device=dev)
+    if return_lse and lse_out is None:
+        lse_out = torch.empty(n, dtype=torch.float32, device=dev)
+    lay = make_layout(vocab_padded, vr, vocab_padded)
+    lib = load_library()
+    need = int(lib.rlk_linear_logp_workspace_bytes(n, ctypes.byref(lay)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = lib.rlk_linear_logp(hidden.data_ptr(), n, d, ldh, weight.data_ptr(), ldw, ctypes.byref(lay),
+                             temperature.data_ptr(), target.data_ptr(), out.data_ptr(),
+                             lse_out.data_ptr() if lse_out is not None else None, workspace.data_ptr(),
+                             workspace.numel(), _stream_handle(stream, dev))
+    if st != RLK_OK:
+        raise RlkError(st, "rlk_linear_logp")
+    return (out, lse_out) if return_lse else out

@@ -1,7 +1,8 @@
 """Ahead-of-time build of the HIP library for gfx950.
 
 Produces ``librlk_logp.so`` next to this file from ``csrc/rlk_logp.hip``
-(token logprobs, their backward) and ``csrc/rlk_norm.hip`` (gradient L2 norm):
+(token logprobs, their backward), ``csrc/rlk_norm.hip`` (gradient L2 norm) and
+``csrc/rlk_linear.hip`` (LM-head linear, fused linear + logprob):
     python -m invariant_token_log_fp32_amd.build
 """
 from __future__ import annotations
@@ -13,7 +14,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "rlk_logp.hip"), os.path.join(PKG, "csrc", "rlk_norm.hip")]
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("rlk_logp.hip", "rlk_norm.hip", "rlk_linear.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librlk_logp.so")
 ARCH = "gfx950"

@@ -1,0 +1,456 @@
+// LM-head linear layer and fused linear + token logprob ("linear-logp") for
+// gfx950, and the C-ABI declared in include/rlk_linear.h.
+//
+// Passages: RL-Kernel page "Reproduce and profile the Qwen3-8B TP4/CP2
+// experiment", section "Capture logs, status, and validation evidence" (the
+// run log is audited for the linear-logp backend), and page "Configurable H100
+// consistency runs", sampling and mode/KL paragraphs (BF16 model logits,
+// float32 temperature scaling, full-vocabulary reference logprob).
+//
+// Kernels:
+//   k_linear<kLogp>  one 128 x 128 tile of logits per step of a grid-stride
+//                    loop over tiles (rows fastest); 4 waves, each a 64 x 64
+//                    quarter as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.
+//                    K runs in 64-wide stages through double-buffered LDS
+//                    (rows padded to 144 bytes, so the 16-byte fragment reads
+//                    of a wave hit distinct banks); the next stage's global
+//                    loads are in flight while the current one is multiplied.
+//                    Epilogue: the fp32 accumulators are rounded to BF16 into
+//                    an LDS tile, then either stored (rlk_linear) or reduced
+//                    per row to a 16-byte summary of the tile's 128 columns
+//                    (rlk_linear_logp): integer reference exponent r from the
+//                    exact tile maximum and l = sum of 2^(x*c - r) in a fixed
+//                    order; greedy rows keep the maximum and its lowest column.
+//   k_lin_merge      one wave per row: the row's tile summaries merged in tile
+//                    order (fp64), then the target's logprob.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "logp_device.hpp"
+#include "rlk_linear.h"
+#include "rlk_logp.h"
+
+namespace rlk_lin {
+
+using rlk::ShardSummary;
+using rlk::u32x4;
+
+constexpr int BM = 128;
+constexpr int BN = 128;
+constexpr int BK = 64;
+constexpr int kThreads = 256;
+constexpr int kLdsRow = BK + 8;         // bf16 per LDS row: 144 bytes
+constexpr int kStage = BM * kLdsRow;    // bf16 per operand per stage (BM == BN)
+constexpr int kOutRow = BN + 8;         // bf16 per row of the epilogue tile: 272 bytes
+constexpr int64_t kMaxGrid = int64_t(1) << 20;
+constexpr int64_t kMaxRows = int64_t(1) << 22;
+constexpr int64_t kMaxVocab = int64_t(1) << 30;
+constexpr int kMaxD = 65536;
+
+static_assert(BM == BN, "one LDS stage shape for both operands");
+static_assert(BM * kOutRow <= 2 * kStage, "the epilogue tile reuses the A stages");
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct Geo {
+  const uint16_t* __restrict__ h;
+  const uint16_t* __restrict__ w;
+  int64_t ldh;
+  int64_t ldw;
+  int64_t n_rows;
+  int64_t vocab_real;
+  int64_t vocab_padded;
+  int d;
+  int m_tiles;
+  int64_t n_tiles;
+};
+
+// Thread t loads 16-byte chunks t, t+256, t+512, t+768 of each operand's
+// 128 x 64 stage: chunk c is row c/8, columns (c%8)*8 .. +7.
+__device__ __forceinline__ void load_stage(const Geo& g, int64_t row0, int64_t col0, int k0, u32x4 (&ra)[4],
+                                           u32x4 (&rb)[4]) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = static_cast<int>(threadIdx.x) + i * kThreads;
+    const int r = c >> 3;
+    const int kc = (c & 7) * 8;
+    const int64_t gr = row0 + r;
+    const int64_t gc = col0 + r;
+    ra[i] = (gr < g.n_rows) ? *reinterpret_cast<const u32x4*>(g.h + gr * g.ldh + k0 + kc) : zero;
+    rb[i] = (gc < g.vocab_real) ? *reinterpret_cast<const u32x4*>(g.w + gc * g.ldw + k0 + kc) : zero;
+  }
+}
+
+__device__ __forceinline__ void store_stage(uint16_t* __restrict__ sa, uint16_t* __restrict__ sb,
+                                            const u32x4 (&ra)[4], const u32x4 (&rb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = static_cast<int>(threadIdx.x) + i * kThreads;
+    const int r = c >> 3;
+    const int kc = (c & 7) * 8;
+    *reinterpret_cast<u32x4*>(sa + r * kLdsRow + kc) = ra[i];
+    *reinterpret_cast<u32x4*>(sb + r * kLdsRow + kc) = rb[i];
+  }
+}
+
+// One 64-deep stage: 4 steps of 16, each 2 x 2 MFMAs. A fragment of a 32-row
+// block: lane l holds row l%32, k = 8*(l/32) .. +7 (same shape for the
+// vocabulary rows of the B operand).
+__device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ sa, const uint16_t* __restrict__ sb, int wm,
+                                          int wn, f32x16 (&acc)[2][2]) {
+  const int lane = threadIdx.x & 63;
+  const int fr = lane & 31;
+  const int fk = (lane >> 5) * 8;
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    bf16x8 a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 64 + i * 32 + fr) * kLdsRow + kk * 16 + fk);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      b[j] = *reinterpret_cast<const bf16x8*>(sb + (wn * 64 + j * 32 + fr) * kLdsRow + kk * 16 + fk);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// Logits of one tile, rounded to BF16, into sO [128][kOutRow]. Accumulator
+// element 4a+b of block (i, j) is row 32i + 8a + 4(l/32) + b, column 32j + l%32
+// of the wave's quarter.
+__device__ __forceinline__ void tile_logits(const Geo& g, int64_t row0, int64_t col0, uint16_t* __restrict__ smem,
+                                            uint16_t* __restrict__ sO) {
+  uint16_t* sa = smem;                  // [2][kStage]
+  uint16_t* sb = smem + 2 * kStage;     // [2][kStage]
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  u32x4 ra[4], rb[4];
+  load_stage(g, row0, col0, 0, ra, rb);
+  store_stage(sa, sb, ra, rb);
+  __syncthreads();
+  const int kt_n = g.d / BK;
+  for (int kt = 0; kt < kt_n; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < kt_n;
+    if (more) load_stage(g, row0, col0, (kt + 1) * BK, ra, rb);
+    mma_stage(sa + cur * kStage, sb + cur * kStage, wm, wn, acc);
+    if (more) store_stage(sa + (cur ^ 1) * kStage, sb + (cur ^ 1) * kStage, ra, rb);
+    __syncthreads();
+  }
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int r = wm * 64 + i * 32 + 8 * a + 4 * (lane >> 5) + b;
+          const int c = wn * 64 + j * 32 + (lane & 31);
+          const __bf16 v = static_cast<__bf16>(acc[i][j][4 * a + b]);
+          sO[r * kOutRow + c] = __builtin_bit_cast(uint16_t, v);
+        }
+  __syncthreads();
+}
+
+// Per-row summary of the tile's 128 columns; two threads per row, 64 columns each.
+__device__ __forceinline__ void tile_summaries(const Geo& g, int64_t row0, int64_t col0, int64_t n_t,
+                                               const uint16_t* __restrict__ sO, const float* __restrict__ temperature,
+                                               const int64_t* __restrict__ target, ShardSummary* __restrict__ ws) {
+  const int r = threadIdx.x >> 1;
+  const int half = threadIdx.x & 1;
+  const int64_t gr = row0 + r;
+  const bool row_ok = gr < g.n_rows;
+  const float t = row_ok ? temperature[gr] : 1.0f;
+  const int64_t tg = row_ok ? target[gr] : -1;
+  const int64_t cb = col0 + half * 64;
+  int64_t nv64 = g.vocab_real - cb;
+  const int nvalid = static_cast<int>(nv64 < 0 ? 0 : (nv64 > 64 ? 64 : nv64));
+  const uint16_t* src = sO + r * kOutRow + half * 64;
+  // pass 1: maximum (and, for greedy rows, NaN/+inf and the first maximum)
+  float m = -INFINITY;
+  bool bad = false;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(src + v * 8);
+    float x[8];
+    rlk::unpack8(q, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const bool ok = v * 8 + e < nvalid;
+      bad |= ok && ((x[e] != x[e]) || (x[e] == INFINITY));
+      m = ok ? fmaxf(m, x[e]) : m;
+    }
+  }
+  m = fmaxf(m, __shfl_xor(m, 1));
+  bad = bad || (__shfl_xor(static_cast<int>(bad), 1) != 0);
+  ShardSummary s;
+  s.r = 0.0f;
+  s.l = 0.0f;
+  s.m = m;
+  s.aux = -1;
+  if (!rlk::temperature_valid(t)) {
+    s.l = NAN;
+  } else if (t == 0.0f) {
+    int first = INT32_MAX;
+    for (int j = 0; j < nvalid; ++j) {
+      const float x = __uint_as_float(static_cast<uint32_t>(src[j]) << 16);
+      if (x == m) {
+        first = static_cast<int>(cb) + j;
+        break;
+      }
+    }
+    const int other = __shfl_xor(first, 1);
+    first = other < first ? other : first;
+    s.l = bad ? NAN : 0.0f;
+    s.aux = (first == INT32_MAX) ? -1 : first;
+  } else {
+    const float c = rlk::kLog2e / t;
+    const float rr = rlk::ref_exponent(m, c);
+    float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(src + v * 8);
+      float x[8];
+      rlk::unpack8(q, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float term = __builtin_amdgcn_exp2f(fmaf(x[e], c, -rr));
+        a4[e & 3] += (v * 8 + e < nvalid) ? term : 0.0f;
+      }
+    }
+    const float mine = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+    const float other = __shfl_xor(mine, 1);
+    s.r = rr;
+    s.l = half == 0 ? mine + other : other + mine;
+    if (tg >= col0 && tg < col0 + BN && tg < g.vocab_real)
+      s.aux = static_cast<int32_t>(sO[r * kOutRow + static_cast<int>(tg - col0)]);
+  }
+  if (row_ok && half == 0) ws[gr * g.n_tiles + n_t] = s;
+}
+
+// Stores the BF16 tile; real columns from the tile, pads -inf.
+__device__ __forceinline__ void tile_store(const Geo& g, int64_t row0, int64_t col0, const uint16_t* __restrict__ sO,
+                                           uint16_t* __restrict__ out, int64_t ldo) {
+  for (int c = threadIdx.x; c < BM * (BN / 8); c += kThreads) {
+    const int r = c >> 4;
+    const int ch = c & 15;
+    const int64_t gr = row0 + r;
+    const int64_t gc = col0 + ch * 8;
+    if (gr >= g.n_rows || gc >= g.vocab_padded) continue;
+    u32x4 v = *reinterpret_cast<const u32x4*>(sO + r * kOutRow + ch * 8);
+    if (gc + 8 > g.vocab_real) {
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t lo = (gc + 2 * h < g.vocab_real) ? (w[h] & 0xFFFFu) : 0xFF80u;
+        const uint32_t hi = (gc + 2 * h + 1 < g.vocab_real) ? (w[h] & 0xFFFF0000u) : 0xFF800000u;
+        w[h] = lo | hi;
+      }
+      v = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + gr * ldo + gc));
+  }
+}
+
+template <bool kLogp>
+__global__ __launch_bounds__(kThreads) void k_linear(Geo g, const float* __restrict__ temperature,
+                                                     const int64_t* __restrict__ target,
+                                                     ShardSummary* __restrict__ ws, uint16_t* __restrict__ out,
+                                                     int64_t ldo) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kStage];
+  uint16_t* sO = smem;  // the epilogue tile reuses the A stages
+  const int64_t tiles = static_cast<int64_t>(g.m_tiles) * g.n_tiles;
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {  // uniform across the workgroup
+    const int64_t m_t = tile % g.m_tiles;
+    const int64_t n_t = tile / g.m_tiles;
+    const int64_t row0 = m_t * BM;
+    const int64_t col0 = n_t * BN;
+    tile_logits(g, row0, col0, smem, sO);
+    if (kLogp)
+      tile_summaries(g, row0, col0, n_t, sO, temperature, target, ws);
+    else
+      tile_store(g, row0, col0, sO, out, ldo);
+    __syncthreads();  // sO is overwritten by the next tile's first stage
+  }
+}
+
+// One wave per row: the tile summaries merged in tile order.
+__global__ __launch_bounds__(256) void k_lin_merge(const ShardSummary* __restrict__ ws, int64_t n_rows,
+                                                   int64_t n_tiles, int64_t vocab_real,
+                                                   const float* __restrict__ temperature,
+                                                   const int64_t* __restrict__ target, float* __restrict__ logp_out,
+                                                   float* __restrict__ lse_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;  // uniform across the wave
+  const ShardSummary* __restrict__ s = ws + row * n_tiles;
+  const float t = temperature[row];
+  const int64_t tg = target[row];
+  float logp = NAN;
+  float lse = NAN;
+  if (rlk::temperature_valid(t) && tg >= 0 && tg < vocab_real) {
+    if (t == 0.0f) {
+      float m = -INFINITY;
+      bool bad = false;
+      for (int64_t k = lane; k < n_tiles; k += 64) {
+        m = fmaxf(m, s[k].m);
+        bad |= (s[k].l != s[k].l);
+      }
+      m = rlk::wave_max(m);
+      bad = __any(bad);
+      int64_t first = INT64_MAX;
+      for (int64_t k = lane; k < n_tiles; k += 64)
+        if (s[k].m == m) {
+          first = k;
+          break;
+        }
+      for (int o = 32; o >= 1; o >>= 1) {
+        const int64_t other = __shfl_xor(first, o);
+        first = other < first ? other : first;
+      }
+      if (!bad && m != -INFINITY && first != INT64_MAX)
+        logp = (static_cast<int64_t>(s[first].aux) == tg) ? 0.0f : -INFINITY;
+    } else {
+      float rmax = -INFINITY;
+      for (int64_t k = lane; k < n_tiles; k += 64)
+        if (s[k].l > 0.0f || s[k].l != s[k].l) rmax = fmaxf(rmax, s[k].r);
+      rmax = rlk::wave_max(rmax);
+      double acc = 0.0;
+      bool nan = false;
+      for (int64_t k = lane; k < n_tiles; k += 64) {
+        const float l = s[k].l;
+        if (l == 0.0f) continue;
+        const float d = fmaxf(s[k].r - rmax, -2000.0f);
+        acc = acc + ldexp(static_cast<double>(l), static_cast<int>(d));
+        nan |= (s[k].r != s[k].r) || (l != l);
+      }
+      for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o);
+      nan = __any(nan);
+      const int tbits = s[tg / BN].aux;
+      if (!nan && acc > 0.0 && acc < INFINITY && rmax > -INFINITY && rmax < INFINITY && tbits >= 0) {
+        const double lse2 = static_cast<double>(rmax) + log2(acc);
+        const double lse_d = lse2 * rlk::kLn2;
+        const float xt = __uint_as_float(static_cast<uint32_t>(tbits) << 16);
+        const float zt = xt / t;  // IEEE float32 division, rounded to nearest
+        lse = static_cast<float>(lse_d);
+        logp = static_cast<float>(static_cast<double>(zt) - lse_d);
+      }
+    }
+  }
+  if (lane == 0) {
+    logp_out[row] = logp;
+    if (lse_out) lse_out[row] = lse;
+  }
+}
+
+static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static int32_t launched() { return hipGetLastError() == hipSuccess ? RLK_OK : RLK_ERR_HIP; }
+
+static int32_t check_layout(int64_t n_rows, const rlk_vocab_layout* L) {
+  if (L == nullptr) return RLK_ERR_NULL;
+  if (n_rows < 0 || n_rows > kMaxRows) return RLK_ERR_SHAPE;
+  if (L->n_shards != 8) return RLK_ERR_SHAPE;
+  if (L->vocab_padded < 64 || L->vocab_padded > kMaxVocab || L->vocab_padded % 64 != 0) return RLK_ERR_SHAPE;
+  if (L->vocab_real < 1 || L->vocab_real > L->vocab_padded) return RLK_ERR_SHAPE;
+  if (L->row_stride < L->vocab_padded || L->row_stride % 8 != 0) return RLK_ERR_SHAPE;
+  if (!(L->groups == 1 || L->groups == 2 || L->groups == 4 || L->groups == 8)) return RLK_ERR_GROUPS;
+  return RLK_OK;
+}
+
+static int32_t check_operands(int64_t n_rows, int64_t d, int64_t ldh, int64_t ldw, const rlk_vocab_layout* L) {
+  if (d < 64 || d > kMaxD || d % BK != 0) return RLK_ERR_SHAPE;
+  if (ldh < d || ldh % 8 != 0 || ldw < d || ldw % 8 != 0) return RLK_ERR_SHAPE;
+  if (n_rows > 0 && ldh > INT64_MAX / 2 / n_rows) return RLK_ERR_SHAPE;
+  if (ldw > INT64_MAX / 2 / L->vocab_real) return RLK_ERR_SHAPE;
+  return RLK_OK;
+}
+
+static Geo make_geo(const uint16_t* h, int64_t n_rows, int64_t d, int64_t ldh, const uint16_t* w, int64_t ldw,
+                    const rlk_vocab_layout* L) {
+  Geo g;
+  g.h = h;
+  g.w = w;
+  g.ldh = ldh;
+  g.ldw = ldw;
+  g.n_rows = n_rows;
+  g.vocab_real = L->vocab_real;
+  g.vocab_padded = L->vocab_padded;
+  g.d = static_cast<int>(d);
+  g.m_tiles = static_cast<int>((n_rows + BM - 1) / BM);
+  g.n_tiles = (L->vocab_padded + BN - 1) / BN;
+  return g;
+}
+
+static unsigned grid_for(const Geo& g) {
+  const int64_t tiles = static_cast<int64_t>(g.m_tiles) * g.n_tiles;
+  return static_cast<unsigned>(tiles < kMaxGrid ? tiles : kMaxGrid);
+}
+
+}  // namespace rlk_lin
+
+extern "C" {
+
+size_t rlk_linear_logp_workspace_bytes(int64_t n_rows, const rlk_vocab_layout* layout) {
+  using namespace rlk_lin;
+  if (check_layout(n_rows, layout) != RLK_OK) return 0;
+  return static_cast<size_t>(n_rows) * static_cast<size_t>((layout->vocab_padded + BN - 1) / BN) *
+         sizeof(ShardSummary);
+}
+
+int32_t rlk_linear(const uint16_t* hidden, int64_t n_rows, int64_t d_model, int64_t hidden_stride,
+                   const uint16_t* weight, int64_t weight_stride, const rlk_vocab_layout* layout,
+                   uint16_t* logits_out, hipStream_t stream) {
+  using namespace rlk_lin;
+  int32_t st = check_layout(n_rows, layout);
+  if (st != RLK_OK) return st;
+  if ((st = check_operands(n_rows, d_model, hidden_stride, weight_stride, layout)) != RLK_OK) return st;
+  if (n_rows > 0 && layout->row_stride > INT64_MAX / 2 / n_rows) return RLK_ERR_SHAPE;
+  if (n_rows == 0) return RLK_OK;
+  if (!hidden || !weight || !logits_out) return RLK_ERR_NULL;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(logits_out, 16)) return RLK_ERR_ALIGN;
+  const Geo g = make_geo(hidden, n_rows, d_model, hidden_stride, weight, weight_stride, layout);
+  k_linear<false><<<dim3(grid_for(g)), dim3(kThreads), 0, stream>>>(g, nullptr, nullptr, nullptr, logits_out,
+                                                                     layout->row_stride);
+  return launched();
+}
+
+int32_t rlk_linear_logp(const uint16_t* hidden, int64_t n_rows, int64_t d_model, int64_t hidden_stride,
+                        const uint16_t* weight, int64_t weight_stride, const rlk_vocab_layout* layout,
+                        const float* temperature, const int64_t* target, float* logp_out, float* lse_out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  using namespace rlk_lin;
+  int32_t st = check_layout(n_rows, layout);
+  if (st != RLK_OK) return st;
+  if ((st = check_operands(n_rows, d_model, hidden_stride, weight_stride, layout)) != RLK_OK) return st;
+  if (n_rows == 0) return RLK_OK;
+  if (!hidden || !weight || !temperature || !target || !logp_out || !workspace) return RLK_ERR_NULL;
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(workspace, 16) || !aligned(temperature, 4) ||
+      !aligned(target, 8) || !aligned(logp_out, 4) || (lse_out && !aligned(lse_out, 4)))
+    return RLK_ERR_ALIGN;
+  if (workspace_bytes < rlk_linear_logp_workspace_bytes(n_rows, layout)) return RLK_ERR_WORKSPACE;
+  const Geo g = make_geo(hidden, n_rows, d_model, hidden_stride, weight, weight_stride, layout);
+  ShardSummary* ws = static_cast<ShardSummary*>(workspace);
+  k_linear<true><<<dim3(grid_for(g)), dim3(kThreads), 0, stream>>>(g, temperature, target, ws, nullptr, 0);
+  if ((st = launched()) != RLK_OK) return st;
+  k_lin_merge<<<dim3(static_cast<unsigned>((n_rows + 3) / 4)), dim3(256), 0, stream>>>(
+      ws, n_rows, g.n_tiles, layout->vocab_real, temperature, target, logp_out, lse_out);
+  return launched();
+}
+
+}  // extern "C"

@@ -40,11 +40,15 @@ def bf16_to_f64(bits) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def acc_exact(hidden_bits, weight_bits) -> np.ndarray:
-    """float64 [n_rows, vocab_real] sums of products (item 1)."""
+def acc_exact(hidden_bits, weight_bits, chunk: int = 8192) -> np.ndarray:
+    """float64 [n_rows, vocab_real] sums of products (item 1); the vocabulary
+    rows are converted ``chunk`` at a time to bound memory."""
     h = bf16_to_f64(hidden_bits)
-    w = bf16_to_f64(weight_bits)
-    return h @ w.T
+    wb = np.asarray(weight_bits)
+    out = np.empty((h.shape[0], wb.shape[0]), dtype=np.float64)
+    for lo in range(0, wb.shape[0], chunk):
+        out[:, lo:lo + chunk] = h @ bf16_to_f64(wb[lo:lo + chunk]).T
+    return out
 
 
 def round_bf16(v) -> np.ndarray:

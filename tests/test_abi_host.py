@@ -51,7 +51,7 @@ def test_every_declared_function_is_exported(lib):
     assert set(names) == {"rlk_logp_full", "rlk_logp_nucleus", "rlk_logp_workspace_bytes", "rlk_status_string",
                           "rlk_logp_shard_summaries", "rlk_logp_merge", "rlk_logp_summary_bytes",
                           "rlk_logp_backward", "rlk_l2norm", "rlk_l2norm_zero", "rlk_l2norm_accumulate",
-                          "rlk_l2norm_finalize"}
+                          "rlk_l2norm_finalize", "rlk_linear", "rlk_linear_logp", "rlk_linear_logp_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -216,3 +216,47 @@ def test_merge_rejects_bad_arguments(lib, kw, code):
 ])
 def test_l2norm_rejects_bad_arguments(lib, call, code):
     assert call(lib) == code
+
+
+def lin(lib, h=P, n=4, d=128, ldh=128, w=P + 0x100000, ldw=128, L=None, out=P + 0x200000):
+    L = L if L is not None else lay()
+    return lib.rlk_linear(h, n, d, ldh, w, ldw, ctypes.byref(L) if L is not False else None, out, None)
+
+
+def linlogp(lib, h=P, n=4, d=128, ldh=128, w=P + 0x100000, ldw=128, L=None, t=P + 0x300000, tg=P + 0x300100,
+            out=P + 0x300200, lse=None, ws=P + 0x400000, wsb=1 << 20):
+    L = L if L is not None else lay()
+    return lib.rlk_linear_logp(h, n, d, ldh, w, ldw, ctypes.byref(L) if L is not False else None, t, tg, out, lse,
+                               ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h=None), NULL), (dict(w=None), NULL), (dict(out=None), NULL), (dict(L=False), NULL),
+    (dict(d=32, ldh=32, ldw=32), SHAPE), (dict(d=100, ldh=104, ldw=104), SHAPE),
+    (dict(d=65600, ldh=65600, ldw=65600), SHAPE), (dict(ldh=120), SHAPE), (dict(ldh=132), SHAPE),
+    (dict(ldw=64), SHAPE), (dict(ldw=130), SHAPE), (dict(n=(1 << 22) + 1), SHAPE), (dict(n=-1), SHAPE),
+    (dict(L=lay(groups=3)), GROUPS), (dict(L=lay(vp=1000, vr=1000)), SHAPE), (dict(L=lay(stride=1020)), SHAPE),
+    (dict(h=P + 8), ALIGN), (dict(w=P + 0x100008), ALIGN), (dict(out=P + 0x200004), ALIGN),
+])
+def test_linear_rejects_bad_arguments(lib, kw, code):
+    assert lin(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h=None), NULL), (dict(w=None), NULL), (dict(t=None), NULL), (dict(tg=None), NULL), (dict(out=None), NULL),
+    (dict(ws=None), NULL), (dict(wsb=4 * 8 * 16 - 1), WS), (dict(ws=P + 0x400008), ALIGN),
+    (dict(t=P + 0x300002), ALIGN), (dict(tg=P + 0x300104), ALIGN), (dict(out=P + 0x300201), ALIGN),
+    (dict(lse=P + 0x300302), ALIGN), (dict(d=96, ldh=96, ldw=96), SHAPE), (dict(L=lay(groups=6)), GROUPS),
+])
+def test_linear_logp_rejects_bad_arguments(lib, kw, code):
+    assert linlogp(lib, **kw) == code
+
+
+def test_linear_zero_rows_and_workspace_size(lib):
+    assert lin(lib, n=0, h=None, w=None, out=None) == OK
+    assert linlogp(lib, n=0, h=None, w=None, t=None, tg=None, out=None, ws=None, wsb=0) == OK
+    L = lay(vp=152576, vr=151936)
+    assert lib.rlk_linear_logp_workspace_bytes(8192, ctypes.byref(L)) == 8192 * 1192 * 16
+    L2 = lay(vp=1088, vr=1000)
+    assert lib.rlk_linear_logp_workspace_bytes(3, ctypes.byref(L2)) == 3 * 9 * 16
+    assert lib.rlk_linear_logp_workspace_bytes(-1, ctypes.byref(L2)) == 0
