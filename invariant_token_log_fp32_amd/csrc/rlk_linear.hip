@@ -8,9 +8,11 @@
 // float32 temperature scaling, full-vocabulary reference logprob).
 //
 // Kernels:
-//   k_linear<kLogp>  one 128 x 128 tile of logits per step of a grid-stride
-//                    loop over tiles (rows fastest); 4 waves, each a 64 x 64
-//                    quarter as 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.
+//   k_linear<kLogp>  one 256 x 256 tile of logits per step of a grid-stride
+//                    loop over tiles, in XCD-aware groups of 4 x 8 tiles
+//                    that share operand panels in L2; 8 waves (two per SIMD,
+//                    so one wave's waits overlap the other's matrix work),
+//                    each 128 x 64 as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16.
 //                    K runs in 64-wide stages through double-buffered LDS
 //                    (rows padded to 144 bytes, so the 16-byte fragment reads
 //                    of a wave hit distinct banks); the next stage's global
@@ -18,11 +20,12 @@
 //                    Epilogue: the fp32 accumulators are rounded to BF16 into
 //                    an LDS tile, then either stored (rlk_linear) or reduced
 //                    per row to a 16-byte summary of the tile's 128 columns
-//                    (rlk_linear_logp): integer reference exponent r from the
-//                    exact tile maximum and l = sum of 2^(x*c - r) in a fixed
-//                    order; greedy rows keep the maximum and its lowest column.
-//   k_lin_merge      one wave per row: the row's tile summaries merged in tile
-//                    order (fp64), then the target's logprob.
+//                    (rlk_linear_logp) for each 128 columns: integer reference
+//                    exponent r from their exact maximum and l = sum of
+//                    2^(x*c - r) in a fixed order; greedy rows keep the
+//                    maximum and its lowest column.
+//   k_lin_merge      one wave per row: the row's 128-column summaries merged
+//                    in column order (fp64), then the target's logprob.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -36,20 +39,35 @@ namespace rlk_lin {
 using rlk::ShardSummary;
 using rlk::u32x4;
 
-constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int BK = 64;
-constexpr int kThreads = 256;
+constexpr int BM = 256;                 // rows of a workgroup tile
+constexpr int BN = 256;                 // vocabulary columns of a workgroup tile
+constexpr int BK = 64;                  // K per LDS stage
+constexpr int SN = 128;                 // columns per summary (nests in the canonical shards)
+constexpr int kThreads = 512;           // 8 waves, 2 x 4, each 128 x 64 (two waves per SIMD)
+constexpr int kWaveM = 128;
+constexpr int kWaveN = 64;
+constexpr int kMB = kWaveM / 32;        // 32 x 32 MFMA blocks per wave
+constexpr int kNB = kWaveN / 32;
 constexpr int kLdsRow = BK + 8;         // bf16 per LDS row: 144 bytes
 constexpr int kStage = BM * kLdsRow;    // bf16 per operand per stage (BM == BN)
-constexpr int kOutRow = BN + 8;         // bf16 per row of the epilogue tile: 272 bytes
+constexpr int kChunks = BM * BK / 8 / kThreads;  // 16-byte chunks per thread per operand per stage
+constexpr int kOutRow = BN + 8;         // bf16 per row of the epilogue tile: 528 bytes
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
+// XCD-aware order: workgroup b runs on XCD b % 8; each XCD takes groups of
+// kGM x kGN tiles (one per CU of the XCD), so the 32 workgroups of a group
+// stream the same 4 hidden-state panels and 8 vocabulary panels through that
+// XCD's L2, stage by stage.
+constexpr int kXcds = 8;
+constexpr int kGM = 4;
+constexpr int kGN = 8;
 constexpr int64_t kMaxRows = int64_t(1) << 22;
 constexpr int64_t kMaxVocab = int64_t(1) << 30;
 constexpr int kMaxD = 65536;
 
 static_assert(BM == BN, "one LDS stage shape for both operands");
-static_assert(BM * kOutRow <= 2 * kStage, "the epilogue tile reuses the A stages");
+static_assert(BM * kOutRow <= 4 * kStage, "the epilogue tile reuses the stages");
+static_assert(BN % SN == 0, "whole summaries per tile");
+static_assert((BM / kWaveM) * (BN / kWaveN) * 64 == kThreads, "one wave per wave tile");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -64,30 +82,57 @@ struct Geo {
   int64_t vocab_padded;
   int d;
   int m_tiles;
-  int64_t n_tiles;
+  int64_t n_tiles;  // workgroup tiles along the vocabulary
+  int64_t n_sum;    // summaries per row (SN columns each)
+  int64_t m_groups; // tile groups along the rows (kGM tiles each)
+  int64_t n_groups; // tile groups along the vocabulary (kGN tiles each)
 };
 
-// Thread t loads 16-byte chunks t, t+256, t+512, t+768 of each operand's
-// 128 x 64 stage: chunk c is row c/8, columns (c%8)*8 .. +7.
-__device__ __forceinline__ void load_stage(const Geo& g, int64_t row0, int64_t col0, int k0, u32x4 (&ra)[4],
-                                           u32x4 (&rb)[4]) {
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+// Tile of virtual workgroup v, or false when v has no tile.
+__device__ __forceinline__ bool tile_of(const Geo& g, int64_t v, int64_t& m_t, int64_t& n_t) {
+  const int64_t xcd = v % kXcds;
+  const int64_t slot = v / kXcds;
+  const int64_t k = (slot / (kGM * kGN)) * kXcds + xcd;  // group id
+  const int64_t local = slot % (kGM * kGN);
+  if (k >= g.m_groups * g.n_groups) return false;
+  m_t = (k % g.m_groups) * kGM + local % kGM;
+  n_t = (k / g.m_groups) * kGN + local / kGM;
+  return m_t < g.m_tiles && n_t < g.n_tiles;
+}
+
+// Thread t loads 16-byte chunks t + 256 i of each operand's BM x 64 stage:
+// chunk c is row c/8, columns (c%8)*8 .. +7.
+// Rows past the end load row 0 instead (always present) and are zeroed
+// afterwards, so the loads need no branches.
+__device__ __forceinline__ void load_stage(const Geo& g, int64_t row0, int64_t col0, int k0, u32x4 (&ra)[kChunks],
+                                           u32x4 (&rb)[kChunks]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kChunks; ++i) {
     const int c = static_cast<int>(threadIdx.x) + i * kThreads;
     const int r = c >> 3;
     const int kc = (c & 7) * 8;
     const int64_t gr = row0 + r;
     const int64_t gc = col0 + r;
-    ra[i] = (gr < g.n_rows) ? *reinterpret_cast<const u32x4*>(g.h + gr * g.ldh + k0 + kc) : zero;
-    rb[i] = (gc < g.vocab_real) ? *reinterpret_cast<const u32x4*>(g.w + gc * g.ldw + k0 + kc) : zero;
+    ra[i] = *reinterpret_cast<const u32x4*>(g.h + (gr < g.n_rows ? gr : 0) * g.ldh + k0 + kc);
+    rb[i] = *reinterpret_cast<const u32x4*>(g.w + (gc < g.vocab_real ? gc : 0) * g.ldw + k0 + kc);
+  }
+}
+
+__device__ __forceinline__ void zero_outside(const Geo& g, int64_t row0, int64_t col0, u32x4 (&ra)[kChunks],
+                                             u32x4 (&rb)[kChunks]) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int r = (static_cast<int>(threadIdx.x) + i * kThreads) >> 3;
+    ra[i] = (row0 + r < g.n_rows) ? ra[i] : zero;
+    rb[i] = (col0 + r < g.vocab_real) ? rb[i] : zero;
   }
 }
 
 __device__ __forceinline__ void store_stage(uint16_t* __restrict__ sa, uint16_t* __restrict__ sb,
-                                            const u32x4 (&ra)[4], const u32x4 (&rb)[4]) {
+                                            u32x4 (&ra)[kChunks], u32x4 (&rb)[kChunks]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kChunks; ++i) {
     const int c = static_cast<int>(threadIdx.x) + i * kThreads;
     const int r = c >> 3;
     const int kc = (c & 7) * 8;
@@ -96,31 +141,30 @@ __device__ __forceinline__ void store_stage(uint16_t* __restrict__ sa, uint16_t*
   }
 }
 
-// One 64-deep stage: 4 steps of 16, each 2 x 2 MFMAs. A fragment of a 32-row
-// block: lane l holds row l%32, k = 8*(l/32) .. +7 (same shape for the
-// vocabulary rows of the B operand).
-__device__ __forceinline__ void mma_stage(const uint16_t* __restrict__ sa, const uint16_t* __restrict__ sb, int wm,
-                                          int wn, f32x16 (&acc)[2][2]) {
+// A fragment of a 32-row block for K step kk of a stage: lane l holds row
+// l%32, k = 16 kk + 8 (l/32) .. +7 (the same shape for the vocabulary rows of
+// the B operand).
+__device__ __forceinline__ void load_frags(const uint16_t* __restrict__ sa, const uint16_t* __restrict__ sb, int wm,
+                                           int wn, int kk, bf16x8 (&a)[kMB], bf16x8 (&b)[kNB]) {
   const int lane = threadIdx.x & 63;
   const int fr = lane & 31;
   const int fk = (lane >> 5) * 8;
 #pragma unroll
-  for (int kk = 0; kk < BK / 16; ++kk) {
-    bf16x8 a[2], b[2];
+  for (int i = 0; i < kMB; ++i)
+    a[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * kWaveM + i * 32 + fr) * kLdsRow + kk * 16 + fk);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * 64 + i * 32 + fr) * kLdsRow + kk * 16 + fk);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(sb + (wn * 64 + j * 32 + fr) * kLdsRow + kk * 16 + fk);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
+  for (int j = 0; j < kNB; ++j)
+    b[j] = *reinterpret_cast<const bf16x8*>(sb + (wn * kWaveN + j * 32 + fr) * kLdsRow + kk * 16 + fk);
 }
 
-// Logits of one tile, rounded to BF16, into sO [128][kOutRow]. Accumulator
+__device__ __forceinline__ void mma_step(const bf16x8 (&a)[kMB], const bf16x8 (&b)[kNB], f32x16 (&acc)[kMB][kNB]) {
+#pragma unroll
+  for (int i = 0; i < kMB; ++i)
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// Logits of one tile, rounded to BF16, into sO [BM][kOutRow]. Accumulator
 // element 4a+b of block (i, j) is row 32i + 8a + 4(l/32) + b, column 32j + l%32
 // of the wave's quarter.
 __device__ __forceinline__ void tile_logits(const Geo& g, int64_t row0, int64_t col0, uint16_t* __restrict__ smem,
@@ -128,51 +172,71 @@ __device__ __forceinline__ void tile_logits(const Geo& g, int64_t row0, int64_t 
   uint16_t* sa = smem;                  // [2][kStage]
   uint16_t* sb = smem + 2 * kStage;     // [2][kStage]
   const int wave = threadIdx.x >> 6;
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
-  f32x16 acc[2][2];
+  const int wm = wave % (BM / kWaveM);
+  const int wn = wave / (BM / kWaveM);
+  f32x16 acc[kMB][kNB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kMB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kNB; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  u32x4 ra[4], rb[4];
+  u32x4 ra[kChunks], rb[kChunks];
   load_stage(g, row0, col0, 0, ra, rb);
+  zero_outside(g, row0, col0, ra, rb);
   store_stage(sa, sb, ra, rb);
   __syncthreads();
   const int kt_n = g.d / BK;
+  // Stage kt: its 4 K steps run from LDS buffer kt&1 with the fragments of
+  // step kk+1 loaded while step kk multiplies; stage kt+1's global loads are
+  // issued first and written to the other buffer after step 1 (that buffer
+  // was last read in stage kt-1, before the barrier that ended it).
   for (int kt = 0; kt < kt_n; ++kt) {
     const int cur = kt & 1;
     const bool more = kt + 1 < kt_n;
+    const uint16_t* ca = sa + cur * kStage;
+    const uint16_t* cb = sb + cur * kStage;
     if (more) load_stage(g, row0, col0, (kt + 1) * BK, ra, rb);
-    mma_stage(sa + cur * kStage, sb + cur * kStage, wm, wn, acc);
-    if (more) store_stage(sa + (cur ^ 1) * kStage, sb + (cur ^ 1) * kStage, ra, rb);
+    bf16x8 fa0[kMB], fb0[kNB], fa1[kMB], fb1[kNB];
+    load_frags(ca, cb, wm, wn, 0, fa0, fb0);
+    load_frags(ca, cb, wm, wn, 1, fa1, fb1);
+    mma_step(fa0, fb0, acc);
+    load_frags(ca, cb, wm, wn, 2, fa0, fb0);
+    mma_step(fa1, fb1, acc);
+    if (more) {
+      zero_outside(g, row0, col0, ra, rb);
+      store_stage(sa + (cur ^ 1) * kStage, sb + (cur ^ 1) * kStage, ra, rb);
+    }
+    load_frags(ca, cb, wm, wn, 3, fa1, fb1);
+    mma_step(fa0, fb0, acc);
+    mma_step(fa1, fb1, acc);
     __syncthreads();
   }
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kMB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kNB; ++j)
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const int r = wm * 64 + i * 32 + 8 * a + 4 * (lane >> 5) + b;
-          const int c = wn * 64 + j * 32 + (lane & 31);
+          const int r = wm * kWaveM + i * 32 + 8 * a + 4 * (lane >> 5) + b;
+          const int c = wn * kWaveN + j * 32 + (lane & 31);
           const __bf16 v = static_cast<__bf16>(acc[i][j][4 * a + b]);
           sO[r * kOutRow + c] = __builtin_bit_cast(uint16_t, v);
         }
   __syncthreads();
 }
 
-// Per-row summary of the tile's 128 columns; two threads per row, 64 columns each.
-__device__ __forceinline__ void tile_summaries(const Geo& g, int64_t row0, int64_t col0, int64_t n_t,
-                                               const uint16_t* __restrict__ sO, const float* __restrict__ temperature,
-                                               const int64_t* __restrict__ target, ShardSummary* __restrict__ ws) {
-  const int r = threadIdx.x >> 1;
+// Summary of columns [q*SN, (q+1)*SN) of row r of the tile; two neighbouring
+// threads share an item, 64 columns each.
+__device__ __forceinline__ void row_summary(const Geo& g, int64_t row0, int64_t tcol0, int r, int q,
+                                            const uint16_t* __restrict__ sO, const float* __restrict__ temperature,
+                                            const int64_t* __restrict__ target, ShardSummary* __restrict__ ws) {
   const int half = threadIdx.x & 1;
+  const int64_t col0 = tcol0 + q * SN;
+  const int64_t n_t = col0 / SN;
   const int64_t gr = row0 + r;
   const bool row_ok = gr < g.n_rows;
   const float t = row_ok ? temperature[gr] : 1.0f;
@@ -180,7 +244,7 @@ __device__ __forceinline__ void tile_summaries(const Geo& g, int64_t row0, int64
   const int64_t cb = col0 + half * 64;
   int64_t nv64 = g.vocab_real - cb;
   const int nvalid = static_cast<int>(nv64 < 0 ? 0 : (nv64 > 64 ? 64 : nv64));
-  const uint16_t* src = sO + r * kOutRow + half * 64;
+  const uint16_t* src = sO + r * kOutRow + q * SN + half * 64;
   // pass 1: maximum (and, for greedy rows, NaN/+inf and the first maximum)
   float m = -INFINITY;
   bool bad = false;
@@ -237,18 +301,29 @@ __device__ __forceinline__ void tile_summaries(const Geo& g, int64_t row0, int64
     const float other = __shfl_xor(mine, 1);
     s.r = rr;
     s.l = half == 0 ? mine + other : other + mine;
-    if (tg >= col0 && tg < col0 + BN && tg < g.vocab_real)
-      s.aux = static_cast<int32_t>(sO[r * kOutRow + static_cast<int>(tg - col0)]);
+    if (tg >= col0 && tg < col0 + SN && tg < g.vocab_real)
+      s.aux = static_cast<int32_t>(sO[r * kOutRow + q * SN + static_cast<int>(tg - col0)]);
   }
-  if (row_ok && half == 0) ws[gr * g.n_tiles + n_t] = s;
+  if (row_ok && half == 0) ws[gr * g.n_sum + n_t] = s;
+}
+
+__device__ __forceinline__ void tile_summaries(const Geo& g, int64_t row0, int64_t col0,
+                                               const uint16_t* __restrict__ sO, const float* __restrict__ temperature,
+                                               const int64_t* __restrict__ target, ShardSummary* __restrict__ ws) {
+  // (BM rows) x (BN / SN summaries) items, two threads each
+  for (int item = threadIdx.x >> 1; item < BM * (BN / SN); item += kThreads / 2) {
+    const int r = item % BM;
+    const int q = item / BM;
+    if (col0 + q * SN < g.vocab_padded) row_summary(g, row0, col0, r, q, sO, temperature, target, ws);
+  }
 }
 
 // Stores the BF16 tile; real columns from the tile, pads -inf.
 __device__ __forceinline__ void tile_store(const Geo& g, int64_t row0, int64_t col0, const uint16_t* __restrict__ sO,
                                            uint16_t* __restrict__ out, int64_t ldo) {
   for (int c = threadIdx.x; c < BM * (BN / 8); c += kThreads) {
-    const int r = c >> 4;
-    const int ch = c & 15;
+    const int r = c / (BN / 8);
+    const int ch = c % (BN / 8);
     const int64_t gr = row0 + r;
     const int64_t gc = col0 + ch * 8;
     if (gr >= g.n_rows || gc >= g.vocab_padded) continue;
@@ -267,38 +342,43 @@ __device__ __forceinline__ void tile_store(const Geo& g, int64_t row0, int64_t c
   }
 }
 
+__host__ __device__ __forceinline__ int64_t virtual_blocks(const Geo& g) {
+  const int64_t groups = g.m_groups * g.n_groups;
+  return ((groups + kXcds - 1) / kXcds) * kXcds * kGM * kGN;
+}
+
 template <bool kLogp>
 __global__ __launch_bounds__(kThreads) void k_linear(Geo g, const float* __restrict__ temperature,
                                                      const int64_t* __restrict__ target,
                                                      ShardSummary* __restrict__ ws, uint16_t* __restrict__ out,
                                                      int64_t ldo) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kStage];
-  uint16_t* sO = smem;  // the epilogue tile reuses the A stages
-  const int64_t tiles = static_cast<int64_t>(g.m_tiles) * g.n_tiles;
-  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {  // uniform across the workgroup
-    const int64_t m_t = tile % g.m_tiles;
-    const int64_t n_t = tile / g.m_tiles;
+  uint16_t* sO = smem;  // the epilogue tile reuses the stages
+  const int64_t n_virtual = virtual_blocks(g);
+  for (int64_t v = blockIdx.x; v < n_virtual; v += gridDim.x) {  // uniform across the workgroup
+    int64_t m_t, n_t;
+    if (!tile_of(g, v, m_t, n_t)) continue;
     const int64_t row0 = m_t * BM;
     const int64_t col0 = n_t * BN;
     tile_logits(g, row0, col0, smem, sO);
     if (kLogp)
-      tile_summaries(g, row0, col0, n_t, sO, temperature, target, ws);
+      tile_summaries(g, row0, col0, sO, temperature, target, ws);
     else
       tile_store(g, row0, col0, sO, out, ldo);
     __syncthreads();  // sO is overwritten by the next tile's first stage
   }
 }
 
-// One wave per row: the tile summaries merged in tile order.
+// One wave per row: the row's 128-column summaries merged in column order.
 __global__ __launch_bounds__(256) void k_lin_merge(const ShardSummary* __restrict__ ws, int64_t n_rows,
-                                                   int64_t n_tiles, int64_t vocab_real,
+                                                   int64_t n_sum, int64_t vocab_real,
                                                    const float* __restrict__ temperature,
                                                    const int64_t* __restrict__ target, float* __restrict__ logp_out,
                                                    float* __restrict__ lse_out) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= n_rows) return;  // uniform across the wave
-  const ShardSummary* __restrict__ s = ws + row * n_tiles;
+  const ShardSummary* __restrict__ s = ws + row * n_sum;
   const float t = temperature[row];
   const int64_t tg = target[row];
   float logp = NAN;
@@ -307,14 +387,14 @@ __global__ __launch_bounds__(256) void k_lin_merge(const ShardSummary* __restric
     if (t == 0.0f) {
       float m = -INFINITY;
       bool bad = false;
-      for (int64_t k = lane; k < n_tiles; k += 64) {
+      for (int64_t k = lane; k < n_sum; k += 64) {
         m = fmaxf(m, s[k].m);
         bad |= (s[k].l != s[k].l);
       }
       m = rlk::wave_max(m);
       bad = __any(bad);
       int64_t first = INT64_MAX;
-      for (int64_t k = lane; k < n_tiles; k += 64)
+      for (int64_t k = lane; k < n_sum; k += 64)
         if (s[k].m == m) {
           first = k;
           break;
@@ -327,12 +407,12 @@ __global__ __launch_bounds__(256) void k_lin_merge(const ShardSummary* __restric
         logp = (static_cast<int64_t>(s[first].aux) == tg) ? 0.0f : -INFINITY;
     } else {
       float rmax = -INFINITY;
-      for (int64_t k = lane; k < n_tiles; k += 64)
+      for (int64_t k = lane; k < n_sum; k += 64)
         if (s[k].l > 0.0f || s[k].l != s[k].l) rmax = fmaxf(rmax, s[k].r);
       rmax = rlk::wave_max(rmax);
       double acc = 0.0;
       bool nan = false;
-      for (int64_t k = lane; k < n_tiles; k += 64) {
+      for (int64_t k = lane; k < n_sum; k += 64) {
         const float l = s[k].l;
         if (l == 0.0f) continue;
         const float d = fmaxf(s[k].r - rmax, -2000.0f);
@@ -341,7 +421,7 @@ __global__ __launch_bounds__(256) void k_lin_merge(const ShardSummary* __restric
       }
       for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o);
       nan = __any(nan);
-      const int tbits = s[tg / BN].aux;
+      const int tbits = s[tg / SN].aux;
       if (!nan && acc > 0.0 && acc < INFINITY && rmax > -INFINITY && rmax < INFINITY && tbits >= 0) {
         const double lse2 = static_cast<double>(rmax) + log2(acc);
         const double lse_d = lse2 * rlk::kLn2;
@@ -394,12 +474,15 @@ static Geo make_geo(const uint16_t* h, int64_t n_rows, int64_t d, int64_t ldh, c
   g.d = static_cast<int>(d);
   g.m_tiles = static_cast<int>((n_rows + BM - 1) / BM);
   g.n_tiles = (L->vocab_padded + BN - 1) / BN;
+  g.n_sum = (L->vocab_padded + SN - 1) / SN;
+  g.m_groups = (g.m_tiles + kGM - 1) / kGM;
+  g.n_groups = (g.n_tiles + kGN - 1) / kGN;
   return g;
 }
 
 static unsigned grid_for(const Geo& g) {
-  const int64_t tiles = static_cast<int64_t>(g.m_tiles) * g.n_tiles;
-  return static_cast<unsigned>(tiles < kMaxGrid ? tiles : kMaxGrid);
+  const int64_t v = virtual_blocks(g);
+  return static_cast<unsigned>(v < kMaxGrid ? v : kMaxGrid);
 }
 
 }  // namespace rlk_lin
@@ -409,7 +492,7 @@ extern "C" {
 size_t rlk_linear_logp_workspace_bytes(int64_t n_rows, const rlk_vocab_layout* layout) {
   using namespace rlk_lin;
   if (check_layout(n_rows, layout) != RLK_OK) return 0;
-  return static_cast<size_t>(n_rows) * static_cast<size_t>((layout->vocab_padded + BN - 1) / BN) *
+  return static_cast<size_t>(n_rows) * static_cast<size_t>((layout->vocab_padded + SN - 1) / SN) *
          sizeof(ShardSummary);
 }
 
@@ -449,7 +532,7 @@ int32_t rlk_linear_logp(const uint16_t* hidden, int64_t n_rows, int64_t d_model,
   k_linear<true><<<dim3(grid_for(g)), dim3(kThreads), 0, stream>>>(g, temperature, target, ws, nullptr, 0);
   if ((st = launched()) != RLK_OK) return st;
   k_lin_merge<<<dim3(static_cast<unsigned>((n_rows + 3) / 4)), dim3(256), 0, stream>>>(
-      ws, n_rows, g.n_tiles, layout->vocab_real, temperature, target, logp_out, lse_out);
+      ws, n_rows, g.n_sum, layout->vocab_real, temperature, target, logp_out, lse_out);
   return launched();
 }
 
