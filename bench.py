@@ -18,8 +18,8 @@ events on the launch stream over the same region. `cpu_baseline` times the
 CPU oracle (float64 numpy, one core) on a bounded sample of the same rows.
 `secondary` reports rlk_logp_nucleus on the top-p 0.95 workload, the
 backward (rlk_logp_backward) on it, rlk_logp_nucleus on the per-request
-workload (64 requests x 128 rows) and the vocabulary-parallel form, for
-information.
+workload (64 requests x 128 rows), the vocabulary-parallel form, the
+gradient L2 norm and the fused LM-head linear + logprob, for information.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "logp tokens/s and logits HBM GB/s (% of peak), 8192×152576 BF16, 1 GPU"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_logp_full_8192x152576.json")
 KERNEL_SOURCES = [
     os.path.join(ROOT, "invariant_token_log_fp32_amd", "csrc", "rlk_logp.hip"),
@@ -295,6 +296,30 @@ def main():
                     "ms_per_step": ms_big, "achieved_GBs": nbytes / (ms_big * 1e-3) / 1e9,
                     "frac": nbytes / (ms_big * 1e-3) / 1e9 / HBM_PEAK_GBS})
         del xl
+        # fused LM-head linear + logprob at the Qwen3-8B shape (8192 x 4096 hidden, 151936 x 4096 projection)
+        d_model = datagen.QWEN3_D_MODEL
+        hb, wb = datagen.linear_inputs(41, w.n_rows, d_model, w.vocab_real)
+        hid = torch.from_numpy(hb.view(np.int16)).to(dev)
+        wt = torch.from_numpy(wb.view(np.int16)).to(dev)
+        del hb, wb
+        lws = torch.empty(rlk.linear_logp_workspace_bytes(w.n_rows, w.vocab_padded, w.vocab_real),
+                          dtype=torch.uint8, device=dev)
+        _, ms_ll = time_calls(lambda i: rlk.linear_logp(hid, wt, temp, tg, vocab_padded=w.vocab_padded, out=out,
+                                                        workspace=lws), 5, 2)
+        lgt = torch.empty((w.n_rows, w.vocab_padded), dtype=torch.bfloat16, device=dev)
+        _, ms_lin = time_calls(lambda i: rlk.linear(hid, wt, vocab_padded=w.vocab_padded, out=lgt), 5, 2)
+        wt16 = wt.view(torch.bfloat16).t()
+        _, ms_lib = time_calls(lambda i: torch.matmul(hid.view(torch.bfloat16), wt16), 5, 2)
+        flops = 2.0 * w.n_rows * w.vocab_real * d_model
+        sec.append({"workload": "linear-logp: 8192 x 4096 BF16 hidden states, 151936 x 4096 BF16 projection, T 0.7",
+                    "entry_point": "rlk_linear_logp", "ms_per_step": ms_ll, "tokens_per_s": w.n_rows / (ms_ll * 1e-3),
+                    "roofline": {"bound": "mfma", "achieved": flops / (ms_ll * 1e-3) / 1e12,
+                                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                 "frac": flops / (ms_ll * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+                    "unfused_ms": {"rlk_linear": ms_lin, "rlk_linear + rlk_logp_full": ms_lin + ms_event,
+                                   "hipBLASLt matmul (shape-dependent reduction order)": ms_lib,
+                                   "hipBLASLt matmul + rlk_logp_full": ms_lib + ms_event}})
+        del hid, wt, lgt, lws
         result["secondary"] = sec
 
     if not args.no_cpu_baseline:
