@@ -310,6 +310,13 @@ def main():
         _, ms_lin = time_calls(lambda i: rlk.linear(hid, wt, vocab_padded=w.vocab_padded, out=lgt), 5, 2)
         wt16 = wt.view(torch.bfloat16).t()
         _, ms_lib = time_calls(lambda i: torch.matmul(hid.view(torch.bfloat16), wt16), 5, 2)
+        # batch dependence of a row's logits: row block 0..6 computed alone vs inside the 8192-row batch
+        lib_full = torch.matmul(hid.view(torch.bfloat16), wt16)
+        lib_part = torch.matmul(hid[:7].contiguous().view(torch.bfloat16), wt16)
+        lib_var = float((lib_part.view(torch.int16) != lib_full[:7].view(torch.int16)).float().mean())
+        del lib_full, lib_part
+        own_part = rlk.linear(hid[:7].contiguous(), wt, vocab_padded=w.vocab_padded)
+        own_var = float((own_part.view(torch.int16) != lgt[:7].view(torch.int16)).float().mean())
         flops = 2.0 * w.n_rows * w.vocab_real * d_model
         sec.append({"workload": "linear-logp: 8192 x 4096 BF16 hidden states, 151936 x 4096 BF16 projection, T 0.7",
                     "entry_point": "rlk_linear_logp", "ms_per_step": ms_ll, "tokens_per_s": w.n_rows / (ms_ll * 1e-3),
@@ -318,7 +325,9 @@ def main():
                                  "frac": flops / (ms_ll * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
                     "unfused_ms": {"rlk_linear": ms_lin, "rlk_linear + rlk_logp_full": ms_lin + ms_event,
                                    "hipBLASLt matmul (shape-dependent reduction order)": ms_lib,
-                                   "hipBLASLt matmul + rlk_logp_full": ms_lib + ms_event}})
+                                   "hipBLASLt matmul + rlk_logp_full": ms_lib + ms_event},
+                    "logit_bits_changed_by_batch": {"rlk_linear": own_var, "hipBLASLt matmul": lib_var,
+                                                    "rows": "0..6 alone vs in the 8192-row batch"}})
         del hid, wt, lgt, lws
         result["secondary"] = sec
 
