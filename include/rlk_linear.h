@@ -33,7 +33,7 @@
  * never read), both BF16 bit patterns, 16-byte aligned, strides multiples of
  * 8; d_model a multiple of 64 in [64, 65536]. layout->row_stride is the row
  * stride of rlk_linear's output (and is only validated by rlk_linear_logp);
- * layout->groups is validated but not used.
+ * layout->groups is validated; only the vocabulary-parallel entry points below use it.
  *
  * Memory: every pointer is caller-owned DEVICE memory except `layout` (host);
  * nothing is allocated, freed or synchronised. Argument errors detectable on
@@ -75,6 +75,35 @@ int32_t rlk_linear_logp(const uint16_t* hidden, int64_t n_rows, int64_t d_model,
 
 /* n_rows * ceil(vocab_padded / 128) * 16 bytes; 0 for an invalid layout or n_rows < 0. */
 size_t rlk_linear_logp_workspace_bytes(int64_t n_rows, const rlk_vocab_layout* layout);
+
+/* Vocabulary-parallel form [REPRO-CANON]: with G = layout->groups ranks, rank
+ * r holds the projection rows of columns [r*C, (r+1)*C), C = vocab_padded / G
+ * (a multiple of 128), and the same hidden states.
+ * rlk_linear_logp_summaries: rank `rank` reduces its columns to n_rows * C/128
+ * summaries of 128 columns (16 bytes each, record (i, j) at i * C/128 + j,
+ * the target's BF16 logit carried by the summary holding the target column).
+ *   weight_shard  the rank's projection rows: row j is vocabulary entry
+ *                 r*C + j, for the min(C, vocab_real - r*C) entries below
+ *                 vocab_real (none when r*C >= vocab_real; the pointer must
+ *                 still be valid and aligned)
+ *   summaries_out rlk_linear_logp_summary_bytes(n_rows, layout) bytes
+ * rlk_linear_logp_merge: from every rank's summaries concatenated in rank
+ * order (what an all-gather yields), the same logp_out / lse_out bytes as
+ * rlk_linear_logp on the whole projection, for every G.
+ * A C that is not a multiple of 128 or a rank outside [0, G) is
+ * RLK_ERR_SHAPE; a short buffer RLK_ERR_WORKSPACE. */
+int32_t rlk_linear_logp_summaries(const uint16_t* hidden, int64_t n_rows, int64_t d_model, int64_t hidden_stride,
+                                  const uint16_t* weight_shard, int64_t weight_stride, const rlk_vocab_layout* layout,
+                                  int32_t rank, const float* temperature, const int64_t* target,
+                                  void* summaries_out, size_t summaries_bytes, hipStream_t stream);
+
+int32_t rlk_linear_logp_merge(const void* summaries, size_t summaries_bytes, int64_t n_rows,
+                              const rlk_vocab_layout* layout, const float* temperature, const int64_t* target,
+                              float* logp_out, float* lse_out, hipStream_t stream);
+
+/* One rank's summary bytes: n_rows * (vocab_padded / groups / 128) * 16; 0 for
+ * an invalid layout, n_rows < 0 or a per-rank width that is not a multiple of 128. */
+size_t rlk_linear_logp_summary_bytes(int64_t n_rows, const rlk_vocab_layout* layout);
 
 #ifdef __cplusplus
 }

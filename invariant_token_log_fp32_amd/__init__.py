@@ -19,7 +19,7 @@ __all__ = [
     "LIB_PATH", "HEADER_PATH", "VocabLayout", "load_library", "status_string", "workspace_bytes",
     "summary_bytes", "logp_full", "logp_nucleus", "logp_shard_summaries", "logp_merge", "logp_backward",
     "support_state_fields", "l2norm", "l2norm_zero", "l2norm_accumulate", "l2norm_finalize", "NORM_BIN_WORDS",
-    "linear", "linear_logp", "linear_logp_workspace_bytes",
+    "linear", "linear_logp", "linear_logp_workspace_bytes", "linear_logp_summaries", "linear_logp_merge",
     "RlkError", "N_SHARDS",
 ]
 
@@ -98,6 +98,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rlk_linear_logp.restype = i32
     lib.rlk_linear_logp_workspace_bytes.argtypes = [i64, lay]
     lib.rlk_linear_logp_workspace_bytes.restype = sz
+    lib.rlk_linear_logp_summaries.argtypes = [vp, i64, i64, i64, vp, i64, lay, i32, vp, vp, vp, sz, vp]
+    lib.rlk_linear_logp_summaries.restype = i32
+    lib.rlk_linear_logp_merge.argtypes = [vp, sz, i64, lay, vp, vp, vp, vp, vp]
+    lib.rlk_linear_logp_merge.restype = i32
+    lib.rlk_linear_logp_summary_bytes.argtypes = [i64, lay]
+    lib.rlk_linear_logp_summary_bytes.restype = sz
     _lib = lib
     return lib
 
@@ -484,4 +490,50 @@ def linear_logp(hidden, weight, temperature, target, *, vocab_padded: int, retur
                              workspace.numel(), _stream_handle(stream, dev))
     if st != RLK_OK:
         raise RlkError(st, "rlk_linear_logp")
+    return (out, lse_out) if return_lse else out
+
+
+def linear_logp_summaries(hidden, weight_shard, temperature, target, *, rank: int, groups: int, vocab_real: int,
+                          vocab_padded: int, out=None, stream=None):
+    """One rank's 128-column summaries of bf16(hidden . weight^T) over its columns
+    [rank*C, (rank+1)*C), C = vocab_padded / groups (rlk_linear_logp_summaries).
+    ``weight_shard`` holds that rank's projection rows below vocab_real."""
+    torch = _torch()
+    ldh = _bf16_matrix(hidden, "hidden")
+    ldw = _bf16_matrix(weight_shard, "weight_shard")
+    n, d = hidden.shape
+    dev = hidden.device
+    temperature = _per_row(temperature, n, torch.float32, dev, "temperature")
+    target = _per_row(target, n, torch.int64, dev, "target")
+    lay = make_layout(vocab_padded, vocab_real, vocab_padded, groups)
+    lib = load_library()
+    need = int(lib.rlk_linear_logp_summary_bytes(n, ctypes.byref(lay)))
+    if out is None:
+        out = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = lib.rlk_linear_logp_summaries(hidden.data_ptr(), n, d, ldh, weight_shard.data_ptr(), ldw, ctypes.byref(lay),
+                                       int(rank), temperature.data_ptr(), target.data_ptr(), out.data_ptr(),
+                                       out.numel(), _stream_handle(stream, dev))
+    if st != RLK_OK:
+        raise RlkError(st, "rlk_linear_logp_summaries")
+    return out
+
+
+def linear_logp_merge(summaries, temperature, target, *, n_rows: int, groups: int, vocab_real: int,
+                      vocab_padded: int, return_lse: bool = False, out=None, lse_out=None, stream=None):
+    """Merge every rank's linear-logp summaries, concatenated in rank order
+    (rlk_linear_logp_merge); equals rlk_linear_logp on the whole projection."""
+    torch = _torch()
+    dev = summaries.device
+    temperature = _per_row(temperature, n_rows, torch.float32, dev, "temperature")
+    target = _per_row(target, n_rows, torch.int64, dev, "target")
+    out = out if out is not None else torch.empty(n_rows, dtype=torch.float32, device=dev)
+    if return_lse and lse_out is None:
+        lse_out = torch.empty(n_rows, dtype=torch.float32, device=dev)
+    lay = make_layout(vocab_padded, vocab_real, vocab_padded, groups)
+    nbytes = summaries.numel() * summaries.element_size()
+    st = load_library().rlk_linear_logp_merge(
+        summaries.data_ptr(), nbytes, int(n_rows), ctypes.byref(lay), temperature.data_ptr(), target.data_ptr(),
+        out.data_ptr(), lse_out.data_ptr() if lse_out is not None else None, _stream_handle(stream, dev))
+    if st != RLK_OK:
+        raise RlkError(st, "rlk_linear_logp_merge")
     return (out, lse_out) if return_lse else out

@@ -82,8 +82,11 @@ struct Geo {
   int64_t vocab_padded;
   int d;
   int m_tiles;
+  int64_t col_base; // first (global) vocabulary column of this launch
+  int64_t col_end;  // end of its columns (multiple of SN, at most vocab_padded)
+  int64_t w_end;    // end of the columns with a projection row: min(col_end, vocab_real)
   int64_t n_tiles;  // workgroup tiles along the vocabulary
-  int64_t n_sum;    // summaries per row (SN columns each)
+  int64_t n_sum;    // summaries per row in this launch (SN columns each)
   int64_t m_groups; // tile groups along the rows (kGM tiles each)
   int64_t n_groups; // tile groups along the vocabulary (kGN tiles each)
 };
@@ -102,8 +105,8 @@ __device__ __forceinline__ bool tile_of(const Geo& g, int64_t v, int64_t& m_t, i
 
 // Thread t loads 16-byte chunks t + 256 i of each operand's BM x 64 stage:
 // chunk c is row c/8, columns (c%8)*8 .. +7.
-// Rows past the end load row 0 instead (always present) and are zeroed
-// afterwards, so the loads need no branches.
+// Rows past the end load the first row instead and are zeroed afterwards, so
+// the loads need no branches (g.w holds the rows from column col_base on).
 __device__ __forceinline__ void load_stage(const Geo& g, int64_t row0, int64_t col0, int k0, u32x4 (&ra)[kChunks],
                                            u32x4 (&rb)[kChunks]) {
 #pragma unroll
@@ -114,7 +117,9 @@ __device__ __forceinline__ void load_stage(const Geo& g, int64_t row0, int64_t c
     const int64_t gr = row0 + r;
     const int64_t gc = col0 + r;
     ra[i] = *reinterpret_cast<const u32x4*>(g.h + (gr < g.n_rows ? gr : 0) * g.ldh + k0 + kc);
-    rb[i] = *reinterpret_cast<const u32x4*>(g.w + (gc < g.vocab_real ? gc : 0) * g.ldw + k0 + kc);
+    rb[i] = (g.w_end > g.col_base)
+                ? *reinterpret_cast<const u32x4*>(g.w + (gc < g.w_end ? gc - g.col_base : 0) * g.ldw + k0 + kc)
+                : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -125,7 +130,7 @@ __device__ __forceinline__ void zero_outside(const Geo& g, int64_t row0, int64_t
   for (int i = 0; i < kChunks; ++i) {
     const int r = (static_cast<int>(threadIdx.x) + i * kThreads) >> 3;
     ra[i] = (row0 + r < g.n_rows) ? ra[i] : zero;
-    rb[i] = (col0 + r < g.vocab_real) ? rb[i] : zero;
+    rb[i] = (col0 + r < g.w_end) ? rb[i] : zero;
   }
 }
 
@@ -236,13 +241,13 @@ __device__ __forceinline__ void row_summary(const Geo& g, int64_t row0, int64_t 
                                             const int64_t* __restrict__ target, ShardSummary* __restrict__ ws) {
   const int half = threadIdx.x & 1;
   const int64_t col0 = tcol0 + q * SN;
-  const int64_t n_t = col0 / SN;
+  const int64_t n_t = (col0 - g.col_base) / SN;  // summary index in this launch
   const int64_t gr = row0 + r;
   const bool row_ok = gr < g.n_rows;
   const float t = row_ok ? temperature[gr] : 1.0f;
   const int64_t tg = row_ok ? target[gr] : -1;
   const int64_t cb = col0 + half * 64;
-  int64_t nv64 = g.vocab_real - cb;
+  int64_t nv64 = g.w_end - cb;
   const int nvalid = static_cast<int>(nv64 < 0 ? 0 : (nv64 > 64 ? 64 : nv64));
   const uint16_t* src = sO + r * kOutRow + q * SN + half * 64;
   // pass 1: maximum (and, for greedy rows, NaN/+inf and the first maximum)
@@ -314,7 +319,7 @@ __device__ __forceinline__ void tile_summaries(const Geo& g, int64_t row0, int64
   for (int item = threadIdx.x >> 1; item < BM * (BN / SN); item += kThreads / 2) {
     const int r = item % BM;
     const int q = item / BM;
-    if (col0 + q * SN < g.vocab_padded) row_summary(g, row0, col0, r, q, sO, temperature, target, ws);
+    if (col0 + q * SN < g.col_end) row_summary(g, row0, col0, r, q, sO, temperature, target, ws);
   }
 }
 
@@ -359,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void k_linear(Geo g, const float* __restr
     int64_t m_t, n_t;
     if (!tile_of(g, v, m_t, n_t)) continue;
     const int64_t row0 = m_t * BM;
-    const int64_t col0 = n_t * BN;
+    const int64_t col0 = g.col_base + n_t * BN;
     tile_logits(g, row0, col0, smem, sO);
     if (kLogp)
       tile_summaries(g, row0, col0, sO, temperature, target, ws);
@@ -369,16 +374,22 @@ __global__ __launch_bounds__(kThreads) void k_linear(Geo g, const float* __restr
   }
 }
 
+// Summary k (global column order) of a row in rank-major storage: rank
+// k / per_rank holds n_rows x per_rank records.
+__device__ __forceinline__ const ShardSummary& summary_at(const ShardSummary* __restrict__ ws, int64_t n_rows,
+                                                          int64_t per_rank, int64_t row, int64_t k) {
+  return ws[((k / per_rank) * n_rows + row) * per_rank + k % per_rank];
+}
+
 // One wave per row: the row's 128-column summaries merged in column order.
 __global__ __launch_bounds__(256) void k_lin_merge(const ShardSummary* __restrict__ ws, int64_t n_rows,
-                                                   int64_t n_sum, int64_t vocab_real,
+                                                   int64_t n_sum, int64_t per_rank, int64_t vocab_real,
                                                    const float* __restrict__ temperature,
                                                    const int64_t* __restrict__ target, float* __restrict__ logp_out,
                                                    float* __restrict__ lse_out) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= n_rows) return;  // uniform across the wave
-  const ShardSummary* __restrict__ s = ws + row * n_sum;
   const float t = temperature[row];
   const int64_t tg = target[row];
   float logp = NAN;
@@ -388,14 +399,15 @@ __global__ __launch_bounds__(256) void k_lin_merge(const ShardSummary* __restric
       float m = -INFINITY;
       bool bad = false;
       for (int64_t k = lane; k < n_sum; k += 64) {
-        m = fmaxf(m, s[k].m);
-        bad |= (s[k].l != s[k].l);
+        const ShardSummary sk = summary_at(ws, n_rows, per_rank, row, k);
+        m = fmaxf(m, sk.m);
+        bad |= (sk.l != sk.l);
       }
       m = rlk::wave_max(m);
       bad = __any(bad);
       int64_t first = INT64_MAX;
       for (int64_t k = lane; k < n_sum; k += 64)
-        if (s[k].m == m) {
+        if (summary_at(ws, n_rows, per_rank, row, k).m == m) {
           first = k;
           break;
         }
@@ -404,24 +416,26 @@ __global__ __launch_bounds__(256) void k_lin_merge(const ShardSummary* __restric
         first = other < first ? other : first;
       }
       if (!bad && m != -INFINITY && first != INT64_MAX)
-        logp = (static_cast<int64_t>(s[first].aux) == tg) ? 0.0f : -INFINITY;
+        logp = (static_cast<int64_t>(summary_at(ws, n_rows, per_rank, row, first).aux) == tg) ? 0.0f : -INFINITY;
     } else {
       float rmax = -INFINITY;
-      for (int64_t k = lane; k < n_sum; k += 64)
-        if (s[k].l > 0.0f || s[k].l != s[k].l) rmax = fmaxf(rmax, s[k].r);
+      for (int64_t k = lane; k < n_sum; k += 64) {
+        const ShardSummary sk = summary_at(ws, n_rows, per_rank, row, k);
+        if (sk.l > 0.0f || sk.l != sk.l) rmax = fmaxf(rmax, sk.r);
+      }
       rmax = rlk::wave_max(rmax);
       double acc = 0.0;
       bool nan = false;
       for (int64_t k = lane; k < n_sum; k += 64) {
-        const float l = s[k].l;
-        if (l == 0.0f) continue;
-        const float d = fmaxf(s[k].r - rmax, -2000.0f);
-        acc = acc + ldexp(static_cast<double>(l), static_cast<int>(d));
-        nan |= (s[k].r != s[k].r) || (l != l);
+        const ShardSummary sk = summary_at(ws, n_rows, per_rank, row, k);
+        if (sk.l == 0.0f) continue;
+        const float d = fmaxf(sk.r - rmax, -2000.0f);
+        acc = acc + ldexp(static_cast<double>(sk.l), static_cast<int>(d));
+        nan |= (sk.r != sk.r) || (sk.l != sk.l);
       }
       for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o);
       nan = __any(nan);
-      const int tbits = s[tg / SN].aux;
+      const int tbits = summary_at(ws, n_rows, per_rank, row, tg / SN).aux;
       if (!nan && acc > 0.0 && acc < INFINITY && rmax > -INFINITY && rmax < INFINITY && tbits >= 0) {
         const double lse2 = static_cast<double>(rmax) + log2(acc);
         const double lse_d = lse2 * rlk::kLn2;
@@ -462,7 +476,7 @@ static int32_t check_operands(int64_t n_rows, int64_t d, int64_t ldh, int64_t ld
 }
 
 static Geo make_geo(const uint16_t* h, int64_t n_rows, int64_t d, int64_t ldh, const uint16_t* w, int64_t ldw,
-                    const rlk_vocab_layout* L) {
+                    const rlk_vocab_layout* L, int64_t col_base, int64_t col_end) {
   Geo g;
   g.h = h;
   g.w = w;
@@ -473,8 +487,11 @@ static Geo make_geo(const uint16_t* h, int64_t n_rows, int64_t d, int64_t ldh, c
   g.vocab_padded = L->vocab_padded;
   g.d = static_cast<int>(d);
   g.m_tiles = static_cast<int>((n_rows + BM - 1) / BM);
-  g.n_tiles = (L->vocab_padded + BN - 1) / BN;
-  g.n_sum = (L->vocab_padded + SN - 1) / SN;
+  g.col_base = col_base;
+  g.col_end = col_end;
+  g.w_end = col_end < L->vocab_real ? col_end : L->vocab_real;
+  g.n_tiles = (col_end - col_base + BN - 1) / BN;
+  g.n_sum = (col_end - col_base + SN - 1) / SN;
   g.m_groups = (g.m_tiles + kGM - 1) / kGM;
   g.n_groups = (g.n_tiles + kGN - 1) / kGN;
   return g;
@@ -507,7 +524,8 @@ int32_t rlk_linear(const uint16_t* hidden, int64_t n_rows, int64_t d_model, int6
   if (n_rows == 0) return RLK_OK;
   if (!hidden || !weight || !logits_out) return RLK_ERR_NULL;
   if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(logits_out, 16)) return RLK_ERR_ALIGN;
-  const Geo g = make_geo(hidden, n_rows, d_model, hidden_stride, weight, weight_stride, layout);
+  const Geo g = make_geo(hidden, n_rows, d_model, hidden_stride, weight, weight_stride, layout, 0,
+                         layout->vocab_padded);
   k_linear<false><<<dim3(grid_for(g)), dim3(kThreads), 0, stream>>>(g, nullptr, nullptr, nullptr, logits_out,
                                                                      layout->row_stride);
   return launched();
@@ -527,12 +545,67 @@ int32_t rlk_linear_logp(const uint16_t* hidden, int64_t n_rows, int64_t d_model,
       !aligned(target, 8) || !aligned(logp_out, 4) || (lse_out && !aligned(lse_out, 4)))
     return RLK_ERR_ALIGN;
   if (workspace_bytes < rlk_linear_logp_workspace_bytes(n_rows, layout)) return RLK_ERR_WORKSPACE;
-  const Geo g = make_geo(hidden, n_rows, d_model, hidden_stride, weight, weight_stride, layout);
+  const Geo g = make_geo(hidden, n_rows, d_model, hidden_stride, weight, weight_stride, layout, 0,
+                         layout->vocab_padded);
   ShardSummary* ws = static_cast<ShardSummary*>(workspace);
   k_linear<true><<<dim3(grid_for(g)), dim3(kThreads), 0, stream>>>(g, temperature, target, ws, nullptr, 0);
   if ((st = launched()) != RLK_OK) return st;
   k_lin_merge<<<dim3(static_cast<unsigned>((n_rows + 3) / 4)), dim3(256), 0, stream>>>(
-      ws, n_rows, g.n_sum, layout->vocab_real, temperature, target, logp_out, lse_out);
+      ws, n_rows, g.n_sum, g.n_sum, layout->vocab_real, temperature, target, logp_out, lse_out);
+  return launched();
+}
+
+size_t rlk_linear_logp_summary_bytes(int64_t n_rows, const rlk_vocab_layout* layout) {
+  using namespace rlk_lin;
+  if (check_layout(n_rows, layout) != RLK_OK) return 0;
+  const int64_t cols = layout->vocab_padded / layout->groups;
+  if (cols % SN != 0) return 0;
+  return static_cast<size_t>(n_rows) * static_cast<size_t>(cols / SN) * sizeof(ShardSummary);
+}
+
+int32_t rlk_linear_logp_summaries(const uint16_t* hidden, int64_t n_rows, int64_t d_model, int64_t hidden_stride,
+                                  const uint16_t* weight_shard, int64_t weight_stride, const rlk_vocab_layout* layout,
+                                  int32_t rank, const float* temperature, const int64_t* target,
+                                  void* summaries_out, size_t summaries_bytes, hipStream_t stream) {
+  using namespace rlk_lin;
+  int32_t st = check_layout(n_rows, layout);
+  if (st != RLK_OK) return st;
+  if ((st = check_operands(n_rows, d_model, hidden_stride, weight_stride, layout)) != RLK_OK) return st;
+  const int64_t cols = layout->vocab_padded / layout->groups;
+  if (cols % SN != 0 || rank < 0 || rank >= layout->groups) return RLK_ERR_SHAPE;
+  if (n_rows == 0) return RLK_OK;
+  if (!hidden || !weight_shard || !temperature || !target || !summaries_out) return RLK_ERR_NULL;
+  if (!aligned(hidden, 16) || !aligned(weight_shard, 16) || !aligned(summaries_out, 16) ||
+      !aligned(temperature, 4) || !aligned(target, 8))
+    return RLK_ERR_ALIGN;
+  if (summaries_bytes < rlk_linear_logp_summary_bytes(n_rows, layout)) return RLK_ERR_WORKSPACE;
+  const int64_t col_base = static_cast<int64_t>(rank) * cols;
+  const Geo g = make_geo(hidden, n_rows, d_model, hidden_stride, weight_shard, weight_stride, layout, col_base,
+                         col_base + cols);
+  k_linear<true><<<dim3(grid_for(g)), dim3(kThreads), 0, stream>>>(g, temperature, target,
+                                                                    static_cast<ShardSummary*>(summaries_out),
+                                                                    nullptr, 0);
+  return launched();
+}
+
+int32_t rlk_linear_logp_merge(const void* summaries, size_t summaries_bytes, int64_t n_rows,
+                              const rlk_vocab_layout* layout, const float* temperature, const int64_t* target,
+                              float* logp_out, float* lse_out, hipStream_t stream) {
+  using namespace rlk_lin;
+  int32_t st = check_layout(n_rows, layout);
+  if (st != RLK_OK) return st;
+  const int64_t cols = layout->vocab_padded / layout->groups;
+  if (cols % SN != 0) return RLK_ERR_SHAPE;
+  if (n_rows == 0) return RLK_OK;
+  if (!summaries || !temperature || !target || !logp_out) return RLK_ERR_NULL;
+  if (!aligned(summaries, 16) || !aligned(temperature, 4) || !aligned(target, 8) || !aligned(logp_out, 4) ||
+      (lse_out && !aligned(lse_out, 4)))
+    return RLK_ERR_ALIGN;
+  if (summaries_bytes < rlk_linear_logp_summary_bytes(n_rows, layout) * static_cast<size_t>(layout->groups))
+    return RLK_ERR_WORKSPACE;
+  k_lin_merge<<<dim3(static_cast<unsigned>((n_rows + 3) / 4)), dim3(256), 0, stream>>>(
+      static_cast<const ShardSummary*>(summaries), n_rows, layout->vocab_padded / SN, cols / SN,
+      layout->vocab_real, temperature, target, logp_out, lse_out);
   return launched();
 }
 

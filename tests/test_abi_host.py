@@ -51,7 +51,8 @@ def test_every_declared_function_is_exported(lib):
     assert set(names) == {"rlk_logp_full", "rlk_logp_nucleus", "rlk_logp_workspace_bytes", "rlk_status_string",
                           "rlk_logp_shard_summaries", "rlk_logp_merge", "rlk_logp_summary_bytes",
                           "rlk_logp_backward", "rlk_l2norm", "rlk_l2norm_zero", "rlk_l2norm_accumulate",
-                          "rlk_l2norm_finalize", "rlk_linear", "rlk_linear_logp", "rlk_linear_logp_workspace_bytes"}
+                          "rlk_l2norm_finalize", "rlk_linear", "rlk_linear_logp", "rlk_linear_logp_workspace_bytes",
+                          "rlk_linear_logp_summaries", "rlk_linear_logp_merge", "rlk_linear_logp_summary_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -260,3 +261,44 @@ def test_linear_zero_rows_and_workspace_size(lib):
     L2 = lay(vp=1088, vr=1000)
     assert lib.rlk_linear_logp_workspace_bytes(3, ctypes.byref(L2)) == 3 * 9 * 16
     assert lib.rlk_linear_logp_workspace_bytes(-1, ctypes.byref(L2)) == 0
+
+
+def linsum(lib, h=P, n=4, d=128, ldh=128, w=P + 0x100000, ldw=128, L=None, rank=0, t=P + 0x300000,
+           tg=P + 0x300100, out=P + 0x400000, ob=1 << 20):
+    L = L if L is not None else lay(groups=2)
+    return lib.rlk_linear_logp_summaries(h, n, d, ldh, w, ldw, ctypes.byref(L) if L is not False else None, rank, t,
+                                         tg, out, ob, None)
+
+
+def linmerge(lib, summ=P + 0x400000, sb=1 << 20, n=4, L=None, t=P + 0x300000, tg=P + 0x300100, out=P + 0x300200,
+             lse=None):
+    L = L if L is not None else lay(groups=2)
+    return lib.rlk_linear_logp_merge(summ, sb, n, ctypes.byref(L) if L is not False else None, t, tg, out, lse, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rank=-1), SHAPE), (dict(rank=2), SHAPE), (dict(L=lay(vp=1088, vr=1000, groups=8)), SHAPE),
+    (dict(h=None), NULL), (dict(w=None), NULL), (dict(t=None), NULL), (dict(tg=None), NULL), (dict(out=None), NULL),
+    (dict(out=P + 0x400008), ALIGN), (dict(w=P + 0x100004), ALIGN), (dict(ob=4 * 4 * 16 - 1), WS),
+    (dict(L=lay(groups=3)), GROUPS), (dict(d=48, ldh=48, ldw=48), SHAPE),
+])
+def test_linear_logp_summaries_rejects_bad_arguments(lib, kw, code):
+    assert linsum(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(summ=None), NULL), (dict(t=None), NULL), (dict(out=None), NULL), (dict(summ=P + 0x400004), ALIGN),
+    (dict(lse=P + 0x300302), ALIGN), (dict(sb=4 * 8 * 16 - 1), WS), (dict(L=lay(vp=1088, vr=1000, groups=8)), SHAPE),
+])
+def test_linear_logp_merge_rejects_bad_arguments(lib, kw, code):
+    assert linmerge(lib, **kw) == code
+
+
+def test_linear_logp_summary_sizes(lib):
+    assert linsum(lib, n=0, h=None, w=None, t=None, tg=None, out=None, ob=0) == OK
+    assert linmerge(lib, n=0, summ=None, sb=0, t=None, tg=None, out=None) == OK
+    for g in (1, 2, 4, 8):
+        L = lay(vp=152576, vr=151936, groups=g)
+        assert lib.rlk_linear_logp_summary_bytes(8192, ctypes.byref(L)) == 8192 * (1192 // g) * 16
+    L = lay(vp=1088, vr=1000, groups=8)
+    assert lib.rlk_linear_logp_summary_bytes(8, ctypes.byref(L)) == 0

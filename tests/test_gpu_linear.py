@@ -163,3 +163,58 @@ def test_full_size_exact():
     ref = rlk.logp_full(logits, t_d, tg_d, vocab_real=vr)
     torch.cuda.synchronize()
     assert_close(to_host(lp), to_host(ref), tol=2e-5, what="fused vs unfused, all rows")
+
+
+def sharded_linear_logp(h, wb_host, t_d, tg_d, vr, vp, groups):
+    """Each emulated rank gets only its own projection rows; summaries are
+    concatenated in rank order and merged."""
+    import torch
+    n = h.shape[0]
+    cols = vp // groups
+    d = wb_host.shape[1]
+    parts = []
+    for r in range(groups):
+        lo, hi = r * cols, min((r + 1) * cols, vr)
+        rows = wb_host[lo:hi] if hi > lo else np.zeros((1, d), np.uint16)   # a valid pointer when the rank owns no row
+        w_r = torch.from_numpy(np.ascontiguousarray(rows).view(np.int16)).to("cuda:0")
+        parts.append(rlk.linear_logp_summaries(h, w_r, t_d, tg_d, rank=r, groups=groups, vocab_real=vr,
+                                               vocab_padded=vp))
+    return rlk.linear_logp_merge(torch.cat(parts), t_d, tg_d, n_rows=n, groups=groups, vocab_real=vr,
+                                 vocab_padded=vp, return_lse=True)
+
+
+def test_vocabulary_parallel_form_matches_one_gpu():
+    """Ranks owning 1/2/4/8 of the columns (one rank owning no real row at
+    8 ranks) give the bytes of the one-GPU call, greedy rows included."""
+    import torch
+    for seed, n, d, vr, vp in [(51, 300, 256, 3000, 4096), (52, 130, 128, 4096, 4096), (53, 17, 192, 999, 1024)]:
+        hb, wb = datagen.linear_inputs(seed, n, d, vr)
+        h = padded(hb, d)
+        temps, tg = params(n, vr, seed)
+        t_d, tg_d = upload(temps, torch.float32), upload(tg, torch.int64)
+        one, one_lse = rlk.linear_logp(h, padded(wb, d), t_d, tg_d, vocab_padded=vp, return_lse=True)
+        torch.cuda.synchronize()
+        for groups in (1, 2, 4, 8):
+            if (vp // groups) % 128:
+                continue
+            say(f"case: sharded linear-logp {n} x {d} x {vr}/{vp}, {groups} ranks")
+            lp, lse = sharded_linear_logp(h, wb, t_d, tg_d, vr, vp, groups)
+            torch.cuda.synchronize()
+            assert to_host(lp).tobytes() == to_host(one).tobytes(), f"{groups} ranks: logp bytes differ"
+            assert to_host(lse).tobytes() == to_host(one_lse).tobytes(), f"{groups} ranks: lse bytes differ"
+
+
+def test_vocabulary_parallel_full_size_eight_ranks():
+    import torch
+    n, d, vr, vp = 8192, datagen.QWEN3_D_MODEL, datagen.QWEN3_VOCAB_REAL, datagen.QWEN3_VOCAB_PADDED
+    say("case: sharded linear-logp at 8192 x 4096 x 151936, 8 ranks of 19072 columns")
+    hb, wb = datagen.linear_inputs(61, n, d, vr)
+    h = torch.from_numpy(hb.view(np.int16)).to("cuda:0")
+    w = torch.from_numpy(wb.view(np.int16)).to("cuda:0")
+    temps, tg = params(n, vr, 61)
+    t_d, tg_d = upload(temps, torch.float32), upload(tg, torch.int64)
+    one = rlk.linear_logp(h, w, t_d, tg_d, vocab_padded=vp)
+    del w
+    lp, _ = sharded_linear_logp(h, wb, t_d, tg_d, vr, vp, 8)
+    torch.cuda.synchronize()
+    assert to_host(lp).tobytes() == to_host(one).tobytes()
