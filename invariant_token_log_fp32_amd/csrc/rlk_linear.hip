@@ -12,8 +12,9 @@
 //                    loop over tiles, in XCD-aware groups of 4 x 8 tiles
 //                    that share operand panels in L2; 8 waves (two per SIMD,
 //                    so one wave's waits overlap the other's matrix work),
-//                    each 128 x 64 as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16.
-//                    K runs in 64-wide stages through double-buffered LDS
+//                    each 128 x 64 as 8 x 4 blocks of v_mfma_f32_16x16x32_bf16.
+//                    K runs in 64-wide stages (two MFMA steps of 32) through
+//                    double-buffered LDS
 //                    (rows padded to 144 bytes, so the 16-byte fragment reads
 //                    of a wave hit distinct banks); the next stage's global
 //                    loads are in flight while the current one is multiplied.
@@ -46,8 +47,8 @@ constexpr int SN = 128;                 // columns per summary (nests in the can
 constexpr int kThreads = 512;           // 8 waves, 2 x 4, each 128 x 64 (two waves per SIMD)
 constexpr int kWaveM = 128;
 constexpr int kWaveN = 64;
-constexpr int kMB = kWaveM / 32;        // 32 x 32 MFMA blocks per wave
-constexpr int kNB = kWaveN / 32;
+constexpr int kMB = kWaveM / 16;        // 16 x 16 MFMA blocks per wave
+constexpr int kNB = kWaveN / 16;
 constexpr int kLdsRow = BK + 8;         // bf16 per LDS row: 144 bytes
 constexpr int kStage = BM * kLdsRow;    // bf16 per operand per stage (BM == BN)
 constexpr int kChunks = BM * BK / 8 / kThreads;  // 16-byte chunks per thread per operand per stage
@@ -70,7 +71,8 @@ static_assert(BN % SN == 0, "whole summaries per tile");
 static_assert((BM / kWaveM) * (BN / kWaveN) * 64 == kThreads, "one wave per wave tile");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef f32x4v Acc;  // accumulator of one 16 x 16 block: 4 floats per lane
 
 struct Geo {
   const uint16_t* __restrict__ h;
@@ -146,32 +148,32 @@ __device__ __forceinline__ void store_stage(uint16_t* __restrict__ sa, uint16_t*
   }
 }
 
-// A fragment of a 32-row block for K step kk of a stage: lane l holds row
-// l%32, k = 16 kk + 8 (l/32) .. +7 (the same shape for the vocabulary rows of
-// the B operand).
+// A fragment of a 16-row block for K step kk (32 deep) of a stage: lane l
+// holds row l%16, k = 32 kk + 8 (l/16) .. +7 (the same shape for the
+// vocabulary rows of the B operand).
 __device__ __forceinline__ void load_frags(const uint16_t* __restrict__ sa, const uint16_t* __restrict__ sb, int wm,
                                            int wn, int kk, bf16x8 (&a)[kMB], bf16x8 (&b)[kNB]) {
   const int lane = threadIdx.x & 63;
-  const int fr = lane & 31;
-  const int fk = (lane >> 5) * 8;
+  const int fr = lane & 15;
+  const int fk = (lane >> 4) * 8;
 #pragma unroll
   for (int i = 0; i < kMB; ++i)
-    a[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * kWaveM + i * 32 + fr) * kLdsRow + kk * 16 + fk);
+    a[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * kWaveM + i * 16 + fr) * kLdsRow + kk * 32 + fk);
 #pragma unroll
   for (int j = 0; j < kNB; ++j)
-    b[j] = *reinterpret_cast<const bf16x8*>(sb + (wn * kWaveN + j * 32 + fr) * kLdsRow + kk * 16 + fk);
+    b[j] = *reinterpret_cast<const bf16x8*>(sb + (wn * kWaveN + j * 16 + fr) * kLdsRow + kk * 32 + fk);
 }
 
-__device__ __forceinline__ void mma_step(const bf16x8 (&a)[kMB], const bf16x8 (&b)[kNB], f32x16 (&acc)[kMB][kNB]) {
+__device__ __forceinline__ void mma_step(const bf16x8 (&a)[kMB], const bf16x8 (&b)[kNB], Acc (&acc)[kMB][kNB]) {
 #pragma unroll
   for (int i = 0; i < kMB; ++i)
 #pragma unroll
-    for (int j = 0; j < kNB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < kNB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
 // Logits of one tile, rounded to BF16, into sO [BM][kOutRow]. Accumulator
-// element 4a+b of block (i, j) is row 32i + 8a + 4(l/32) + b, column 32j + l%32
-// of the wave's quarter.
+// element e of block (i, j) is row 16i + 4(l/16) + e, column 16j + l%16 of the
+// wave's part.
 __device__ __forceinline__ void tile_logits(const Geo& g, int64_t row0, int64_t col0, uint16_t* __restrict__ smem,
                                             uint16_t* __restrict__ sO) {
   uint16_t* sa = smem;                  // [2][kStage]
@@ -179,23 +181,23 @@ __device__ __forceinline__ void tile_logits(const Geo& g, int64_t row0, int64_t 
   const int wave = threadIdx.x >> 6;
   const int wm = wave % (BM / kWaveM);
   const int wn = wave / (BM / kWaveM);
-  f32x16 acc[kMB][kNB];
+  Acc acc[kMB][kNB];
 #pragma unroll
   for (int i = 0; i < kMB; ++i)
 #pragma unroll
     for (int j = 0; j < kNB; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
   u32x4 ra[kChunks], rb[kChunks];
   load_stage(g, row0, col0, 0, ra, rb);
   zero_outside(g, row0, col0, ra, rb);
   store_stage(sa, sb, ra, rb);
   __syncthreads();
   const int kt_n = g.d / BK;
-  // Stage kt: its 4 K steps run from LDS buffer kt&1 with the fragments of
-  // step kk+1 loaded while step kk multiplies; stage kt+1's global loads are
-  // issued first and written to the other buffer after step 1 (that buffer
-  // was last read in stage kt-1, before the barrier that ended it).
+  // Stage kt: its 2 K steps run from LDS buffer kt&1, both steps' fragments
+  // loaded before the first multiplies; stage kt+1's global loads are issued
+  // first and written to the other buffer after step 0 (that buffer was last
+  // read in stage kt-1, before the barrier that ended it).
   for (int kt = 0; kt < kt_n; ++kt) {
     const int cur = kt & 1;
     const bool more = kt + 1 < kt_n;
@@ -206,14 +208,10 @@ __device__ __forceinline__ void tile_logits(const Geo& g, int64_t row0, int64_t 
     load_frags(ca, cb, wm, wn, 0, fa0, fb0);
     load_frags(ca, cb, wm, wn, 1, fa1, fb1);
     mma_step(fa0, fb0, acc);
-    load_frags(ca, cb, wm, wn, 2, fa0, fb0);
-    mma_step(fa1, fb1, acc);
     if (more) {
       zero_outside(g, row0, col0, ra, rb);
       store_stage(sa + (cur ^ 1) * kStage, sb + (cur ^ 1) * kStage, ra, rb);
     }
-    load_frags(ca, cb, wm, wn, 3, fa1, fb1);
-    mma_step(fa0, fb0, acc);
     mma_step(fa1, fb1, acc);
     __syncthreads();
   }
@@ -223,14 +221,12 @@ __device__ __forceinline__ void tile_logits(const Geo& g, int64_t row0, int64_t 
 #pragma unroll
     for (int j = 0; j < kNB; ++j)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int r = wm * kWaveM + i * 32 + 8 * a + 4 * (lane >> 5) + b;
-          const int c = wn * kWaveN + j * 32 + (lane & 31);
-          const __bf16 v = static_cast<__bf16>(acc[i][j][4 * a + b]);
-          sO[r * kOutRow + c] = __builtin_bit_cast(uint16_t, v);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int r = wm * kWaveM + i * 16 + 4 * (lane >> 4) + e;
+        const int c = wn * kWaveN + j * 16 + (lane & 15);
+        const __bf16 v = static_cast<__bf16>(acc[i][j][e]);
+        sO[r * kOutRow + c] = __builtin_bit_cast(uint16_t, v);
+      }
   __syncthreads();
 }
 
