@@ -31,7 +31,7 @@
  * Shapes: hidden [n_rows x d_model] (row stride hidden_stride), weight
  * [vocab_real x d_model] (row stride weight_stride; rows >= vocab_real are
  * never read), both BF16 bit patterns, 16-byte aligned, strides multiples of
- * 8; d_model a multiple of 64 in [64, 65536]. layout->row_stride is the row
+ * 8 and at most 2^21; d_model a multiple of 64 in [64, 65536]. layout->row_stride is the row
  * stride of rlk_linear's output (and is only validated by rlk_linear_logp);
  * layout->groups is validated; only the vocabulary-parallel entry points below use it.
  *

@@ -10,15 +10,25 @@
 // Kernels:
 //   k_linear<kLogp>  one 256 x 256 tile of logits per step of a grid-stride
 //                    loop over tiles, in XCD-aware groups of 4 x 8 tiles
-//                    that share operand panels in L2; 8 waves (two per SIMD,
-//                    so one wave's waits overlap the other's matrix work),
-//                    each 128 x 64 as 8 x 4 blocks of v_mfma_f32_16x16x32_bf16.
-//                    K runs in 64-wide stages (two MFMA steps of 32) through
-//                    double-buffered LDS
-//                    (rows padded to 160 bytes: with 144-byte rows the
-//                    16x16x32 fragment reads counted 18% of the CU cycles as
-//                    bank conflicts, with 160 none); the next stage's global
-//                    loads are in flight while the current one is multiplied.
+//                    that share operand panels in L2; 4 waves (one per SIMD),
+//                    each 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16
+//                    (the largest wave tile the 512 registers hold, so the
+//                    fewest LDS reads per multiply-add; the 32 x 32 blocks
+//                    need 8 fragments per K step of 16, which leaves registers
+//                    for a second set in flight and the staged panels).
+//                    K runs in 64-wide stages (four MFMA steps of 16) through
+//                    double-buffered LDS. Panels go from global memory to LDS
+//                    directly (16-byte buffer loads into LDS: no registers,
+//                    no LDS store instructions); the loads' range check
+//                    returns zeros for rows past the operand's end. A load
+//                    instruction fills 1 KB of LDS in lane order, so rows are
+//                    128 bytes with the 16-byte chunks of row r permuted by
+//                    an XOR with swz(r) (no bank conflicts for the fragment
+//                    reads). Each step's multiplies run with the LDS reads of
+//                    the next step's fragments; step 3 also issues the loads
+//                    of the stage after next into the buffer just finished
+//                    with; one barrier per stage, before step 3, after the
+//                    next stage's loads have landed.
 //                    Epilogue: the fp32 accumulators are rounded to BF16 into
 //                    an LDS tile, then either stored (rlk_linear) or reduced
 //                    per row to a 16-byte summary of the tile's 128 columns
@@ -45,14 +55,15 @@ constexpr int BM = 256;                 // rows of a workgroup tile
 constexpr int BN = 256;                 // vocabulary columns of a workgroup tile
 constexpr int BK = 64;                  // K per LDS stage
 constexpr int SN = 128;                 // columns per summary (nests in the canonical shards)
-constexpr int kThreads = 512;           // 8 waves, 2 x 4, each 128 x 64 (two waves per SIMD)
+constexpr int kThreads = 256;           // 4 waves, 2 x 2, each 128 x 128 (one per SIMD)
 constexpr int kWaveM = 128;
-constexpr int kWaveN = 64;
-constexpr int kMB = kWaveM / 16;        // 16 x 16 MFMA blocks per wave
-constexpr int kNB = kWaveN / 16;
-constexpr int kLdsRow = BK + 16;        // bf16 per LDS row: 160 bytes (the 4 stages fill the 160 KB)
+constexpr int kWaveN = 128;
+constexpr int kMB = kWaveM / 32;        // 32 x 32 MFMA blocks per wave
+constexpr int kNB = kWaveN / 32;
+constexpr int kSteps = BK / 16;         // MFMA K steps per stage
+constexpr int kLdsRow = BK;             // bf16 per LDS row: 128 bytes, chunks permuted (swz)
 constexpr int kStage = BM * kLdsRow;    // bf16 per operand per stage (BM == BN)
-constexpr int kChunks = BM * BK / 8 / kThreads;  // 16-byte chunks per thread per operand per stage
+constexpr int kChunks = BM * BK / 8 / kThreads;  // 16-byte loads per thread per operand per stage
 constexpr int kOutRow = BN + 8;         // bf16 per row of the epilogue tile: 528 bytes
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
 // XCD-aware order: workgroup b runs on XCD b % 8; each XCD takes groups of
@@ -63,17 +74,20 @@ constexpr int kXcds = 8;
 constexpr int kGM = 4;
 constexpr int kGN = 8;
 constexpr int64_t kMaxRows = int64_t(1) << 22;
+constexpr int64_t kMaxLd = int64_t(1) << 21;  // row strides: a panel's byte offsets fit 31 bits
 constexpr int64_t kMaxVocab = int64_t(1) << 30;
 constexpr int kMaxD = 65536;
 
 static_assert(BM == BN, "one LDS stage shape for both operands");
-static_assert(BM * kOutRow <= 4 * kStage, "the epilogue tile reuses the stages");
+constexpr int kSmem = (4 * kStage > BM * kOutRow) ? 4 * kStage : BM * kOutRow;  // bf16: stages, or the epilogue tile
 static_assert(BN % SN == 0, "whole summaries per tile");
 static_assert((BM / kWaveM) * (BN / kWaveN) * 64 == kThreads, "one wave per wave tile");
+static_assert(kChunks == 8, "the interleaving below issues 8 panel loads per operand, thread and stage");
+static_assert(kLdsRow == 64 && kThreads == 256, "the load-to-LDS mapping assumes 8 chunks per row, 4 waves");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4v __attribute__((ext_vector_type(4)));
-typedef f32x4v Acc;  // accumulator of one 16 x 16 block: 4 floats per lane
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef f32x16 Acc;  // accumulator of one 32 x 32 block: 16 floats per lane
 
 struct Geo {
   const uint16_t* __restrict__ h;
@@ -106,75 +120,140 @@ __device__ __forceinline__ bool tile_of(const Geo& g, int64_t v, int64_t& m_t, i
   return m_t < g.m_tiles && n_t < g.n_tiles;
 }
 
-// Thread t loads 16-byte chunks t + 256 i of each operand's BM x 64 stage:
-// chunk c is row c/8, columns (c%8)*8 .. +7.
-// Rows past the end load the first row instead and are zeroed afterwards, so
-// the loads need no branches (g.w holds the rows from column col_base on).
-__device__ __forceinline__ void load_stage(const Geo& g, int64_t row0, int64_t col0, int k0, u32x4 (&ra)[kChunks],
-                                           u32x4 (&rb)[kChunks]) {
+// Chunk permutation of the LDS rows: chunk c (8 bf16) of row r sits in slot
+// c ^ swz(r). For the fragment reads (lane l: row l%32 of a 32-row block,
+// chunk 2kk + l/32) the 16 rows read together at one chunk land in 16
+// different 16-byte bank groups, and the rows 0-7 of lanes 0-7 and 32-39 (two
+// neighbouring chunks) in disjoint ones.
+__host__ __device__ __forceinline__ constexpr int swz(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
+
+// The operand panels of a tile as buffer resources: num_records covers the
+// panel's valid rows only, so a load from a row past the operand's end (the
+// ragged last row tile, pad columns of the vocabulary) returns zeros.
+//
+// Load i (0..7) of wave w fills LDS slots q = 64 (8w + i) + l, i.e. row
+// r = 64w + 8i + l/8, slot l%8, with chunk (l%8) ^ swz(r) of that row; swz(r)
+// depends on i only through its parity, so two base offsets serve all eight.
+struct Panels {
+  __amdgpu_buffer_rsrc_t a;
+  __amdgpu_buffer_rsrc_t b;
+  int offa[2];  // byte offsets of this lane's loads 0 and 1 in the A panel
+  int offb[2];
+  int stepa;    // byte offset between loads i and i+2 (16 rows)
+  int stepb;
+};
+
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
+constexpr int kNoLoad = 0x40000000;     // added to an offset: past every num_records, the load fetches nothing
+
+__device__ __forceinline__ Panels make_panels(const Geo& g, int64_t row0, int64_t col0) {
+  Panels p;
+  const int64_t ra = g.n_rows - row0;
+  const int rows_a = static_cast<int>(ra < BM ? ra : BM);
+  p.a = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(g.h + row0 * g.ldh), 0,
+                                          static_cast<int>(rows_a * g.ldh * 2), kRsrcWord3);
+  const int64_t rb = g.w_end - col0;
+  const int rows_b = static_cast<int>(rb <= 0 ? 0 : (rb < BN ? rb : BN));
+  const uint16_t* wb = rows_b > 0 ? g.w + (col0 - g.col_base) * g.ldw : g.w;
+  p.b = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wb), 0, static_cast<int>(rows_b * g.ldw * 2),
+                                          kRsrcWord3);
+  const int l = static_cast<int>(threadIdx.x) & 63;
+  const int w = static_cast<int>(threadIdx.x) >> 6;
 #pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    const int c = static_cast<int>(threadIdx.x) + i * kThreads;
-    const int r = c >> 3;
-    const int kc = (c & 7) * 8;
-    const int64_t gr = row0 + r;
-    const int64_t gc = col0 + r;
-    ra[i] = *reinterpret_cast<const u32x4*>(g.h + (gr < g.n_rows ? gr : 0) * g.ldh + k0 + kc);
-    rb[i] = (g.w_end > g.col_base)
-                ? *reinterpret_cast<const u32x4*>(g.w + (gc < g.w_end ? gc - g.col_base : 0) * g.ldw + k0 + kc)
-                : u32x4{0u, 0u, 0u, 0u};
+  for (int par = 0; par < 2; ++par) {
+    const int r = 64 * w + 8 * par + (l >> 3);
+    const int c = (l & 7) ^ swz(r);
+    p.offa[par] = r * static_cast<int>(g.ldh) * 2 + c * 16;
+    p.offb[par] = r * static_cast<int>(g.ldw) * 2 + c * 16;
   }
+  p.stepa = 16 * static_cast<int>(g.ldh) * 2;
+  p.stepb = 16 * static_cast<int>(g.ldw) * 2;
+  return p;
 }
 
-__device__ __forceinline__ void zero_outside(const Geo& g, int64_t row0, int64_t col0, u32x4 (&ra)[kChunks],
-                                             u32x4 (&rb)[kChunks]) {
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    const int r = (static_cast<int>(threadIdx.x) + i * kThreads) >> 3;
-    ra[i] = (row0 + r < g.n_rows) ? ra[i] : zero;
-    rb[i] = (col0 + r < g.w_end) ? rb[i] : zero;
-  }
+typedef __attribute__((address_space(3))) void* LdsPtr;
+
+// The 8 loads of one operand's BM x 64 stage at byte offset koff (K offset
+// times 2, or kNoLoad) into the LDS stage s.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6); }
+
+__device__ __forceinline__ void load_one(__amdgpu_buffer_rsrc_t r, const int (&off)[2], int step, int koff,
+                                         uint16_t* __restrict__ s, int i) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (LdsPtr)(s + (8 * wave_id() + i) * 512), 16,
+                                           off[i & 1] + (i >> 1) * step + koff, 0, 0, 0);
 }
 
-__device__ __forceinline__ void store_stage(uint16_t* __restrict__ sa, uint16_t* __restrict__ sb,
-                                            u32x4 (&ra)[kChunks], u32x4 (&rb)[kChunks]) {
+__device__ __forceinline__ void load_panel(__amdgpu_buffer_rsrc_t r, const int (&off)[2], int step, int koff,
+                                           uint16_t* __restrict__ s) {
 #pragma unroll
-  for (int i = 0; i < kChunks; ++i) {
-    const int c = static_cast<int>(threadIdx.x) + i * kThreads;
-    const int r = c >> 3;
-    const int kc = (c & 7) * 8;
-    *reinterpret_cast<u32x4*>(sa + r * kLdsRow + kc) = ra[i];
-    *reinterpret_cast<u32x4*>(sb + r * kLdsRow + kc) = rb[i];
-  }
+  for (int i = 0; i < kChunks; ++i) load_one(r, off, step, koff, s, i);
 }
 
-// A fragment of a 16-row block for K step kk (32 deep) of a stage: lane l
-// holds row l%16, k = 32 kk + 8 (l/16) .. +7 (the same shape for the
-// vocabulary rows of the B operand).
+// Waits for this wave's LDS operations and panel loads, then for the whole
+// workgroup. The memory clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Fragments of K step kk (16 deep) of a stage: for the 32-row block i, lane
+// l holds row 32i + l%32, k = 16 kk + 8 (l/32) .. +7, i.e. chunk 2kk + l/32
+// (the same shape for the vocabulary rows of the B operand).
 __device__ __forceinline__ void load_frags(const uint16_t* __restrict__ sa, const uint16_t* __restrict__ sb, int wm,
                                            int wn, int kk, bf16x8 (&a)[kMB], bf16x8 (&b)[kNB]) {
   const int lane = threadIdx.x & 63;
-  const int fr = lane & 15;
-  const int fk = (lane >> 4) * 8;
+  const int fr = lane & 31;
+  const int slot = ((2 * kk + (lane >> 5)) ^ swz(fr)) * 8;
 #pragma unroll
   for (int i = 0; i < kMB; ++i)
-    a[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * kWaveM + i * 16 + fr) * kLdsRow + kk * 32 + fk);
+    a[i] = *reinterpret_cast<const bf16x8*>(sa + (wm * kWaveM + i * 32 + fr) * kLdsRow + slot);
 #pragma unroll
   for (int j = 0; j < kNB; ++j)
-    b[j] = *reinterpret_cast<const bf16x8*>(sb + (wn * kWaveN + j * 16 + fr) * kLdsRow + kk * 32 + fk);
+    b[j] = *reinterpret_cast<const bf16x8*>(sb + (wn * kWaveN + j * 32 + fr) * kLdsRow + slot);
 }
 
-__device__ __forceinline__ void mma_step(const bf16x8 (&a)[kMB], const bf16x8 (&b)[kNB], Acc (&acc)[kMB][kNB]) {
+// One K step by hand: MFMA slot t (block t/4, t%4) is followed by the read
+// of next-step fragment t (t < 8: A blocks 0-3, then B blocks 0-3) and, when
+// the step carries the panel loads, by load t of the next panels (t < 8: the
+// hidden-state panel, then the vocabulary panel). sched_barrier keeps the
+// compiler from regrouping them.
+template <bool kPanel>
+__device__ __forceinline__ void mma_step(const bf16x8 (&a)[kMB], const bf16x8 (&b)[kNB], Acc (&acc)[kMB][kNB],
+                                         const uint16_t* __restrict__ na_src, const uint16_t* __restrict__ nb_src,
+                                         int wm, int wn, int kk, bf16x8 (&na)[kMB], bf16x8 (&nb)[kNB],
+                                         const Panels& p, int koff, uint16_t* __restrict__ la,
+                                         uint16_t* __restrict__ lb) {
+  const int lane = threadIdx.x & 63;
+  const int fr = lane & 31;
+  const int slot = ((2 * kk + (lane >> 5)) ^ swz(fr)) * 8;
 #pragma unroll
-  for (int i = 0; i < kMB; ++i)
-#pragma unroll
-    for (int j = 0; j < kNB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  for (int t = 0; t < kMB * kNB; ++t) {
+    const int i = t / kNB;
+    const int j = t % kNB;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    if (t < kMB)
+      na[t] = *reinterpret_cast<const bf16x8*>(na_src + (wm * kWaveM + t * 32 + fr) * kLdsRow + slot);
+    else if (t < kMB + kNB)
+      nb[t - kMB] = *reinterpret_cast<const bf16x8*>(nb_src + (wn * kWaveN + (t - kMB) * 32 + fr) * kLdsRow + slot);
+    if (kPanel) {
+      if (t < 8)
+        load_one(p.a, p.offa, p.stepa, koff, la, t);
+      else
+        load_one(p.b, p.offb, p.stepb, koff, lb, t - 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Logits of one tile, rounded to BF16, into sO [BM][kOutRow]. Accumulator
-// element e of block (i, j) is row 16i + 4(l/16) + e, column 16j + l%16 of the
-// wave's part.
+// element 4q + e of block (i, j) is row 32i + 8q + 4(l/32) + e, column
+// 32j + l%32 of the wave's part.
+//
+// Stage kt multiplies from LDS buffer kt&1 in 4 steps; the fragments of step
+// s+1 (of step 0 of stage kt+1 during step 3) are read during step s. The
+// barrier before step 3 waits for the loads of stage kt+1 (issued in step 3
+// of stage kt-1) and for every wave's reads of buffer kt&1; step 3 then loads
+// stage kt+2 into that buffer. Past the last stage the loads fetch nothing.
 __device__ __forceinline__ void tile_logits(const Geo& g, int64_t row0, int64_t col0, uint16_t* __restrict__ smem,
                                             uint16_t* __restrict__ sO) {
   uint16_t* sa = smem;                  // [2][kStage]
@@ -188,43 +267,40 @@ __device__ __forceinline__ void tile_logits(const Geo& g, int64_t row0, int64_t 
 #pragma unroll
     for (int j = 0; j < kNB; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
-  u32x4 ra[kChunks], rb[kChunks];
-  load_stage(g, row0, col0, 0, ra, rb);
-  zero_outside(g, row0, col0, ra, rb);
-  store_stage(sa, sb, ra, rb);
-  __syncthreads();
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  const Panels p = make_panels(g, row0, col0);
   const int kt_n = g.d / BK;
-  // Stage kt: its 2 K steps run from LDS buffer kt&1, both steps' fragments
-  // loaded before the first multiplies; stage kt+1's global loads are issued
-  // first and written to the other buffer after step 0 (that buffer was last
-  // read in stage kt-1, before the barrier that ended it).
+  load_panel(p.a, p.offa, p.stepa, 0, sa);
+  load_panel(p.b, p.offb, p.stepb, 0, sb);
+  const int k1 = kt_n > 1 ? BK * 2 : kNoLoad;
+  load_panel(p.a, p.offa, p.stepa, k1, sa + kStage);
+  load_panel(p.b, p.offb, p.stepb, k1, sb + kStage);
+  asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");  // stage 0 landed
+  bf16x8 fa[2][kMB], fb[2][kNB];
+  load_frags(sa, sb, wm, wn, 0, fa[0], fb[0]);
   for (int kt = 0; kt < kt_n; ++kt) {
     const int cur = kt & 1;
-    const bool more = kt + 1 < kt_n;
-    const uint16_t* ca = sa + cur * kStage;
-    const uint16_t* cb = sb + cur * kStage;
-    if (more) load_stage(g, row0, col0, (kt + 1) * BK, ra, rb);
-    bf16x8 fa0[kMB], fb0[kNB], fa1[kMB], fb1[kNB];
-    load_frags(ca, cb, wm, wn, 0, fa0, fb0);
-    load_frags(ca, cb, wm, wn, 1, fa1, fb1);
-    mma_step(fa0, fb0, acc);
-    if (more) {
-      zero_outside(g, row0, col0, ra, rb);
-      store_stage(sa + (cur ^ 1) * kStage, sb + (cur ^ 1) * kStage, ra, rb);
-    }
-    mma_step(fa1, fb1, acc);
-    __syncthreads();
+    uint16_t* ca = sa + cur * kStage;
+    uint16_t* cb = sb + cur * kStage;
+    mma_step<false>(fa[0], fb[0], acc, ca, cb, wm, wn, 1, fa[1], fb[1], p, 0, ca, cb);
+    mma_step<false>(fa[1], fb[1], acc, ca, cb, wm, wn, 2, fa[0], fb[0], p, 0, ca, cb);
+    mma_step<false>(fa[0], fb[0], acc, ca, cb, wm, wn, 3, fa[1], fb[1], p, 0, ca, cb);
+    stage_barrier();
+    const int k2 = kt + 2 < kt_n ? (kt + 2) * BK * 2 : kNoLoad;
+    mma_step<true>(fa[1], fb[1], acc, sa + (cur ^ 1) * kStage, sb + (cur ^ 1) * kStage, wm, wn, 0, fa[0], fb[0], p,
+                   k2, ca, cb);
   }
+  stage_barrier();  // the epilogue tile overwrites the stages (the loads past the end write zeros)
+
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < kMB; ++i)
 #pragma unroll
     for (int j = 0; j < kNB; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = wm * kWaveM + i * 16 + 4 * (lane >> 4) + e;
-        const int c = wn * kWaveN + j * 16 + (lane & 15);
+      for (int e = 0; e < 16; ++e) {
+        const int r = wm * kWaveM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int c = wn * kWaveN + j * 32 + (lane & 31);
         const __bf16 v = static_cast<__bf16>(acc[i][j][e]);
         sO[r * kOutRow + c] = __builtin_bit_cast(uint16_t, v);
       }
@@ -354,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void k_linear(Geo g, const float* __restr
                                                      const int64_t* __restrict__ target,
                                                      ShardSummary* __restrict__ ws, uint16_t* __restrict__ out,
                                                      int64_t ldo) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kStage];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
   uint16_t* sO = smem;  // the epilogue tile reuses the stages
   const int64_t n_virtual = virtual_blocks(g);
   for (int64_t v = blockIdx.x; v < n_virtual; v += gridDim.x) {  // uniform across the workgroup
@@ -467,6 +543,7 @@ static int32_t check_layout(int64_t n_rows, const rlk_vocab_layout* L) {
 static int32_t check_operands(int64_t n_rows, int64_t d, int64_t ldh, int64_t ldw, const rlk_vocab_layout* L) {
   if (d < 64 || d > kMaxD || d % BK != 0) return RLK_ERR_SHAPE;
   if (ldh < d || ldh % 8 != 0 || ldw < d || ldw % 8 != 0) return RLK_ERR_SHAPE;
+  if (ldh > kMaxLd || ldw > kMaxLd) return RLK_ERR_SHAPE;
   if (n_rows > 0 && ldh > INT64_MAX / 2 / n_rows) return RLK_ERR_SHAPE;
   if (ldw > INT64_MAX / 2 / L->vocab_real) return RLK_ERR_SHAPE;
   return RLK_OK;
