@@ -8,8 +8,9 @@
 // float32 temperature scaling, full-vocabulary reference logprob).
 //
 // Kernels:
-//   k_linear<kLogp>  one 256 x 256 tile of logits per step of a grid-stride
-//                    loop over tiles, in XCD-aware groups of 4 x 8 tiles
+//   k_linear<kLogp>  one 256 x 256 tile of logits per step of a loop over
+//                    tiles (one workgroup per compute unit), in XCD-aware
+//                    groups of 4 x 8 tiles
 //                    that share operand panels in L2; 4 waves (one per SIMD),
 //                    each 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16
 //                    (the largest wave tile the 512 registers hold, so the
@@ -24,23 +25,30 @@
 //                    instruction fills 1 KB of LDS in lane order, so rows are
 //                    128 bytes with the 16-byte chunks of row r permuted by
 //                    an XOR with swz(r) (no bank conflicts for the fragment
-//                    reads). Each step's multiplies run with the LDS reads of
-//                    the next step's fragments; step 3 also issues the loads
-//                    of the stage after next into the buffer just finished
-//                    with; one barrier per stage, before step 3, after the
-//                    next stage's loads have landed.
-//                    Epilogue: the fp32 accumulators are rounded to BF16 into
-//                    an LDS tile, then either stored (rlk_linear) or reduced
-//                    per row to a 16-byte summary of the tile's 128 columns
-//                    (rlk_linear_logp) for each 128 columns: integer reference
-//                    exponent r from their exact maximum and l = sum of
-//                    2^(x*c - r) in a fixed order; greedy rows keep the
-//                    maximum and its lowest column.
+//                    reads). Fragments are read two steps ahead (four sets in
+//                    registers), so a stage's buffer is free after step 1:
+//                    one barrier per stage, there, after the next stage's
+//                    loads have landed; steps 2 and 3 then load the stage
+//                    after next into the freed buffer, which spreads the LDS
+//                    writes over half of the stage.
+//                    The MFMA takes the vocabulary fragment first, so a lane
+//                    holds 4 consecutive columns of one row per accumulator
+//                    quad and a row's 128 columns of a wave sit in two lanes.
+//                    Epilogue, from the registers (no LDS, so the next
+//                    tile's first two stages load meanwhile): the fp32
+//                    accumulators rounded to BF16 and either stored
+//                    (rlk_linear) or reduced per row to a 16-byte summary of
+//                    the wave's 128 columns (rlk_linear_logp): integer
+//                    reference exponent r from their exact maximum and l =
+//                    sum of 2^(x*c - r) in a fixed order; greedy rows keep
+//                    the maximum and its lowest column.
 //   k_lin_merge      one wave per row: the row's 128-column summaries merged
 //                    in column order (fp64), then the target's logprob.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "logp_device.hpp"
 #include "rlk_linear.h"
@@ -64,7 +72,6 @@ constexpr int kSteps = BK / 16;         // MFMA K steps per stage
 constexpr int kLdsRow = BK;             // bf16 per LDS row: 128 bytes, chunks permuted (swz)
 constexpr int kStage = BM * kLdsRow;    // bf16 per operand per stage (BM == BN)
 constexpr int kChunks = BM * BK / 8 / kThreads;  // 16-byte loads per thread per operand per stage
-constexpr int kOutRow = BN + 8;         // bf16 per row of the epilogue tile: 528 bytes
 constexpr int64_t kMaxGrid = int64_t(1) << 20;
 // XCD-aware order: workgroup b runs on XCD b % 8; each XCD takes groups of
 // kGM x kGN tiles (one per CU of the XCD), so the 32 workgroups of a group
@@ -79,8 +86,8 @@ constexpr int64_t kMaxVocab = int64_t(1) << 30;
 constexpr int kMaxD = 65536;
 
 static_assert(BM == BN, "one LDS stage shape for both operands");
-constexpr int kSmem = (4 * kStage > BM * kOutRow) ? 4 * kStage : BM * kOutRow;  // bf16: stages, or the epilogue tile
-static_assert(BN % SN == 0, "whole summaries per tile");
+constexpr int kSmem = 4 * kStage;       // bf16: two stages of both operands
+static_assert(SN == kWaveN, "one summary per row of a wave's part");
 static_assert((BM / kWaveM) * (BN / kWaveN) * 64 == kThreads, "one wave per wave tile");
 static_assert(kChunks == 8, "the interleaving below issues 8 panel loads per operand, thread and stage");
 static_assert(kLdsRow == 64 && kThreads == 256, "the load-to-LDS mapping assumes 8 chunks per row, 4 waves");
@@ -213,11 +220,11 @@ __device__ __forceinline__ void load_frags(const uint16_t* __restrict__ sa, cons
 }
 
 // One K step by hand: MFMA slot t (block t/4, t%4) is followed by the read
-// of next-step fragment t (t < 8: A blocks 0-3, then B blocks 0-3) and, when
-// the step carries the panel loads, by load t of the next panels (t < 8: the
-// hidden-state panel, then the vocabulary panel). sched_barrier keeps the
-// compiler from regrouping them.
-template <bool kPanel>
+// of fragment t of the step after next (t < 8: A blocks 0-3, then B blocks
+// 0-3) and, after every other slot, when the step carries panel loads, by one
+// load of the next panels (kPanel 1: the hidden-state panel's 8, 2: the
+// vocabulary panel's). sched_barrier keeps the compiler from regrouping them.
+template <int kPanel>
 __device__ __forceinline__ void mma_step(const bf16x8 (&a)[kMB], const bf16x8 (&b)[kNB], Acc (&acc)[kMB][kNB],
                                          const uint16_t* __restrict__ na_src, const uint16_t* __restrict__ nb_src,
                                          int wm, int wn, int kk, bf16x8 (&na)[kMB], bf16x8 (&nb)[kNB],
@@ -230,193 +237,233 @@ __device__ __forceinline__ void mma_step(const bf16x8 (&a)[kMB], const bf16x8 (&
   for (int t = 0; t < kMB * kNB; ++t) {
     const int i = t / kNB;
     const int j = t % kNB;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
     if (t < kMB)
       na[t] = *reinterpret_cast<const bf16x8*>(na_src + (wm * kWaveM + t * 32 + fr) * kLdsRow + slot);
     else if (t < kMB + kNB)
       nb[t - kMB] = *reinterpret_cast<const bf16x8*>(nb_src + (wn * kWaveN + (t - kMB) * 32 + fr) * kLdsRow + slot);
-    if (kPanel) {
-      if (t < 8)
-        load_one(p.a, p.offa, p.stepa, koff, la, t);
+    if (kPanel && (t & 1) == 0) {
+      if (kPanel == 1)
+        load_one(p.a, p.offa, p.stepa, koff, la, t >> 1);
       else
-        load_one(p.b, p.offb, p.stepb, koff, lb, t - 8);
+        load_one(p.b, p.offb, p.stepb, koff, lb, t >> 1);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Logits of one tile, rounded to BF16, into sO [BM][kOutRow]. Accumulator
-// element 4q + e of block (i, j) is row 32i + 8q + 4(l/32) + e, column
-// 32j + l%32 of the wave's part.
+// Panels of stages 0 and 1 of a tile into LDS buffers 0 and 1.
+__device__ __forceinline__ void prefetch_tile(const Panels& p, int kt_n, uint16_t* __restrict__ smem) {
+  load_panel(p.a, p.offa, p.stepa, 0, smem);
+  load_panel(p.b, p.offb, p.stepb, 0, smem + 2 * kStage);
+  const int k1 = kt_n > 1 ? BK * 2 : kNoLoad;
+  load_panel(p.a, p.offa, p.stepa, k1, smem + kStage);
+  load_panel(p.b, p.offb, p.stepb, k1, smem + 3 * kStage);
+}
+
+// Logits of one tile (fp32) into acc; stages 0 and 1 were loaded by
+// prefetch_tile. The MFMA takes the vocabulary fragment as its first operand,
+// so block (i, j) holds the transposed product: element 4q + e of lane l is
+// row 32i + l%32, column 32j + 8q + 4(l/32) + e of the wave's part.
 //
 // Stage kt multiplies from LDS buffer kt&1 in 4 steps; the fragments of step
-// s+1 (of step 0 of stage kt+1 during step 3) are read during step s. The
-// barrier before step 3 waits for the loads of stage kt+1 (issued in step 3
-// of stage kt-1) and for every wave's reads of buffer kt&1; step 3 then loads
-// stage kt+2 into that buffer. Past the last stage the loads fetch nothing.
-__device__ __forceinline__ void tile_logits(const Geo& g, int64_t row0, int64_t col0, uint16_t* __restrict__ smem,
-                                            uint16_t* __restrict__ sO) {
+// s+2 (of steps 0 and 1 of stage kt+1 during steps 2 and 3) are read during
+// step s. The barrier after step 1 waits for the loads of stage kt+1 (issued
+// in steps 2 and 3 of stage kt-1) and for every wave's reads of buffer kt&1;
+// steps 2 and 3 then load stage kt+2 into that buffer. Past the last stage
+// the loads fetch nothing. On return every wave is done with the LDS.
+__device__ __forceinline__ void tile_logits(const Geo& g, const Panels& p, uint16_t* __restrict__ smem,
+                                            Acc (&acc)[kMB][kNB]) {
   uint16_t* sa = smem;                  // [2][kStage]
   uint16_t* sb = smem + 2 * kStage;     // [2][kStage]
   const int wave = threadIdx.x >> 6;
   const int wm = wave % (BM / kWaveM);
   const int wn = wave / (BM / kWaveM);
-  Acc acc[kMB][kNB];
 #pragma unroll
   for (int i = 0; i < kMB; ++i)
 #pragma unroll
     for (int j = 0; j < kNB; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  const Panels p = make_panels(g, row0, col0);
   const int kt_n = g.d / BK;
-  load_panel(p.a, p.offa, p.stepa, 0, sa);
-  load_panel(p.b, p.offb, p.stepb, 0, sb);
-  const int k1 = kt_n > 1 ? BK * 2 : kNoLoad;
-  load_panel(p.a, p.offa, p.stepa, k1, sa + kStage);
-  load_panel(p.b, p.offb, p.stepb, k1, sb + kStage);
-  asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");  // stage 0 landed
-  bf16x8 fa[2][kMB], fb[2][kNB];
+  // stage 0 landed: all but the last 16 panel loads (stage 1) are done
+  asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  bf16x8 fa[kSteps][kMB], fb[kSteps][kNB];
   load_frags(sa, sb, wm, wn, 0, fa[0], fb[0]);
+  load_frags(sa, sb, wm, wn, 1, fa[1], fb[1]);
   for (int kt = 0; kt < kt_n; ++kt) {
     const int cur = kt & 1;
     uint16_t* ca = sa + cur * kStage;
     uint16_t* cb = sb + cur * kStage;
-    mma_step<false>(fa[0], fb[0], acc, ca, cb, wm, wn, 1, fa[1], fb[1], p, 0, ca, cb);
-    mma_step<false>(fa[1], fb[1], acc, ca, cb, wm, wn, 2, fa[0], fb[0], p, 0, ca, cb);
-    mma_step<false>(fa[0], fb[0], acc, ca, cb, wm, wn, 3, fa[1], fb[1], p, 0, ca, cb);
+    uint16_t* na = sa + (cur ^ 1) * kStage;
+    uint16_t* nb = sb + (cur ^ 1) * kStage;
+    mma_step<0>(fa[0], fb[0], acc, ca, cb, wm, wn, 2, fa[2], fb[2], p, 0, ca, cb);
+    mma_step<0>(fa[1], fb[1], acc, ca, cb, wm, wn, 3, fa[3], fb[3], p, 0, ca, cb);
     stage_barrier();
     const int k2 = kt + 2 < kt_n ? (kt + 2) * BK * 2 : kNoLoad;
-    mma_step<true>(fa[1], fb[1], acc, sa + (cur ^ 1) * kStage, sb + (cur ^ 1) * kStage, wm, wn, 0, fa[0], fb[0], p,
-                   k2, ca, cb);
+    mma_step<1>(fa[2], fb[2], acc, na, nb, wm, wn, 0, fa[0], fb[0], p, k2, ca, cb);
+    mma_step<2>(fa[3], fb[3], acc, na, nb, wm, wn, 1, fa[1], fb[1], p, k2, ca, cb);
   }
-  stage_barrier();  // the epilogue tile overwrites the stages (the loads past the end write zeros)
-
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < kMB; ++i)
-#pragma unroll
-    for (int j = 0; j < kNB; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = wm * kWaveM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int c = wn * kWaveN + j * 32 + (lane & 31);
-        const __bf16 v = static_cast<__bf16>(acc[i][j][e]);
-        sO[r * kOutRow + c] = __builtin_bit_cast(uint16_t, v);
-      }
-  __syncthreads();
+  stage_barrier();
 }
 
-// Summary of columns [q*SN, (q+1)*SN) of row r of the tile; two neighbouring
-// threads share an item, 64 columns each.
-__device__ __forceinline__ void row_summary(const Geo& g, int64_t row0, int64_t tcol0, int r, int q,
-                                            const uint16_t* __restrict__ sO, const float* __restrict__ temperature,
-                                            const int64_t* __restrict__ target, ShardSummary* __restrict__ ws) {
-  const int half = threadIdx.x & 1;
-  const int64_t col0 = tcol0 + q * SN;
-  const int64_t n_t = (col0 - g.col_base) / SN;  // summary index in this launch
-  const int64_t gr = row0 + r;
-  const bool row_ok = gr < g.n_rows;
-  const float t = row_ok ? temperature[gr] : 1.0f;
-  const int64_t tg = row_ok ? target[gr] : -1;
-  const int64_t cb = col0 + half * 64;
-  int64_t nv64 = g.w_end - cb;
-  const int nvalid = static_cast<int>(nv64 < 0 ? 0 : (nv64 > 64 ? 64 : nv64));
-  const uint16_t* src = sO + r * kOutRow + q * SN + half * 64;
-  // pass 1: maximum (and, for greedy rows, NaN/+inf and the first maximum)
-  float m = -INFINITY;
-  bool bad = false;
-#pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(src + v * 8);
-    float x[8];
-    rlk::unpack8(q, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bool ok = v * 8 + e < nvalid;
-      bad |= ok && ((x[e] != x[e]) || (x[e] == INFINITY));
-      m = ok ? fmaxf(m, x[e]) : m;
-    }
-  }
-  m = fmaxf(m, __shfl_xor(m, 1));
-  bad = bad || (__shfl_xor(static_cast<int>(bad), 1) != 0);
-  ShardSummary s;
-  s.r = 0.0f;
-  s.l = 0.0f;
-  s.m = m;
-  s.aux = -1;
-  if (!rlk::temperature_valid(t)) {
-    s.l = NAN;
-  } else if (t == 0.0f) {
-    int first = INT32_MAX;
-    for (int j = 0; j < nvalid; ++j) {
-      const float x = __uint_as_float(static_cast<uint32_t>(src[j]) << 16);
-      if (x == m) {
-        first = static_cast<int>(cb) + j;
-        break;
-      }
-    }
-    const int other = __shfl_xor(first, 1);
-    first = other < first ? other : first;
-    s.l = bad ? NAN : 0.0f;
-    s.aux = (first == INT32_MAX) ? -1 : first;
-  } else {
-    const float c = rlk::kLog2e / t;
-    const float rr = rlk::ref_exponent(m, c);
-    float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const u32x4 q = *reinterpret_cast<const u32x4*>(src + v * 8);
-      float x[8];
-      rlk::unpack8(q, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float term = __builtin_amdgcn_exp2f(fmaf(x[e], c, -rr));
-        a4[e & 3] += (v * 8 + e < nvalid) ? term : 0.0f;
-      }
-    }
-    const float mine = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-    const float other = __shfl_xor(mine, 1);
-    s.r = rr;
-    s.l = half == 0 ? mine + other : other + mine;
-    if (tg >= col0 && tg < col0 + SN && tg < g.vocab_real)
-      s.aux = static_cast<int32_t>(sO[r * kOutRow + q * SN + static_cast<int>(tg - col0)]);
-  }
-  if (row_ok && half == 0) ws[gr * g.n_sum + n_t] = s;
+// BF16 bits of an fp32 value, rounded to nearest even, as a float.
+__device__ __forceinline__ float round_bf16(float v) {
+  const __bf16 b = static_cast<__bf16>(v);
+  return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
-__device__ __forceinline__ void tile_summaries(const Geo& g, int64_t row0, int64_t col0,
-                                               const uint16_t* __restrict__ sO, const float* __restrict__ temperature,
-                                               const int64_t* __restrict__ target, ShardSummary* __restrict__ ws) {
-  // (BM rows) x (BN / SN summaries) items, two threads each
-  for (int item = threadIdx.x >> 1; item < BM * (BN / SN); item += kThreads / 2) {
-    const int r = item % BM;
-    const int q = item / BM;
-    if (col0 + q * SN < g.col_end) row_summary(g, row0, col0, r, q, sO, temperature, target, ws);
-  }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const __bf16 a = static_cast<__bf16>(lo);
+  const __bf16 b = static_cast<__bf16>(hi);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
-// Stores the BF16 tile; real columns from the tile, pads -inf.
-__device__ __forceinline__ void tile_store(const Geo& g, int64_t row0, int64_t col0, const uint16_t* __restrict__ sO,
+// 8 BF16 logits (4 packed pairs) at column c of a row; pad columns -inf.
+__device__ __forceinline__ void store8(const Geo& g, uint16_t* __restrict__ dst, int64_t c, uint32_t w0, uint32_t w1,
+                                      uint32_t w2, uint32_t w3) {
+  if (c + 8 > g.vocab_real) {
+    const uint32_t w[4] = {w0, w1, w2, w3};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = (c + 2 * k < g.vocab_real) ? (w[k] & 0xFFFFu) : 0xFF80u;
+      const uint32_t hi = (c + 2 * k + 1 < g.vocab_real) ? (w[k] & 0xFFFF0000u) : 0xFF800000u;
+      o[k] = lo | hi;
+    }
+    w0 = o[0];
+    w1 = o[1];
+    w2 = o[2];
+    w3 = o[3];
+  }
+  // an ordinary store: L2 merges the 16-byte pieces of a row into whole lines
+  // (with the non-temporal hint they reach HBM as partial lines, 15% slower)
+  *reinterpret_cast<u32x4*>(dst) = u32x4{w0, w1, w2, w3};
+}
+
+// Stores the tile's BF16 logits from the accumulators; pads -inf. Lane l
+// holds, for q = 0..3, columns 8q + 4h .. +3 (h = l/32) of row l%32 of block
+// (i, j); one exchange with lane l^32 gives lane l the 16 columns 16h .. +15,
+// stored as two 16-byte pieces.
+__device__ __forceinline__ void tile_store(const Geo& g, int64_t row0, int64_t col0, const Acc (&acc)[kMB][kNB],
                                            uint16_t* __restrict__ out, int64_t ldo) {
-  for (int c = threadIdx.x; c < BM * (BN / 8); c += kThreads) {
-    const int r = c / (BN / 8);
-    const int ch = c % (BN / 8);
-    const int64_t gr = row0 + r;
-    const int64_t gc = col0 + ch * 8;
-    if (gr >= g.n_rows || gc >= g.vocab_padded) continue;
-    u32x4 v = *reinterpret_cast<const u32x4*>(sO + r * kOutRow + ch * 8);
-    if (gc + 8 > g.vocab_real) {
-      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave % (BM / kWaveM);
+  const int wn = wave / (BM / kWaveM);
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const uint32_t lo = (gc + 2 * h < g.vocab_real) ? (w[h] & 0xFFFFu) : 0xFF80u;
-        const uint32_t hi = (gc + 2 * h + 1 < g.vocab_real) ? (w[h] & 0xFFFF0000u) : 0xFF800000u;
-        w[h] = lo | hi;
-      }
-      v = u32x4{w[0], w[1], w[2], w[3]};
+  for (int i = 0; i < kMB; ++i) {
+    const int64_t gr = row0 + wm * kWaveM + i * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) {
+      const Acc& v = acc[i][j];
+      // columns 8q + 4h + (0, 1) and (2, 3) of this lane, q = 0..3
+      const uint32_t p00 = pack_bf16(v[0], v[1]), p01 = pack_bf16(v[2], v[3]);
+      const uint32_t p10 = pack_bf16(v[4], v[5]), p11 = pack_bf16(v[6], v[7]);
+      const uint32_t p20 = pack_bf16(v[8], v[9]), p21 = pack_bf16(v[10], v[11]);
+      const uint32_t p30 = pack_bf16(v[12], v[13]), p31 = pack_bf16(v[14], v[15]);
+      // h = 0 keeps q = 0, 1 and takes the partner's; h = 1 keeps q = 2, 3
+      const uint32_t g00 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(h ? p00 : p20), 32));
+      const uint32_t g01 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(h ? p01 : p21), 32));
+      const uint32_t g10 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(h ? p10 : p30), 32));
+      const uint32_t g11 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(h ? p11 : p31), 32));
+      const int64_t gc = col0 + wn * kWaveN + j * 32 + 16 * h;
+      if (gr >= g.n_rows || gc >= g.vocab_padded) continue;
+      const uint32_t a0 = h ? p20 : p00, a1 = h ? p21 : p01;
+      const uint32_t b0 = h ? p30 : p10, b1 = h ? p31 : p11;
+      store8(g, out + gr * ldo + gc, gc, h ? g00 : a0, h ? g01 : a1, h ? a0 : g00, h ? a1 : g01);
+      store8(g, out + gr * ldo + gc + 8, gc + 8, h ? g10 : b0, h ? g11 : b1, h ? b0 : g10, h ? b1 : g11);
     }
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + gr * ldo + gc));
+  }
+}
+
+// Per-row summaries of the wave's 128 columns from the accumulators: lane l
+// holds 64 of a row's columns (32j + 8q + 4h + e, h = l/32), lane l^32 the
+// other 64. Each lane reduces its columns in the order (j, q, e) (the sum in
+// four partial sums, k mod 4), then the two halves combine, the h = 0 half
+// first. Integer reference exponent r from the exact row maximum; greedy rows
+// keep the maximum and its lowest column; the target's BF16 bits when the
+// target is one of the columns.
+__device__ __forceinline__ void tile_summaries(const Geo& g, int64_t row0, int64_t col0, const Acc (&acc)[kMB][kNB],
+                                               const float (&tr)[kMB], const int64_t (&tgr)[kMB],
+                                               ShardSummary* __restrict__ ws) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave % (BM / kWaveM);
+  const int wn = wave / (BM / kWaveM);
+  const int64_t cb = col0 + wn * kWaveN;  // first column of the summary
+  if (cb >= g.col_end) return;            // uniform across the wave
+  const int64_t n_t = (cb - g.col_base) / SN;
+  int64_t lim64 = g.w_end - cb - 4 * h;   // this lane's column 32j + 8q + e is real iff below lim
+  const int lim = static_cast<int>(lim64 < 0 ? 0 : (lim64 > 128 ? 128 : lim64));
+  const bool all_real = cb + kWaveN <= g.w_end;  // uniform across the wave
+#pragma unroll
+  for (int i = 0; i < kMB; ++i) {
+    const int64_t gr = row0 + wm * kWaveM + i * 32 + (lane & 31);
+    const float t = tr[i];
+    const int64_t tg = tgr[i];
+    float m = -INFINITY;
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < 64; ++k) {
+      const int j = k >> 4, q = (k >> 2) & 3, e = k & 3;
+      const float x = round_bf16(acc[i][j][4 * q + e]);
+      const bool ok = all_real || (32 * j + 8 * q + e < lim);
+      bad |= ok && ((x != x) || (x == INFINITY));
+      m = ok ? fmaxf(m, x) : m;
+    }
+    m = fmaxf(m, __shfl_xor(m, 32));
+    bad = bad || (__shfl_xor(static_cast<int>(bad), 32) != 0);
+    ShardSummary s;
+    s.r = 0.0f;
+    s.l = 0.0f;
+    s.m = m;
+    s.aux = -1;
+    if (!rlk::temperature_valid(t)) {
+      s.l = NAN;
+    } else if (t == 0.0f) {
+      int first = INT32_MAX;
+#pragma unroll
+      for (int k = 63; k >= 0; --k) {
+        const int j = k >> 4, q = (k >> 2) & 3, e = k & 3;
+        const float x = round_bf16(acc[i][j][4 * q + e]);
+        const bool ok = all_real || (32 * j + 8 * q + e < lim);
+        first = (ok && x == m) ? static_cast<int>(cb) + 32 * j + 8 * q + 4 * h + e : first;
+      }
+      const int other = __shfl_xor(first, 32);
+      first = other < first ? other : first;
+      s.l = bad ? NAN : 0.0f;
+      s.aux = (first == INT32_MAX) ? -1 : first;
+    } else {
+      const float c = rlk::kLog2e / t;
+      const float rr = rlk::ref_exponent(m, c);
+      // the target's position among this lane's columns, or -1
+      const int64_t lc = tg - cb;
+      const bool tin = (lc >= 0) && (lc < SN) && (tg < g.vocab_real);
+      const int lci = static_cast<int>(tin ? lc : 0);
+      const int kt = (tin && ((lci >> 2) & 1) == h) ? (lci >> 5) * 16 + ((lci >> 3) & 3) * 4 + (lci & 3) : -1;
+      float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      int tbits = -1;
+#pragma unroll
+      for (int k = 0; k < 64; ++k) {
+        const int j = k >> 4, q = (k >> 2) & 3, e = k & 3;
+        const float x = round_bf16(acc[i][j][4 * q + e]);
+        const bool ok = all_real || (32 * j + 8 * q + e < lim);
+        const float term = __builtin_amdgcn_exp2f(fmaf(x, c, -rr));
+        a4[k & 3] += ok ? term : 0.0f;
+        tbits = (k == kt) ? static_cast<int>(__float_as_uint(x) >> 16) : tbits;
+      }
+      const float mine = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+      const float other = __shfl_xor(mine, 32);
+      s.r = rr;
+      s.l = h == 0 ? mine + other : other + mine;
+      const int otb = __shfl_xor(tbits, 32);
+      s.aux = tin ? (tbits >= 0 ? tbits : otb) : -1;
+    }
+    if (gr < g.n_rows && h == 0) ws[gr * g.n_sum + n_t] = s;
   }
 }
 
@@ -425,25 +472,59 @@ __host__ __device__ __forceinline__ int64_t virtual_blocks(const Geo& g) {
   return ((groups + kXcds - 1) / kXcds) * kXcds * kGM * kGN;
 }
 
+// First tile at or after virtual workgroup v (stepping by the grid), or false.
+__device__ __forceinline__ bool next_tile(const Geo& g, int64_t n_virtual, int64_t& v, int64_t& m_t, int64_t& n_t) {
+  while (v < n_virtual) {
+    if (tile_of(g, v, m_t, n_t)) return true;
+    v += gridDim.x;
+  }
+  return false;
+}
+
 template <bool kLogp>
 __global__ __launch_bounds__(kThreads) void k_linear(Geo g, const float* __restrict__ temperature,
                                                      const int64_t* __restrict__ target,
                                                      ShardSummary* __restrict__ ws, uint16_t* __restrict__ out,
                                                      int64_t ldo) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
-  uint16_t* sO = smem;  // the epilogue tile reuses the stages
   const int64_t n_virtual = virtual_blocks(g);
-  for (int64_t v = blockIdx.x; v < n_virtual; v += gridDim.x) {  // uniform across the workgroup
-    int64_t m_t, n_t;
-    if (!tile_of(g, v, m_t, n_t)) continue;
+  const int kt_n = g.d / BK;
+  int64_t v = blockIdx.x, m_t = 0, n_t = 0;
+  if (!next_tile(g, n_virtual, v, m_t, n_t)) return;  // uniform across the workgroup
+  Panels p = make_panels(g, m_t * BM, g.col_base + n_t * BN);
+  prefetch_tile(p, kt_n, smem);
+  const int lane = threadIdx.x & 63;
+  const int wm = (threadIdx.x >> 6) % (BM / kWaveM);
+  while (true) {
     const int64_t row0 = m_t * BM;
     const int64_t col0 = g.col_base + n_t * BN;
-    tile_logits(g, row0, col0, smem, sO);
+    float tr[kMB];
+    int64_t tgr[kMB];
+    if (kLogp) {
+#pragma unroll
+      for (int i = 0; i < kMB; ++i) {
+        const int64_t gr = row0 + wm * kWaveM + i * 32 + (lane & 31);
+        tr[i] = gr < g.n_rows ? temperature[gr] : 1.0f;
+        tgr[i] = gr < g.n_rows ? target[gr] : -1;
+      }
+    }
+    Acc acc[kMB][kNB];
+    tile_logits(g, p, smem, acc);
+    // the next tile's first stages load while this tile's results are written
+    int64_t v2 = v + gridDim.x, m2 = 0, n2 = 0;
+    const bool more = next_tile(g, n_virtual, v2, m2, n2);
+    if (more) {
+      p = make_panels(g, m2 * BM, g.col_base + n2 * BN);
+      prefetch_tile(p, kt_n, smem);
+    }
     if (kLogp)
-      tile_summaries(g, row0, col0, sO, temperature, target, ws);
+      tile_summaries(g, row0, col0, acc, tr, tgr, ws);
     else
-      tile_store(g, row0, col0, sO, out, ldo);
-    __syncthreads();  // sO is overwritten by the next tile's first stage
+      tile_store(g, row0, col0, acc, out, ldo);
+    if (!more) break;
+    v = v2;
+    m_t = m2;
+    n_t = n2;
   }
 }
 
@@ -571,9 +652,30 @@ static Geo make_geo(const uint16_t* h, int64_t n_rows, int64_t d, int64_t ldh, c
   return g;
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+static int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// One workgroup per compute unit (a workgroup's LDS fills one), each looping
+// over its tiles: no workgroup launches between tiles. Workgroup b stays on
+// XCD b % 8, so its tiles v = b + k * grid keep the XCD of the tile order.
 static unsigned grid_for(const Geo& g) {
   const int64_t v = virtual_blocks(g);
-  return static_cast<unsigned>(v < kMaxGrid ? v : kMaxGrid);
+  int64_t cap = cu_count();
+  cap = cap > 0 ? (cap + kXcds - 1) / kXcds * kXcds : kMaxGrid;
+  if (cap > kMaxGrid) cap = kMaxGrid;
+  return static_cast<unsigned>(v < cap ? v : cap);
 }
 
 }  // namespace rlk_lin
