@@ -175,6 +175,10 @@ __device__ __forceinline__ Panels make_panels(const Geo& g, int64_t row0, int64_
   }
   p.stepa = 16 * static_cast<int>(g.ldh) * 2;
   p.stepb = 16 * static_cast<int>(g.ldw) * 2;
+  // The offsets do not depend on the tile; without this the compiler hoists
+  // the 32 per-load offsets out of the loop over tiles, spills them, and each
+  // reload then waits behind the panel loads already in flight.
+  asm volatile("" : "+v"(p.offa[0]), "+v"(p.offa[1]), "+v"(p.offb[0]), "+v"(p.offb[1]));
   return p;
 }
 
