@@ -389,7 +389,9 @@ __device__ __forceinline__ void tile_store(const Geo& g, int64_t row0, int64_t c
 // four partial sums, k mod 4), then the two halves combine, the h = 0 half
 // first. Integer reference exponent r from the exact row maximum; greedy rows
 // keep the maximum and its lowest column; the target's BF16 bits when the
-// target is one of the columns.
+// target is one of the columns. The rare cases (a target among the columns,
+// a greedy row) run behind branches that are uniform across the wave, so the
+// common path stays short.
 __device__ __forceinline__ void tile_summaries(const Geo& g, int64_t row0, int64_t col0, const Acc (&acc)[kMB][kNB],
                                                const float (&tr)[kMB], const int64_t (&tgr)[kMB],
                                                ShardSummary* __restrict__ ws) {
@@ -409,63 +411,71 @@ __device__ __forceinline__ void tile_summaries(const Geo& g, int64_t row0, int64
     const int64_t gr = row0 + wm * kWaveM + i * 32 + (lane & 31);
     const float t = tr[i];
     const int64_t tg = tgr[i];
-    float m = -INFINITY;
-    bool bad = false;
+    float x[64];
 #pragma unroll
-    for (int k = 0; k < 64; ++k) {
-      const int j = k >> 4, q = (k >> 2) & 3, e = k & 3;
-      const float x = round_bf16(acc[i][j][4 * q + e]);
-      const bool ok = all_real || (32 * j + 8 * q + e < lim);
-      bad |= ok && ((x != x) || (x == INFINITY));
-      m = ok ? fmaxf(m, x) : m;
+    for (int k = 0; k < 64; ++k) x[k] = round_bf16(acc[i][k >> 4][k & 15]);
+    if (!all_real) {
+      // columns past the real vocabulary: -inf (they follow every real column of the lane)
+#pragma unroll
+      for (int k = 0; k < 64; ++k) x[k] = (32 * (k >> 4) + 8 * ((k >> 2) & 3) + (k & 3) < lim) ? x[k] : -INFINITY;
     }
-    m = fmaxf(m, __shfl_xor(m, 32));
-    bad = bad || (__shfl_xor(static_cast<int>(bad), 32) != 0);
+    float mx[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) mx[u] = fmaxf(fmaxf(x[4 * u], x[4 * u + 1]), fmaxf(x[4 * u + 2], x[4 * u + 3]));
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int u = 0; u < w; ++u) mx[u] = fmaxf(mx[u], mx[u + w]);
+    const float m = fmaxf(mx[0], __shfl_xor(mx[0], 32));
     ShardSummary s;
-    s.r = 0.0f;
-    s.l = 0.0f;
     s.m = m;
     s.aux = -1;
-    if (!rlk::temperature_valid(t)) {
-      s.l = NAN;
-    } else if (t == 0.0f) {
+    // positive temperature
+    const float c = rlk::kLog2e / t;
+    const float rr = rlk::ref_exponent(m, c);
+    float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < 64; ++k) a4[k & 3] += __builtin_amdgcn_exp2f(fmaf(x[k], c, -rr));
+    const float mine = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+    const float other = __shfl_xor(mine, 32);
+    s.r = rr;
+    s.l = h == 0 ? mine + other : other + mine;
+    const int64_t lc = tg - cb;
+    const bool tin = (lc >= 0) && (lc < SN) && (tg < g.vocab_real);
+    if (__any(tin)) {
+      const int lci = static_cast<int>(tin ? lc : 0);
+      const int kt = (tin && ((lci >> 2) & 1) == h) ? (lci >> 5) * 16 + ((lci >> 3) & 3) * 4 + (lci & 3) : -1;
+      int tbits = -1;
+#pragma unroll
+      for (int k = 0; k < 64; ++k) tbits = (k == kt) ? static_cast<int>(__float_as_uint(x[k]) >> 16) : tbits;
+      const int otb = __shfl_xor(tbits, 32);
+      s.aux = tin ? (tbits >= 0 ? tbits : otb) : -1;
+    }
+    const bool greedy = (t == 0.0f);
+    if (__any(greedy)) {
+      // first column holding the maximum, and NaN or +inf among the real columns
+      bool bad = false;
       int first = INT32_MAX;
 #pragma unroll
       for (int k = 63; k >= 0; --k) {
-        const int j = k >> 4, q = (k >> 2) & 3, e = k & 3;
-        const float x = round_bf16(acc[i][j][4 * q + e]);
-        const bool ok = all_real || (32 * j + 8 * q + e < lim);
-        first = (ok && x == m) ? static_cast<int>(cb) + 32 * j + 8 * q + 4 * h + e : first;
+        const int cl = 32 * (k >> 4) + 8 * ((k >> 2) & 3) + (k & 3);
+        const bool ok = cl < lim;
+        bad |= ok && ((x[k] != x[k]) || (x[k] == INFINITY));
+        first = (ok && x[k] == m) ? static_cast<int>(cb) + cl + 4 * h : first;
       }
-      const int other = __shfl_xor(first, 32);
-      first = other < first ? other : first;
-      s.l = bad ? NAN : 0.0f;
-      s.aux = (first == INT32_MAX) ? -1 : first;
-    } else {
-      const float c = rlk::kLog2e / t;
-      const float rr = rlk::ref_exponent(m, c);
-      // the target's position among this lane's columns, or -1
-      const int64_t lc = tg - cb;
-      const bool tin = (lc >= 0) && (lc < SN) && (tg < g.vocab_real);
-      const int lci = static_cast<int>(tin ? lc : 0);
-      const int kt = (tin && ((lci >> 2) & 1) == h) ? (lci >> 5) * 16 + ((lci >> 3) & 3) * 4 + (lci & 3) : -1;
-      float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      int tbits = -1;
-#pragma unroll
-      for (int k = 0; k < 64; ++k) {
-        const int j = k >> 4, q = (k >> 2) & 3, e = k & 3;
-        const float x = round_bf16(acc[i][j][4 * q + e]);
-        const bool ok = all_real || (32 * j + 8 * q + e < lim);
-        const float term = __builtin_amdgcn_exp2f(fmaf(x, c, -rr));
-        a4[k & 3] += ok ? term : 0.0f;
-        tbits = (k == kt) ? static_cast<int>(__float_as_uint(x) >> 16) : tbits;
+      bad = bad || (__shfl_xor(static_cast<int>(bad), 32) != 0);
+      const int ofirst = __shfl_xor(first, 32);
+      first = ofirst < first ? ofirst : first;
+      if (greedy) {
+        s.r = 0.0f;
+        s.l = bad ? NAN : 0.0f;
+        s.aux = (first == INT32_MAX) ? -1 : first;
       }
-      const float mine = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-      const float other = __shfl_xor(mine, 32);
-      s.r = rr;
-      s.l = h == 0 ? mine + other : other + mine;
-      const int otb = __shfl_xor(tbits, 32);
-      s.aux = tin ? (tbits >= 0 ? tbits : otb) : -1;
+    }
+    if (!rlk::temperature_valid(t)) {
+      s.r = 0.0f;
+      s.l = NAN;
+      s.aux = -1;
     }
     if (gr < g.n_rows && h == 0) ws[gr * g.n_sum + n_t] = s;
   }
