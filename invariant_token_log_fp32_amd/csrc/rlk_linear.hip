@@ -256,28 +256,35 @@ __device__ __forceinline__ void mma_step(const bf16x8 (&a)[kMB], const bf16x8 (&
   }
 }
 
-// Panels of stages 0 and 1 of a tile into LDS buffers 0 and 1.
-__device__ __forceinline__ void prefetch_tile(const Panels& p, int kt_n, uint16_t* __restrict__ smem) {
-  load_panel(p.a, p.offa, p.stepa, 0, smem);
-  load_panel(p.b, p.offb, p.stepb, 0, smem + 2 * kStage);
+// Panels of stages 0 and 1 of a tile into LDS buffers par and par ^ 1
+// (stage 1 only when the tile has it).
+__device__ __forceinline__ void prefetch_tile(const Panels& p, int kt_n, int par, uint16_t* __restrict__ smem) {
+  load_panel(p.a, p.offa, p.stepa, 0, smem + par * kStage);
+  load_panel(p.b, p.offb, p.stepb, 0, smem + (2 + par) * kStage);
   const int k1 = kt_n > 1 ? BK * 2 : kNoLoad;
-  load_panel(p.a, p.offa, p.stepa, k1, smem + kStage);
-  load_panel(p.b, p.offb, p.stepb, k1, smem + 3 * kStage);
+  load_panel(p.a, p.offa, p.stepa, k1, smem + (par ^ 1) * kStage);
+  load_panel(p.b, p.offb, p.stepb, k1, smem + (2 + (par ^ 1)) * kStage);
 }
 
-// Logits of one tile (fp32) into acc; stages 0 and 1 were loaded by
-// prefetch_tile. The MFMA takes the vocabulary fragment as its first operand,
-// so block (i, j) holds the transposed product: element 4q + e of lane l is
-// row 32i + l%32, column 32j + 8q + 4(l/32) + e of the wave's part.
+// Logits of one tile (fp32) into acc. The tile's stage kt lives in LDS
+// buffer (kt + par) & 1; on entry stages 0 and 1 are loaded or in flight and
+// the fragments of steps 0 and 1 of stage 0 are in fa[0..1], fb[0..1]. The
+// MFMA takes the vocabulary fragment as its first operand, so block (i, j)
+// holds the transposed product: element 4q + e of lane l is row 32i + l%32,
+// column 32j + 8q + 4(l/32) + e of the wave's part.
 //
-// Stage kt multiplies from LDS buffer kt&1 in 4 steps; the fragments of step
-// s+2 (of steps 0 and 1 of stage kt+1 during steps 2 and 3) are read during
-// step s. The barrier after step 1 waits for the loads of stage kt+1 (issued
-// in steps 2 and 3 of stage kt-1) and for every wave's reads of buffer kt&1;
-// steps 2 and 3 then load stage kt+2 into that buffer. Past the last stage
-// the loads fetch nothing. On return every wave is done with the LDS.
-__device__ __forceinline__ void tile_logits(const Geo& g, const Panels& p, uint16_t* __restrict__ smem,
-                                            Acc (&acc)[kMB][kNB]) {
+// Stage kt multiplies in 4 steps; the fragments of step s+2 (of steps 0 and
+// 1 of the next stage during steps 2 and 3) are read during step s. The
+// barrier after step 1 waits for the loads of the next stage (issued in steps
+// 2 and 3 of the stage before) and for every wave's reads of this stage's
+// buffer; steps 2 and 3 then load, into that buffer, the stage two ahead:
+// stage kt+2 of this tile, or, in the last two stages, stage 0 or 1 of the
+// next tile (pn) when there is one and the tile has two stages or more, else
+// nothing. So on return the next tile's stages 0 and 1 are loaded or in
+// flight and its first fragments are in fa, fb, with no pause between tiles.
+__device__ __forceinline__ void tile_logits(const Geo& g, const Panels& p, const Panels& pn, bool next, int par,
+                                            uint16_t* __restrict__ smem, Acc (&acc)[kMB][kNB],
+                                            bf16x8 (&fa)[kSteps][kMB], bf16x8 (&fb)[kSteps][kNB]) {
   uint16_t* sa = smem;                  // [2][kStage]
   uint16_t* sb = smem + 2 * kStage;     // [2][kStage]
   const int wave = threadIdx.x >> 6;
@@ -290,13 +297,9 @@ __device__ __forceinline__ void tile_logits(const Geo& g, const Panels& p, uint1
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   const int kt_n = g.d / BK;
-  // stage 0 landed: all but the last 16 panel loads (stage 1) are done
-  asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-  bf16x8 fa[kSteps][kMB], fb[kSteps][kNB];
-  load_frags(sa, sb, wm, wn, 0, fa[0], fb[0]);
-  load_frags(sa, sb, wm, wn, 1, fa[1], fb[1]);
+  const bool ahead = next && kt_n >= 2;
   for (int kt = 0; kt < kt_n; ++kt) {
-    const int cur = kt & 1;
+    const int cur = (kt + par) & 1;
     uint16_t* ca = sa + cur * kStage;
     uint16_t* cb = sb + cur * kStage;
     uint16_t* na = sa + (cur ^ 1) * kStage;
@@ -304,11 +307,14 @@ __device__ __forceinline__ void tile_logits(const Geo& g, const Panels& p, uint1
     mma_step<0>(fa[0], fb[0], acc, ca, cb, wm, wn, 2, fa[2], fb[2], p, 0, ca, cb);
     mma_step<0>(fa[1], fb[1], acc, ca, cb, wm, wn, 3, fa[3], fb[3], p, 0, ca, cb);
     stage_barrier();
-    const int k2 = kt + 2 < kt_n ? (kt + 2) * BK * 2 : kNoLoad;
-    mma_step<1>(fa[2], fb[2], acc, na, nb, wm, wn, 0, fa[0], fb[0], p, k2, ca, cb);
-    mma_step<2>(fa[3], fb[3], acc, na, nb, wm, wn, 1, fa[1], fb[1], p, k2, ca, cb);
+    const bool own = kt + 2 < kt_n;
+    Panels q = p;
+    q.a = own ? p.a : pn.a;
+    q.b = own ? p.b : pn.b;
+    const int k2 = own ? (kt + 2) * BK * 2 : (ahead ? (kt + 2 - kt_n) * BK * 2 : kNoLoad);
+    mma_step<1>(fa[2], fb[2], acc, na, nb, wm, wn, 0, fa[0], fb[0], q, k2, ca, cb);
+    mma_step<2>(fa[3], fb[3], acc, na, nb, wm, wn, 1, fa[1], fb[1], q, k2, ca, cb);
   }
-  stage_barrier();
 }
 
 // BF16 bits of an fp32 value, rounded to nearest even, as a float.
@@ -317,11 +323,12 @@ __device__ __forceinline__ float round_bf16(float v) {
   return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to BF16 (nearest even) in one 32-bit word, low first.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const __bf16 a = static_cast<__bf16>(lo);
-  const __bf16 b = static_cast<__bf16>(hi);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // 8 BF16 logits (4 packed pairs) at column c of a row; pad columns -inf.
@@ -341,15 +348,36 @@ __device__ __forceinline__ void store8(const Geo& g, uint16_t* __restrict__ dst,
     w2 = o[2];
     w3 = o[3];
   }
-  // an ordinary store: L2 merges the 16-byte pieces of a row into whole lines
-  // (with the non-temporal hint they reach HBM as partial lines, 15% slower)
   *reinterpret_cast<u32x4*>(dst) = u32x4{w0, w1, w2, w3};
 }
 
-// Stores the tile's BF16 logits from the accumulators; pads -inf. Lane l
-// holds, for q = 0..3, columns 8q + 4h .. +3 (h = l/32) of row l%32 of block
-// (i, j); one exchange with lane l^32 gives lane l the 16 columns 16h .. +15,
-// stored as two 16-byte pieces.
+// The 16 BF16 logits of block (i, j) that lane l stores, as 8 packed words:
+// lane l holds, for q = 0..3, columns 8q + 4h .. +3 (h = l/32) of row l%32;
+// one exchange with lane l^32 gives it the 16 columns 16h .. +15.
+__device__ __forceinline__ void block_words(const Acc& v, int h, uint32_t (&w)[8]) {
+  // columns 8q + 4h + (0, 1) and (2, 3) of this lane, q = 0..3
+  const uint32_t p00 = pack_bf16(v[0], v[1]), p01 = pack_bf16(v[2], v[3]);
+  const uint32_t p10 = pack_bf16(v[4], v[5]), p11 = pack_bf16(v[6], v[7]);
+  const uint32_t p20 = pack_bf16(v[8], v[9]), p21 = pack_bf16(v[10], v[11]);
+  const uint32_t p30 = pack_bf16(v[12], v[13]), p31 = pack_bf16(v[14], v[15]);
+  // h = 0 keeps q = 0, 1 and takes the partner's; h = 1 keeps q = 2, 3
+  const uint32_t g00 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(h ? p00 : p20), 32));
+  const uint32_t g01 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(h ? p01 : p21), 32));
+  const uint32_t g10 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(h ? p10 : p30), 32));
+  const uint32_t g11 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(h ? p11 : p31), 32));
+  const uint32_t a0 = h ? p20 : p00, a1 = h ? p21 : p01;
+  const uint32_t b0 = h ? p30 : p10, b1 = h ? p31 : p11;
+  w[0] = h ? g00 : a0;
+  w[1] = h ? g01 : a1;
+  w[2] = h ? a0 : g00;
+  w[3] = h ? a1 : g01;
+  w[4] = h ? g10 : b0;
+  w[5] = h ? g11 : b1;
+  w[6] = h ? b0 : g10;
+  w[7] = h ? b1 : g11;
+}
+
+// Stores the tile's BF16 logits from the accumulators; pads -inf.
 __device__ __forceinline__ void tile_store(const Geo& g, int64_t row0, int64_t col0, const Acc (&acc)[kMB][kNB],
                                            uint16_t* __restrict__ out, int64_t ldo) {
   const int lane = threadIdx.x & 63;
@@ -357,28 +385,37 @@ __device__ __forceinline__ void tile_store(const Geo& g, int64_t row0, int64_t c
   const int wave = threadIdx.x >> 6;
   const int wm = wave % (BM / kWaveM);
   const int wn = wave / (BM / kWaveM);
+  const int64_t cw = col0 + wn * kWaveN + 16 * h;  // this lane's first column of block j = 0
+  if (col0 + BN <= g.vocab_real) {                 // uniform: every column of the tile is real
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) {
+      const int64_t gr = row0 + wm * kWaveM + i * 32 + (lane & 31);
+      u32x4* dst = reinterpret_cast<u32x4*>(out + gr * ldo + cw);
+#pragma unroll
+      for (int j = 0; j < kNB; ++j) {
+        uint32_t w[8];
+        block_words(acc[i][j], h, w);
+        // ordinary stores: L2 merges the 16-byte pieces of a row into whole lines
+        // (with the non-temporal hint they reach HBM as partial lines, 15% slower)
+        if (gr < g.n_rows) {
+          dst[4 * j] = u32x4{w[0], w[1], w[2], w[3]};
+          dst[4 * j + 1] = u32x4{w[4], w[5], w[6], w[7]};
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kMB; ++i) {
     const int64_t gr = row0 + wm * kWaveM + i * 32 + (lane & 31);
 #pragma unroll
     for (int j = 0; j < kNB; ++j) {
-      const Acc& v = acc[i][j];
-      // columns 8q + 4h + (0, 1) and (2, 3) of this lane, q = 0..3
-      const uint32_t p00 = pack_bf16(v[0], v[1]), p01 = pack_bf16(v[2], v[3]);
-      const uint32_t p10 = pack_bf16(v[4], v[5]), p11 = pack_bf16(v[6], v[7]);
-      const uint32_t p20 = pack_bf16(v[8], v[9]), p21 = pack_bf16(v[10], v[11]);
-      const uint32_t p30 = pack_bf16(v[12], v[13]), p31 = pack_bf16(v[14], v[15]);
-      // h = 0 keeps q = 0, 1 and takes the partner's; h = 1 keeps q = 2, 3
-      const uint32_t g00 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(h ? p00 : p20), 32));
-      const uint32_t g01 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(h ? p01 : p21), 32));
-      const uint32_t g10 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(h ? p10 : p30), 32));
-      const uint32_t g11 = static_cast<uint32_t>(__shfl_xor(static_cast<int>(h ? p11 : p31), 32));
-      const int64_t gc = col0 + wn * kWaveN + j * 32 + 16 * h;
+      uint32_t w[8];
+      block_words(acc[i][j], h, w);
+      const int64_t gc = cw + j * 32;
       if (gr >= g.n_rows || gc >= g.vocab_padded) continue;
-      const uint32_t a0 = h ? p20 : p00, a1 = h ? p21 : p01;
-      const uint32_t b0 = h ? p30 : p10, b1 = h ? p31 : p11;
-      store8(g, out + gr * ldo + gc, gc, h ? g00 : a0, h ? g01 : a1, h ? a0 : g00, h ? a1 : g01);
-      store8(g, out + gr * ldo + gc + 8, gc + 8, h ? g10 : b0, h ? g11 : b1, h ? b0 : g10, h ? b1 : g11);
+      store8(g, out + gr * ldo + gc, gc, w[0], w[1], w[2], w[3]);
+      store8(g, out + gr * ldo + gc + 8, gc + 8, w[4], w[5], w[6], w[7]);
     }
   }
 }
@@ -505,10 +542,20 @@ __global__ __launch_bounds__(kThreads) void k_linear(Geo g, const float* __restr
   const int kt_n = g.d / BK;
   int64_t v = blockIdx.x, m_t = 0, n_t = 0;
   if (!next_tile(g, n_virtual, v, m_t, n_t)) return;  // uniform across the workgroup
-  Panels p = make_panels(g, m_t * BM, g.col_base + n_t * BN);
-  prefetch_tile(p, kt_n, smem);
   const int lane = threadIdx.x & 63;
   const int wm = (threadIdx.x >> 6) % (BM / kWaveM);
+  const int wn = (threadIdx.x >> 6) / (BM / kWaveM);
+  Panels p = make_panels(g, m_t * BM, g.col_base + n_t * BN);
+  int par = 0;
+  bf16x8 fa[kSteps][kMB], fb[kSteps][kNB];
+  prefetch_tile(p, kt_n, par, smem);
+  // stage 0 landed: all but the last 16 panel loads (stage 1) are done
+  asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  load_frags(smem, smem + 2 * kStage, wm, wn, 0, fa[0], fb[0]);
+  load_frags(smem, smem + 2 * kStage, wm, wn, 1, fa[1], fb[1]);
+  int64_t v2 = v + gridDim.x, m2 = 0, n2 = 0;
+  bool more = next_tile(g, n_virtual, v2, m2, n2);
+  Panels pn = more ? make_panels(g, m2 * BM, g.col_base + n2 * BN) : p;
   while (true) {
     const int64_t row0 = m_t * BM;
     const int64_t col0 = g.col_base + n_t * BN;
@@ -523,23 +570,29 @@ __global__ __launch_bounds__(kThreads) void k_linear(Geo g, const float* __restr
       }
     }
     Acc acc[kMB][kNB];
-    tile_logits(g, p, smem, acc);
-    // the next tile's first stages load while this tile's results are written
-    int64_t v2 = v + gridDim.x, m2 = 0, n2 = 0;
-    const bool more = next_tile(g, n_virtual, v2, m2, n2);
-    if (more) {
-      p = make_panels(g, m2 * BM, g.col_base + n2 * BN);
-      prefetch_tile(p, kt_n, smem);
-    }
+    tile_logits(g, p, pn, more, par, smem, acc, fa, fb);
     if (kLogp)
       tile_summaries(g, row0, col0, acc, tr, tgr, ws);
     else
       tile_store(g, row0, col0, acc, out, ldo);
     if (!more) break;
-    v = v2;
+    par = (par + kt_n) & 1;
     m_t = m2;
     n_t = n2;
+    p = pn;
+    v = v2;
+    v2 = v + gridDim.x;
+    more = next_tile(g, n_virtual, v2, m2, n2);
+    pn = more ? make_panels(g, m2 * BM, g.col_base + n2 * BN) : p;
+    if (kt_n == 1) {
+      // a one-stage tile could not load the next one in its loop
+      prefetch_tile(p, kt_n, par, smem);
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      load_frags(smem + par * kStage, smem + (2 + par) * kStage, wm, wn, 0, fa[0], fb[0]);
+      load_frags(smem + par * kStage, smem + (2 + par) * kStage, wm, wn, 1, fa[1], fb[1]);
+    }
   }
+  (void)wn;
 }
 
 // Summary k (global column order) of a row in rank-major storage: rank

@@ -57,10 +57,19 @@ def params(n, vr, seed):
 
 
 def test_exact_inputs_small_shapes():
+    """Exactly summable inputs: the logits bit for bit, the logprob against the
+    oracle. The last three shapes have more 256 x 256 tiles than a GPU has
+    compute units, so a workgroup runs several tiles in a row, with one, two
+    and three 64-deep stages per tile (the loads of a tile's first stages run
+    during the previous tile's last ones; three stages flip the LDS buffer
+    order from one tile to the next)."""
     import torch
     for seed, n, d, vr, vp, hpad, wpad, opad in [(1, 5, 64, 300, 320, 0, 8, 8), (2, 130, 128, 1000, 1024, 8, 0, 0),
                                                   (3, 257, 448, 1999, 2048, 16, 24, 64), (4, 1, 4096, 700, 768, 0, 0, 0),
-                                                  (5, 129, 192, 64, 64, 0, 0, 0)]:
+                                                  (5, 129, 192, 64, 64, 0, 0, 0),
+                                                  (6, 2000, 64, 10000, 10240, 0, 0, 0),
+                                                  (7, 1500, 128, 12000, 12288, 8, 8, 0),
+                                                  (8, 1100, 192, 14999, 15360, 0, 8, 8)]:
         say(f"case: exact {n} x {d} x {vr}/{vp}")
         hb, wb = datagen.linear_exact_inputs(seed, n, d, vr)
         h, w = padded(hb, d + hpad), padded(wb, d + wpad)
