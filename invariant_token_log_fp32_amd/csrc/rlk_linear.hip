@@ -491,16 +491,17 @@ __device__ __forceinline__ void tile_summaries(const Geo& g, int64_t row0, int64
     const bool greedy = (t == 0.0f);
     if (__any(greedy)) {
       // first column holding the maximum, and NaN or +inf among the real columns
-      bool bad = false;
+      // bitwise operators, not && and ||: no branch per column
+      int bad = 0;
       int first = INT32_MAX;
 #pragma unroll
       for (int k = 63; k >= 0; --k) {
         const int cl = 32 * (k >> 4) + 8 * ((k >> 2) & 3) + (k & 3);
-        const bool ok = cl < lim;
-        bad |= ok && ((x[k] != x[k]) || (x[k] == INFINITY));
-        first = (ok && x[k] == m) ? static_cast<int>(cb) + cl + 4 * h : first;
+        const int ok = cl < lim;
+        bad |= ok & (static_cast<int>(x[k] != x[k]) | static_cast<int>(x[k] == INFINITY));
+        first = (ok & static_cast<int>(x[k] == m)) ? static_cast<int>(cb) + cl + 4 * h : first;
       }
-      bad = bad || (__shfl_xor(static_cast<int>(bad), 32) != 0);
+      bad |= __shfl_xor(bad, 32);
       const int ofirst = __shfl_xor(first, 32);
       first = ofirst < first ? ofirst : first;
       if (greedy) {
