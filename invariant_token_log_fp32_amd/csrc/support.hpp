@@ -759,9 +759,11 @@ __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restric
   uint32_t bt = 0;
   if (tid == 0) {
     const bool tok = (tg >= 0) && (tg < vocab_real);
-    if (tok) bt = rowp[tg];
-    const float xt = __uint_as_float(bt << 16);
     const RowMerge mr = merge_row(L.sm, t, tok, tg, shard_width);
+    // the target's BF16 bits ride in its shard's summary (a searched row has
+    // T > 0 and a successful merge, so that summary reported them)
+    if (tok && mr.ok && t > 0.0f) bt = static_cast<uint32_t>(L.sm[tg / shard_width].aux) & 0xFFFFu;
+    const float xt = __uint_as_float(bt << 16);
     ref = mr.logp;
     lse = mr.lse;
     ref_out[row] = ref;
