@@ -238,6 +238,8 @@ def linlogp(lib, h=P, n=4, d=128, ldh=128, w=P + 0x100000, ldw=128, L=None, t=P 
     (dict(ldw=64), SHAPE), (dict(ldw=130), SHAPE), (dict(n=(1 << 22) + 1), SHAPE), (dict(n=-1), SHAPE),
     (dict(L=lay(groups=3)), GROUPS), (dict(L=lay(vp=1000, vr=1000)), SHAPE), (dict(L=lay(stride=1020)), SHAPE),
     (dict(h=P + 8), ALIGN), (dict(w=P + 0x100008), ALIGN), (dict(out=P + 0x200004), ALIGN),
+    # row strides above 2^21 elements: a 256-row panel's byte offsets would not fit the buffer offsets
+    (dict(ldh=(1 << 21) + 8), SHAPE), (dict(ldw=(1 << 21) + 8), SHAPE),
 ])
 def test_linear_rejects_bad_arguments(lib, kw, code):
     assert lin(lib, **kw) == code
@@ -248,6 +250,7 @@ def test_linear_rejects_bad_arguments(lib, kw, code):
     (dict(ws=None), NULL), (dict(wsb=4 * 8 * 16 - 1), WS), (dict(ws=P + 0x400008), ALIGN),
     (dict(t=P + 0x300002), ALIGN), (dict(tg=P + 0x300104), ALIGN), (dict(out=P + 0x300201), ALIGN),
     (dict(lse=P + 0x300302), ALIGN), (dict(d=96, ldh=96, ldw=96), SHAPE), (dict(L=lay(groups=6)), GROUPS),
+    (dict(ldh=(1 << 21) + 8), SHAPE), (dict(ldw=(1 << 21) + 8), SHAPE),
 ])
 def test_linear_logp_rejects_bad_arguments(lib, kw, code):
     assert linlogp(lib, **kw) == code
