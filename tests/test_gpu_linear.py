@@ -104,6 +104,74 @@ def test_special_rows():
     assert_close(to_host(lp), want, what="special rows")
 
 
+def test_special_logit_values():
+    """Non-finite logits produced by the product itself: a NaN hidden value (a
+    NaN row), +inf against a dense projection column (every logit +inf), one
+    logit overflowing to +inf (2^100 * 2^100), -inf logits (one of them the
+    target), plain rows, each at temperature 0.7, 1.3 and 0 (greedy); the
+    summaries' NaN, +inf and -inf handling must give the oracle's values.
+    The last rows hold a finite logit of 2^98, outside the scaled-logit domain
+    |x * log2(e) / T| < 2^30: there the result must be the oracle's value or
+    NaN, never another number."""
+    import torch
+    n, d, vr, vp = 18, 128, 1000, 1024
+    say("case: special logits 18 x 128 x 1000")
+    hb, wb = datagen.linear_exact_inputs(31, n, d, vr)
+    big = datagen.f32_to_bf16_bits(np.array([2.0 ** 100, -(2.0 ** 100), np.inf, np.nan], np.float32))
+    quarter = datagen.f32_to_bf16_bits(np.array([0.25], np.float32))[0]
+    wb[:, 3] = quarter                 # a dense column: hidden value +inf there makes every logit +inf
+    wb[:, 11] = 0
+    wb[700, 11] = big[0]               # only column 700 sees hidden column 11
+    wb[:, 12] = 0
+    wb[[5, 6], 12] = big[0]            # columns 5 and 6 see hidden column 12
+    hb[:, 11] = 0
+    hb[:, 12] = 0
+    kinds = []
+    for r in range(n):
+        kind = r // 3                  # 0 NaN row, 1 all +inf, 2 one +inf, 3 two -inf, 4 plain, 5 out of domain
+        kinds.append(kind)
+        if kind == 0:
+            hb[r, 40] = big[3]
+        elif kind == 1:
+            hb[r, 3] = big[2]
+        elif kind == 2:
+            hb[r, 11] = big[0]
+        elif kind == 3:
+            hb[r, 12] = big[1]
+        elif kind == 5:
+            hb[r, 11] = quarter        # logit 700 = 2^98, finite
+    temps = np.array([0.7, 1.3, 0.0] * 6, np.float32)
+    tg = np.array([700 if k in (2, 5) else (5 if k == 3 else 17) for k in kinds], np.int64)
+    tg[10] = 6                         # rows 9-11 hold two -inf logits (columns 5, 6); row 10 targets the other
+    h, w = padded(hb, d), padded(wb, d)
+    logits = run_linear(h, w, vp)
+    want_logits = LIN.logits_bf16(hb, wb, vp)
+    # a NaN logit may carry any sign and payload; every other logit is bit-exact
+    gnan = (logits & 0x7FFF) > 0x7F80
+    wnan = (want_logits & 0x7FFF) > 0x7F80
+    assert np.array_equal(gnan, wnan), f"NaN logits differ: rows {np.flatnonzero((gnan != wnan).any(axis=1))}"
+    diff = np.argwhere((logits != want_logits) & ~wnan)
+    assert diff.size == 0, (f"logits differ from the exactly rounded oracle at {diff[:5].tolist()}: "
+                            f"got {[hex(logits[tuple(i)]) for i in diff[:5]]} "
+                            f"want {[hex(want_logits[tuple(i)]) for i in diff[:5]]}")
+    t_d, tg_d = upload(temps, torch.float32), upload(tg, torch.int64)
+    lp, lse = rlk.linear_logp(h, w, t_d, tg_d, vocab_padded=vp, return_lse=True)
+    ref = rlk.logp_full(torch.from_numpy(logits.view(np.int16)).to("cuda:0"), t_d, tg_d, vocab_real=vr)
+    torch.cuda.synchronize()
+    lp, lse, ref = to_host(lp), to_host(lse), to_host(ref)
+    want_lp, want_lse = LIN.linear_logp(hb, wb, vp, temps, tg)
+    tol = row_tolerance(want_logits, vr, temps)
+    inside = np.array([k != 5 for k in kinds])
+    assert_close(lp[inside], want_lp[inside], tol=tol[inside], what="special logits: logp")
+    assert_close(lse[inside], want_lse[inside], tol=tol[inside], what="special logits: lse")
+    assert_close(lp[inside], ref[inside], tol=tol[inside], what="special logits: fused vs unfused")
+    for r in np.flatnonzero(~inside):
+        for name, got in (("fused", lp[r]), ("unfused", ref[r])):
+            ok = np.isnan(got) or (np.isfinite(want_lp[r]) == np.isfinite(got) and
+                                   (not np.isfinite(got) or abs(got - want_lp[r]) <= tol[r]))
+            assert ok, f"row {r} (scaled logit beyond 2^30, {name}): {got} is neither NaN nor {want_lp[r]}"
+
+
 def test_random_inputs_against_rlk_logp_full():
     import torch
     n, d, vr, vp = 300, 512, 5000, 5120
