@@ -137,32 +137,66 @@ struct ShardAcc {
     m0 = -INFINITY;
   }
 
-  // Consumes UU vectors; hook(x, nvalid[u]) sees each vector's unpacked values
-  // right after their terms are accumulated.
+  // Consumes UU vectors; hook(v[u], x, nvalid[u]) sees each vector as loaded
+  // and its unpacked values right after their terms are accumulated. Without
+  // a hook every vector is widened once, up front; a hook with kLateWiden
+  // widens each vector next to its use (the first chunk's maximum from an
+  // opaque copy), which keeps the widened values out of the registers the
+  // hook needs. Both orders compute the same values.
   template <int UU, typename Hook>
   __device__ __forceinline__ void consume(const u32x4 (&v)[UU], float c, Hook& hook, const int (&nvalid)[UU]) {
-    float x[UU][8];
+    if constexpr (Hook::kLateWiden) {
+      if (!have_ref) {  // wave-uniform branch, taken until a value above -inf appears
+        float cm = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < UU; ++u) unpack8(v[u], x[u]);
-    if (!have_ref) {  // wave-uniform branch, taken until a value above -inf appears
-      float cm = -INFINITY;
+        for (int u = 0; u < UU; ++u) {
+          u32x4 w = v[u];
+          asm volatile("" : "+v"(w));
+          float y[8];
+          unpack8(w, y);
 #pragma unroll
-      for (int u = 0; u < UU; ++u)
+          for (int p = 0; p < 8; ++p) cm = fmaxf(cm, y[p]);
+        }
+        set_ref(wave_max(cm), c);
+      }
+      const float nr = -r;
 #pragma unroll
-        for (int p = 0; p < 8; ++p) cm = fmaxf(cm, x[u][p]);
-      const float wm = wave_max(cm);
-      if (wm > -INFINITY) {
-        r = ref_exponent(wm, c);
-        m0 = wm;
-        have_ref = true;
+      for (int u = 0; u < UU; ++u) {
+        float x[8];
+        unpack8(v[u], x);
+#pragma unroll
+        for (int p = 0; p < 8; ++p) acc[p] += __builtin_amdgcn_exp2f(fmaf(x[p], c, nr));
+        hook(v[u], x, nvalid[u]);
+      }
+    } else {
+      float x[UU][8];
+#pragma unroll
+      for (int u = 0; u < UU; ++u) unpack8(v[u], x[u]);
+      if (!have_ref) {  // wave-uniform branch, taken until a value above -inf appears
+        float cm = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < UU; ++u)
+#pragma unroll
+          for (int p = 0; p < 8; ++p) cm = fmaxf(cm, x[u][p]);
+        set_ref(wave_max(cm), c);
+      }
+      const float nr = -r;
+#pragma unroll
+      for (int u = 0; u < UU; ++u) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) acc[p] += __builtin_amdgcn_exp2f(fmaf(x[u][p], c, nr));
+        hook(v[u], x[u], nvalid[u]);
       }
     }
-    const float nr = -r;
-#pragma unroll
-    for (int u = 0; u < UU; ++u) {
-#pragma unroll
-      for (int p = 0; p < 8; ++p) acc[p] += __builtin_amdgcn_exp2f(fmaf(x[u][p], c, nr));
-      hook(x[u], nvalid[u]);
+  }
+
+  // Fixes the reference from the wave maximum of the first chunk that holds
+  // a value above -inf.
+  __device__ __forceinline__ void set_ref(float wm, float c) {
+    if (wm > -INFINITY) {
+      r = ref_exponent(wm, c);
+      m0 = wm;
+      have_ref = true;
     }
   }
 
@@ -182,11 +216,12 @@ __device__ __forceinline__ void load_chunk(const u32x4* __restrict__ base, int f
   }
 }
 
-// Per-vector observer called by the streaming pass with each vector's 8
-// values (float32 widenings of the BF16 columns, in column order) and the
-// number of them that are real columns (8, the tail count, or 0).
+// Per-vector observer called by the streaming pass with each vector as
+// loaded, its 8 values (float32 widenings of the BF16 columns, in column
+// order) and the number of them that are real columns (8, the tail count, or 0).
 struct NoHook {
-  __device__ __forceinline__ void operator()(const float (&)[8], int) const {}
+  static constexpr bool kLateWiden = false;
+  __device__ __forceinline__ void operator()(const u32x4&, const float (&)[8], int) const {}
 };
 
 // One pass over the shard with the state machine above.

@@ -261,6 +261,7 @@ __device__ __forceinline__ uint32_t window_slots2(uint32_t w, uint32_t& outside)
 // Counts tokens into the window while a pass streams them. Per lane: the
 // number of -inf tokens and whether any other token fell outside the window.
 struct WindowHook {
+  static constexpr bool kLateWiden = true;
   uint32_t* win;
   uint32_t ninf;
   bool odd;
@@ -275,39 +276,34 @@ struct WindowHook {
     }
   }
 
-  // x: 8 values (float32 widenings of BF16 columns); nvalid of them are real.
-  __device__ __forceinline__ void operator()(const float (&x)[8], int nvalid) {
+  // v: one vector of 8 BF16 columns as loaded (column 2i in the low half of
+  // word i); x: their float32 widenings; nvalid of them are real.
+  __device__ __forceinline__ void operator()(const u32x4& v, const float (&x)[8], int nvalid) {
     if (nvalid == 8) {
-      bool any_out = false;
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t slots[4];
+      uint32_t out = 0u;
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        // the two BF16 patterns of columns e, e + 1 as one word (low half = column e)
-        const uint32_t w = __builtin_amdgcn_perm(__float_as_uint(x[e + 1]), __float_as_uint(x[e]), 0x07060302u);
-        uint32_t out;
-        const uint32_t slots = window_slots2(w, out);
-        const bool in = (out == 0u);
-        atomicAdd(&win[in ? (slots & 0xFFFFu) : static_cast<uint32_t>(kWin)], 1u);
-        atomicAdd(&win[in ? (slots >> 16) : static_cast<uint32_t>(kWin)], 1u);
-        any_out |= !in;
+      for (int i = 0; i < 4; ++i) {
+        uint32_t o;
+        slots[i] = window_slots2(w[i], o);
+        out |= o;
       }
-      if (any_out) {  // rare: a word with a value outside the window went to the trash slot whole
+      if (out == 0u) {  // all 8 values in the window
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const uint32_t b0 = __float_as_uint(x[e]) >> 16;
-          const uint32_t b1 = __float_as_uint(x[e + 1]) >> 16;
-          const uint32_t s0 = window_slot(b0);
-          const uint32_t s1 = window_slot(b1);
-          if (s0 == static_cast<uint32_t>(kWin) || s1 == static_cast<uint32_t>(kWin)) {
-            if (s0 == static_cast<uint32_t>(kWin)) {
-              outside(b0);
-            } else {
-              atomicAdd(&win[s0], 1u);
-            }
-            if (s1 == static_cast<uint32_t>(kWin)) {
-              outside(b1);
-            } else {
-              atomicAdd(&win[s1], 1u);
-            }
+        for (int i = 0; i < 4; ++i) {
+          atomicAdd(&win[slots[i] & 0xFFFFu], 1u);
+          atomicAdd(&win[slots[i] >> 16], 1u);
+        }
+      } else {  // rare: a value outside the window, taken one by one
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t b = (w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+          const uint32_t slot = window_slot(b);
+          if (slot < static_cast<uint32_t>(kWin)) {
+            atomicAdd(&win[slot], 1u);
+          } else {
+            outside(b);
           }
         }
       }
@@ -350,11 +346,13 @@ __device__ __forceinline__ void window_pass(NucLds& L, const uint16_t* __restric
                  v.x = ws4[0]; v.y = ws4[1]; v.z = ws4[2]; v.w = ws4[3];
                  float x[8];
                  unpack8(v, x);
-                 hook(x, 8);
+                 hook(v, x, 8);
                },
                [&](uint32_t b) {
+                 u32x4 v;
+                 v.x = b; v.y = 0u; v.z = 0u; v.w = 0u;
                  const float x[8] = {__uint_as_float(b << 16), 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                 hook(x, 1);
+                 hook(v, x, 1);
                });
   hook.publish(L);
 }
