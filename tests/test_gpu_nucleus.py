@@ -115,6 +115,56 @@ def test_tied_classes_and_parameter_mix():
     check(logits, vr, temps, top_p, top_k, targets, "ties in-support")
 
 
+def test_tied_classes_without_zero():
+    """Palette rows with no zero and no value below 2^-24 in magnitude: every
+    row stays in the 16-bit rank window, so the ties are resolved there."""
+    say("case: ties without zero")
+    vp, vr = 2048, 1999
+    rng = np.random.default_rng(61)
+    pal = np.array([-3.0, -1.0, -0.5, 0.25, 1.0, 1.5, 2.0, 2.5, 3.0], dtype=np.float32)
+    n = 40
+    logits = np.full((n, vp), datagen.BF16_NEG_INF, dtype=np.uint16)
+    for i in range(n):
+        logits[i, :vr] = datagen.f32_to_bf16_bits(rng.choice(pal, size=vr))
+    temps = rng.choice(np.array([0.7, 1.0, 1.3, 0.4], dtype=np.float32), n)
+    top_p = rng.choice(np.array([0.95, 0.99, 0.5, 1.0, 0.1], dtype=np.float32), n)
+    top_k = rng.choice(np.array([-1, 128, 1, 300, 1999, 1500], dtype=np.int32), n)
+    targets = support_targets(logits, vr, temps, top_p, top_k, 62)
+    check(logits, vr, temps, top_p, top_k, targets, "ties without zero")
+
+
+# BF16 patterns at and just past the ends of the value ranges a 16-bit rank
+# window can cover: the top (65536 and the next value), the smallest
+# magnitudes (2^-24 and the next smaller value, both signs) and two pairs of
+# large negative values (-4.24e9 / -4.26e9 and -1.823e19 / -1.830e19).
+EDGE_BITS = [0x4780, 0x4781, 0x3380, 0x337F, 0xB380, 0xB37F, 0xCF7D, 0xCF7E, 0xDF7D, 0xDF7E]
+
+
+def test_window_edge_values():
+    """Rows holding one value at or just past an edge of the rank window, with
+    supports that reach that value (top-k down to the last classes, top-p 1)
+    or stop above it; targets on that value and on the maximum."""
+    say("case: window edge values")
+    vp, vr = 3072, 3000
+    rng = np.random.default_rng(71)
+    rows, T, P, K, TG = [], [], [], [], []
+    for bits in EDGE_BITS:
+        for p, k in ((0.9, -1), (1.0, vr - 1), (1.0, vr), (0.5, 3), (0.999, vr - 2)):
+            for tg_edge in (True, False):
+                r = np.full(vp, datagen.BF16_NEG_INF, dtype=np.uint16)
+                r[:vr] = datagen.f32_to_bf16_bits(rng.normal(0.0, 2.5, vr).astype(np.float32))
+                col = int(rng.integers(0, vr))
+                r[col] = bits
+                rows.append(r)
+                T.append(0.7)
+                P.append(p)
+                K.append(k)
+                TG.append(col if tg_edge else int(np.argmax(datagen.bf16_bits_to_f32(r[:vr]))))
+    logits = np.stack(rows)
+    check(logits, vr, np.array(T, np.float32), np.array(P, np.float32), np.array(K, np.int32),
+          np.array(TG, np.int64), "window edges")
+
+
 def test_support_limited_rows_match_enumeration():
     """Rows with at most 12 finite real logits (the rest -inf): the oracle's
     support on these is pinned by exhaustive subset enumeration."""
