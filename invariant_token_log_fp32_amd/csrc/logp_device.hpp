@@ -122,6 +122,10 @@ __device__ __forceinline__ u32x4 neg_inf_vec() {
   return out;
 }
 
+// Vectors per lane (2048 columns of a shard) whose wave maximum fixes the
+// streaming reference: the first such group that holds a value above -inf.
+constexpr int kRefGroup = 4;
+
 // Wave-level streaming state for one shard.
 struct ShardAcc {
   float acc[8];
@@ -146,18 +150,21 @@ struct ShardAcc {
   template <int UU, typename Hook>
   __device__ __forceinline__ void consume(const u32x4 (&v)[UU], float c, Hook& hook, const int (&nvalid)[UU]) {
     if constexpr (Hook::kLateWiden) {
-      if (!have_ref) {  // wave-uniform branch, taken until a value above -inf appears
-        float cm = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < UU; ++u) {
-          u32x4 w = v[u];
-          asm volatile("" : "+v"(w));
-          float y[8];
-          unpack8(w, y);
+      for (int g = 0; g < UU; g += kRefGroup) {
+        if (!have_ref) {  // wave-uniform branch, taken until a value above -inf appears
+          float cm = -INFINITY;
 #pragma unroll
-          for (int p = 0; p < 8; ++p) cm = fmaxf(cm, y[p]);
+          for (int u = g; u < g + kRefGroup && u < UU; ++u) {
+            u32x4 w = v[u];
+            asm volatile("" : "+v"(w));
+            float y[8];
+            unpack8(w, y);
+#pragma unroll
+            for (int p = 0; p < 8; ++p) cm = fmaxf(cm, y[p]);
+          }
+          set_ref(wave_max(cm), c);
         }
-        set_ref(wave_max(cm), c);
       }
       const float nr = -r;
 #pragma unroll
@@ -172,13 +179,16 @@ struct ShardAcc {
       float x[UU][8];
 #pragma unroll
       for (int u = 0; u < UU; ++u) unpack8(v[u], x[u]);
-      if (!have_ref) {  // wave-uniform branch, taken until a value above -inf appears
-        float cm = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < UU; ++u)
+      for (int g = 0; g < UU; g += kRefGroup) {
+        if (!have_ref) {  // wave-uniform branch, taken until a value above -inf appears
+          float cm = -INFINITY;
 #pragma unroll
-          for (int p = 0; p < 8; ++p) cm = fmaxf(cm, x[u][p]);
-        set_ref(wave_max(cm), c);
+          for (int u = g; u < g + kRefGroup && u < UU; ++u)
+#pragma unroll
+            for (int p = 0; p < 8; ++p) cm = fmaxf(cm, x[u][p]);
+          set_ref(wave_max(cm), c);
+        }
       }
       const float nr = -r;
 #pragma unroll
@@ -190,8 +200,8 @@ struct ShardAcc {
     }
   }
 
-  // Fixes the reference from the wave maximum of the first chunk that holds
-  // a value above -inf.
+  // Fixes the reference from the wave maximum of a group of kRefGroup vectors
+  // per lane (the first group that holds a value above -inf).
   __device__ __forceinline__ void set_ref(float wm, float c) {
     if (wm > -INFINITY) {
       r = ref_exponent(wm, c);
@@ -224,18 +234,34 @@ struct NoHook {
   __device__ __forceinline__ void operator()(const u32x4&, const float (&)[8], int) const {}
 };
 
+// No observer, with the register-light order of a hook (for kernels whose
+// register budget is set by a hooked pass).
+struct NoHookLate : NoHook {
+  static constexpr bool kLateWiden = true;
+};
+
 // One pass over the shard with the state machine above.
+template <int U, typename Hook>
+__device__ __forceinline__ void pass_chunk(const u32x4* __restrict__ base, int first, int nfull, int lane, float c,
+                                           ShardAcc& st, Hook& hook) {
+  u32x4 v[U];
+  load_chunk<U>(base, first, nfull, lane, v);
+  int nvalid[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) nvalid[u] = (first + u * kWave + lane < nfull) ? 8 : 0;
+  st.template consume<U>(v, c, hook, nvalid);
+}
+
+// With a kLateWiden hook the chunks hold kRefGroup vectors per lane (fewer
+// loads in flight per wave, for kernels that run more waves per SIMD). Every
+// lane consumes its vectors in the same order and the reference comes from
+// the same group in both cases, so the sums are identical.
 template <int U, typename Hook = NoHook>
 __device__ __forceinline__ void shard_pass(const u32x4* __restrict__ base, int nfull, int tail, int lane,
                                            float c, ShardAcc& st, Hook& hook) {
-  for (int first = 0; first < nfull; first += U * kWave) {
-    u32x4 v[U];
-    load_chunk<U>(base, first, nfull, lane, v);
-    int nvalid[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) nvalid[u] = (first + u * kWave + lane < nfull) ? 8 : 0;
-    st.template consume<U>(v, c, hook, nvalid);
-  }
+  static_assert(U % kRefGroup == 0, "chunks hold whole reference groups");
+  constexpr int kU = Hook::kLateWiden ? kRefGroup : U;
+  for (int first = 0; first < nfull; first += kU * kWave) pass_chunk<kU>(base, first, nfull, lane, c, st, hook);
   if (tail) {
     const bool owner = (lane == (nfull & (kWave - 1)));
     u32x4 v[1];

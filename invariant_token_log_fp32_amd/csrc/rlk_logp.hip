@@ -38,7 +38,8 @@
 
 namespace rlk {
 
-// Vectors per lane per chunk in the streaming loop.
+// Vectors per lane per chunk in the streaming loop (kRefGroup under a hook
+// that widens late: those kernels run more waves per SIMD).
 constexpr int kChunk = 8;
 constexpr int kRowThreads = kShards * kWave;  // 512
 
@@ -64,7 +65,7 @@ __device__ __forceinline__ ShardSummary summarize_row_shard(const uint16_t* __re
   if (ncols == 0) return s;
   if (t == 0.0f) return summarize_shard_greedy(shard, static_cast<int>(col0), ncols);
   const float c = kLog2e / t;  // IEEE float32 division
-  s = summarize_shard<kChunk>(shard, ncols, c, hook);
+  s = summarize_shard<(Hook::kLateWiden ? kRefGroup : kChunk)>(shard, ncols, c, hook);
   if (tg >= col0 && tg < col0 + ncols) s.aux = static_cast<int32_t>(shard[tg - col0]);
   return s;
 }
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(256) void k_merge(const ShardSummary* __restrict__ 
 // ----------------------------------------------------------------------------
 // Support path (top-k then top-p): see support.hpp.
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_nucleus_g1(
+__global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(6, 6))) void k_nucleus_g1(
     const uint16_t* __restrict__ logits, int64_t row_stride, int shard_width, int64_t vocab_real,
     const float* __restrict__ temperature, const float* __restrict__ top_p, const int32_t* __restrict__ top_k,
     const int64_t* __restrict__ target, float* __restrict__ policy_out, float* __restrict__ ref_out,
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(4, 
     if ((threadIdx.x & (kWave - 1)) == 0) L.sm[wave] = s;
     hook.publish(L);
   } else {
-    NoHook none;
+    NoHookLate none;
     const ShardSummary s = summarize_row_shard(rowp + col0, col0, shard_width, vocab_real, t, tg, none);
     if ((threadIdx.x & (kWave - 1)) == 0) L.sm[wave] = s;
   }

@@ -18,8 +18,8 @@
 // "cumulative >= p * Z" is evaluated exactly as cumulative >= ceil(p * Z).
 //
 // Fast path: every token is counted per compressed 16-bit rank (LDS u32
-// atomics) in a fixed window of 16384 ranks that covers every BF16 value from
-// -1.82e19 to 65536 with magnitude at least 2^-24 (the rank keeps the order of
+// atomics) in a fixed window of 12288 ranks that covers every BF16 value from
+// -4.24e9 to 65536 with magnitude at least 2^-24 (the rank keeps the order of
 // the values; -inf tokens are counted apart, mass 0). With groups == 1 the
 // shard-waves count while they stream the row for the reference logprob, so
 // the support costs no extra pass; otherwise one pass builds it. The row
@@ -41,8 +41,8 @@ constexpr int kNucThreads = 512;
 constexpr int kNucWaves = kNucThreads / kWave;
 constexpr int kBinsA = 4096;
 constexpr int kSub = 16;
-constexpr int kWin = 16384;
-constexpr int kWinPerThread = kWin / kNucThreads;  // 32
+constexpr int kWin = 12288;                        // 48 KB of counts: three rows per CU
+constexpr int kWinPerThread = kWin / kNucThreads;  // 24
 constexpr uint32_t kWinHi = 0x6081u;               // rank of 65536.0: window slot 0
 constexpr uint32_t kTinyExp = 103;                 // biased exponent: |x| < 2^-24
 constexpr uint32_t kNegInfBits = 0xFF80u;
@@ -236,7 +236,7 @@ typedef short i16x2 __attribute__((ext_vector_type(2)));
 
 // Window slots of the two BF16 values packed in one 32-bit word, computed on
 // 16-bit integer lane pairs (low half = first value):
-//   negative b: slot = b - 0x9F7E, in the window iff slot - 0x1402 <= 0x2BFD
+//   negative b: slot = b - 0x9F7E, in the window iff slot - 0x1402 <= 0x1BFD
 //   positive b: slot = 0x4780 - b, in the window iff slot <= 0x1400
 // `outside` is nonzero iff a half lies outside the window; halves inside get
 // exactly window_slot() (checked against it on all 65536 patterns).
@@ -253,7 +253,7 @@ __device__ __forceinline__ uint32_t window_slots2(uint32_t w, uint32_t& outside)
       "v_pk_sub_u16 %[out], %[d], %[span] clamp"
       : [neg] "=&v"(neg), [a] "=&v"(a), [b] "=&v"(b), [slot] "=&v"(slot), [lo] "=&v"(lo), [d] "=&v"(d),
         [span] "=&v"(span), [out] "=&v"(outside)
-      : [w] "v"(w), [k1] "v"(0x9F7E9F7Eu), [k2] "v"(0x47804780u), [k3] "v"(0x14021402u), [k4] "v"(0x2BFD2BFDu),
+      : [w] "v"(w), [k1] "v"(0x9F7E9F7Eu), [k2] "v"(0x47804780u), [k3] "v"(0x14021402u), [k4] "v"(0x1BFD1BFDu),
         [k5] "v"(0x14001400u));
   return slot;
 }
