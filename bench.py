@@ -18,7 +18,9 @@ events on the launch stream over the same region. `cpu_baseline` times the
 CPU oracle (float64 numpy, one core) on a bounded sample of the same rows.
 `secondary` reports rlk_logp_nucleus on the top-p 0.95 workload, the
 backward (rlk_logp_backward) on it, rlk_logp_nucleus on the per-request
-workload (64 requests x 128 rows), the vocabulary-parallel form, the
+workload (64 requests x 128 rows) and on the invariance-stress workload (64
+ragged sequences evaluated as batches of 1, 7 and 64 sequences, with the
+byte mismatches between those passes), the vocabulary-parallel form, the
 gradient L2 norm and the fused LM-head linear + logprob, for information.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -255,6 +257,52 @@ def main():
                     "top-k {-1,128}", "entry_point": "rlk_logp_nucleus", "ms_per_step": ms_r,
                     "tokens_per_s": wr.n_rows / (ms_r * 1e-3), "achieved_GBs": ab / (ms_r * 1e-3) / 1e9,
                     "frac": ab / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS})
+        del lg_r
+        # invariance stress: 64 ragged sequences (lengths 1..1024), top-p 0.95, evaluated as batches of
+        # 1, 7 and 64 sequences; reports each pass's time and the byte mismatches against one call
+        wst = datagen.stress()
+        lg_s = torch.empty((wst.n_rows, wst.row_stride), dtype=torch.int16, device=dev)
+        tg_s = np.empty(wst.n_rows, dtype=np.int64)
+        for s0 in range(0, wst.n_rows, 4096):
+            blk, tblk = wst.generate(rows=range(s0, min(s0 + 4096, wst.n_rows)))
+            tg_s[s0:s0 + len(blk)] = tblk
+            lg_s[s0:s0 + len(blk)].copy_(torch.from_numpy(blk.view(np.int16)))
+            del blk
+        prm_s = dict(t=torch.from_numpy(wst.temperature).to(dev), p=torch.from_numpy(wst.top_p).to(dev),
+                     k=torch.from_numpy(wst.top_k).to(dev), target=torch.from_numpy(tg_s).to(dev))
+        starts = np.concatenate([[0], np.cumsum(wst.seq_lengths)]).astype(np.int64)
+        nseq = len(wst.seq_lengths)
+        pol_s = torch.empty(wst.n_rows, dtype=torch.float32, device=dev)
+        ref_s = torch.empty(wst.n_rows, dtype=torch.float32, device=dev)
+        wss = rlk.workspace_bytes(wst.n_rows, wst.vocab_padded, wst.vocab_real, groups=args.groups, nucleus=True)
+        wss = torch.empty(wss, dtype=torch.uint8, device=dev) if wss else None
+
+        def spass(bs):
+            for b in range(0, nseq, bs):
+                lo, hi = int(starts[b]), int(starts[min(b + bs, nseq)])
+                rlk.logp_nucleus(lg_s[lo:hi], prm_s["t"][lo:hi], prm_s["p"][lo:hi], prm_s["k"][lo:hi],
+                                 prm_s["target"][lo:hi], vocab_real=wst.vocab_real, vocab_padded=wst.vocab_padded,
+                                 groups=args.groups, policy_out=pol_s[lo:hi], ref_out=ref_s[lo:hi], workspace=wss)
+
+        spass(nseq)
+        torch.cuda.synchronize()
+        base_s = (pol_s.clone(), ref_s.clone())
+        modes = {}
+        mism = 0
+        for bs in (1, 7, nseq):
+            _, ms_s = time_calls(lambda i, bs=bs: spass(bs), 3, 1)
+            mism += int((pol_s.view(torch.int32) != base_s[0].view(torch.int32)).sum().item())
+            mism += int((ref_s.view(torch.int32) != base_s[1].view(torch.int32)).sum().item())
+            modes[f"batches of {bs} sequences"] = {"calls": (nseq + bs - 1) // bs, "ms_per_pass": ms_s,
+                                                   "tokens_per_s": wst.n_rows / (ms_s * 1e-3)}
+        ab_s = bytes_nucleus(wst.n_rows, wst.vocab_real)
+        ms_one = modes[f"batches of {nseq} sequences"]["ms_per_pass"]
+        sec.append({"workload": f"invariance stress: {nseq} ragged sequences ({wst.n_rows} rows) x 152576, "
+                    "T 0.7, top-p 0.95, batches of 1, 7 and 64 sequences", "entry_point": "rlk_logp_nucleus",
+                    "ms_per_step": ms_one, "tokens_per_s": wst.n_rows / (ms_one * 1e-3),
+                    "achieved_GBs": ab_s / (ms_one * 1e-3) / 1e9, "frac": ab_s / (ms_one * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "modes": modes, "byte_mismatches_vs_one_call": mism})
+        del lg_s, base_s
         # vocabulary-parallel form: 8 ranks, each with its own 8192 x 19072 slice
         G = 8
         cols = w.vocab_padded // G
