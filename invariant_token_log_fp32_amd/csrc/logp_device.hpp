@@ -150,31 +150,7 @@ struct ShardAcc {
   template <int UU, typename Hook>
   __device__ __forceinline__ void consume(const u32x4 (&v)[UU], float c, Hook& hook, const int (&nvalid)[UU]) {
     if constexpr (Hook::kLateWiden) {
-#pragma unroll
-      for (int g = 0; g < UU; g += kRefGroup) {
-        if (!have_ref) {  // wave-uniform branch, taken until a value above -inf appears
-          float cm = -INFINITY;
-#pragma unroll
-          for (int u = g; u < g + kRefGroup && u < UU; ++u) {
-            u32x4 w = v[u];
-            asm volatile("" : "+v"(w));
-            float y[8];
-            unpack8(w, y);
-#pragma unroll
-            for (int p = 0; p < 8; ++p) cm = fmaxf(cm, y[p]);
-          }
-          set_ref(wave_max(cm), c);
-        }
-      }
-      const float nr = -r;
-#pragma unroll
-      for (int u = 0; u < UU; ++u) {
-        float x[8];
-        unpack8(v[u], x);
-#pragma unroll
-        for (int p = 0; p < 8; ++p) acc[p] += __builtin_amdgcn_exp2f(fmaf(x[p], c, nr));
-        hook(v[u], x, nvalid[u]);
-      }
+      consume_late<UU, true, false>(v, c, hook, nvalid);
     } else {
       float x[UU][8];
 #pragma unroll
@@ -196,6 +172,45 @@ struct ShardAcc {
 #pragma unroll
         for (int p = 0; p < 8; ++p) acc[p] += __builtin_amdgcn_exp2f(fmaf(x[u][p], c, nr));
         hook(v[u], x[u], nvalid[u]);
+      }
+    }
+  }
+
+  // The late-widening order. kRef: the reference may still be unset, so each
+  // group first checks for it; kFull: every vector holds 8 real columns (the
+  // hook's full() sees it and nvalid is not read). Once the reference is set
+  // the check is a no-op, so both instantiations compute the same values.
+  template <int UU, bool kRef, bool kFull, typename Hook>
+  __device__ __forceinline__ void consume_late(const u32x4 (&v)[UU], float c, Hook& hook, const int (&nvalid)[UU]) {
+    if constexpr (kRef) {
+#pragma unroll
+      for (int g = 0; g < UU; g += kRefGroup) {
+        if (!have_ref) {  // wave-uniform branch, taken until a value above -inf appears
+          float cm = -INFINITY;
+#pragma unroll
+          for (int u = g; u < g + kRefGroup && u < UU; ++u) {
+            u32x4 w = v[u];
+            asm volatile("" : "+v"(w));
+            float y[8];
+            unpack8(w, y);
+#pragma unroll
+            for (int p = 0; p < 8; ++p) cm = fmaxf(cm, y[p]);
+          }
+          set_ref(wave_max(cm), c);
+        }
+      }
+    }
+    const float nr = -r;
+#pragma unroll
+    for (int u = 0; u < UU; ++u) {
+      float x[8];
+      unpack8(v[u], x);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) acc[p] += __builtin_amdgcn_exp2f(fmaf(x[p], c, nr));
+      if constexpr (kFull) {
+        hook.full(v[u]);
+      } else {
+        hook(v[u], x, nvalid[u]);
       }
     }
   }
@@ -232,6 +247,7 @@ __device__ __forceinline__ void load_chunk(const u32x4* __restrict__ base, int f
 struct NoHook {
   static constexpr bool kLateWiden = false;
   __device__ __forceinline__ void operator()(const u32x4&, const float (&)[8], int) const {}
+  __device__ __forceinline__ void full(const u32x4&) const {}
 };
 
 // No observer, with the register-light order of a hook (for kernels whose
@@ -255,13 +271,34 @@ __device__ __forceinline__ void pass_chunk(const u32x4* __restrict__ base, int f
 // With a kLateWiden hook the chunks hold kRefGroup vectors per lane (fewer
 // loads in flight per wave, for kernels that run more waves per SIMD). Every
 // lane consumes its vectors in the same order and the reference comes from
-// the same group in both cases, so the sums are identical.
+// the same group in both cases, so the sums are identical. Under such a hook
+// the chunks whose vectors are all in range load without bounds checks, and
+// after the chunk that fixed the reference they skip its check; the chunk
+// boundaries and the order of the terms are the same as in the guarded loop.
 template <int U, typename Hook = NoHook>
 __device__ __forceinline__ void shard_pass(const u32x4* __restrict__ base, int nfull, int tail, int lane,
                                            float c, ShardAcc& st, Hook& hook) {
   static_assert(U % kRefGroup == 0, "chunks hold whole reference groups");
   constexpr int kU = Hook::kLateWiden ? kRefGroup : U;
-  for (int first = 0; first < nfull; first += kU * kWave) pass_chunk<kU>(base, first, nfull, lane, c, st, hook);
+  int first = 0;
+  if constexpr (Hook::kLateWiden) {
+    constexpr int kStep = kU * kWave;
+    const int nmain = nfull - nfull % kStep;
+    const int unused[kU] = {};
+    for (; first < nmain && !st.have_ref; first += kStep) {  // wave-uniform condition
+      u32x4 v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] = __builtin_nontemporal_load(base + first + u * kWave + lane);
+      st.template consume_late<kU, true, true>(v, c, hook, unused);
+    }
+    for (; first < nmain; first += kStep) {
+      u32x4 v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] = __builtin_nontemporal_load(base + first + u * kWave + lane);
+      st.template consume_late<kU, false, true>(v, c, hook, unused);
+    }
+  }
+  for (; first < nfull; first += kU * kWave) pass_chunk<kU>(base, first, nfull, lane, c, st, hook);
   if (tail) {
     const bool owner = (lane == (nfull & (kWave - 1)));
     u32x4 v[1];

@@ -83,14 +83,17 @@ __device__ __forceinline__ uint32_t window_slot(uint32_t b) {
   return (normal && idx < static_cast<uint32_t>(kWin)) ? idx : static_cast<uint32_t>(kWin);
 }
 
-// floor(w * 2^40) for 0 <= w < 2^24, from the float's bits.
+// floor(w * 2^40) for 0 <= w < 2^24 (NaN excluded). Every step is exact: a =
+// w * 2^40 is a power-of-two scaling (0 when w is 0 or below the normal range,
+// where the floor is 0 as well), hi = floor(a / 2^32) < 2^32 comes from a
+// truncating conversion, and a - hi * 2^32 is a multiple of ulp(a) below
+// 2^32, so it fits in 24 bits and its truncation is the low word.
 __device__ __forceinline__ u64 fixed40(float w) {
-  const uint32_t u = __float_as_uint(w);
-  const uint32_t e = u >> 23;
-  const u64 m = static_cast<u64>((u & 0x7FFFFFu) | 0x800000u);
-  const int sh = static_cast<int>(e) - 110;
-  if (e == 0 || sh <= -24) return 0ull;
-  return sh >= 0 ? (m << sh) : (m >> (-sh));
+  const float a = (w < 0x1p-126f) ? 0.0f : w * 0x1p40f;
+  const float hf = a * 0x1p-32f;
+  const uint32_t hi = __float2uint_rz(hf);
+  const float lo = fmaf(static_cast<float>(hi), -0x1p32f, a);
+  return (static_cast<u64>(hi) << 32) | static_cast<u64>(__float2uint_rz(lo));
 }
 
 __device__ __forceinline__ u64 weight(uint32_t b, float c, float nr) {
@@ -109,21 +112,52 @@ __device__ __forceinline__ u64 ceil_mul(float p, u64 z) {
   return static_cast<u64>((a + ((one << sh) - 1)) >> sh);
 }
 
+// Integer wave reductions and scans on DPP row operations (VALU only, no LDS
+// round trips). Integer sums are exact, so their grouping is free.
+// DPP controls: row_shr:n = 0x110 + n, row_ror:n = 0x120 + n, row_bcast:15 =
+// 0x142, row_bcast:31 = 0x143.
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t v) {  // 0 where no source lane / row masked off
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), Ctrl, RowMask, 0xF, true));
+}
+
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_add(uint32_t v) {
+  return v + dpp_or_zero<Ctrl, RowMask>(v);
+}
+
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ u64 dpp_add(u64 v) {
+  const uint32_t lo = dpp_or_zero<Ctrl, RowMask>(static_cast<uint32_t>(v));
+  const uint32_t hi = dpp_or_zero<Ctrl, RowMask>(static_cast<uint32_t>(v >> 32));
+  return v + ((static_cast<u64>(hi) << 32) | lo);
+}
+
+// Inclusive scan over the 64 lanes in lane order: within each row of 16 lanes
+// (shifts 1, 2, 4, 8), then row 0's total into row 1 and row 2's running total
+// into row 3, then rows 0-1's total into rows 2 and 3.
 template <typename T>
-__device__ __forceinline__ T wave_incl_scan(T v, int lane) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const T o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
+__device__ __forceinline__ T wave_incl_scan(T v, int /*lane*/) {
+  v = dpp_add<0x111>(v);
+  v = dpp_add<0x112>(v);
+  v = dpp_add<0x114>(v);
+  v = dpp_add<0x118>(v);
+  v = dpp_add<0x142, 0xA>(v);
+  v = dpp_add<0x143, 0xC>(v);
   return v;
 }
 
+__device__ __forceinline__ uint32_t lane63(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+__device__ __forceinline__ u64 lane63(u64 v) {
+  return (static_cast<u64>(lane63(static_cast<uint32_t>(v >> 32))) << 32) | lane63(static_cast<uint32_t>(v));
+}
+
+// Sum over the wave, in every lane (wave-uniform).
 template <typename T>
 __device__ __forceinline__ T wave_total(T v) {
-#pragma unroll
-  for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
+  return lane63(wave_incl_scan<T>(v, 0));
 }
 
 struct NucGeneral {
@@ -258,6 +292,43 @@ __device__ __forceinline__ uint32_t window_slots2(uint32_t w, uint32_t& outside)
   return slot;
 }
 
+// Window slots of the two BF16 values packed in one 32-bit word, without the
+// range check: equal to window_slot() for every half whose value lies in the
+// window.
+__device__ __forceinline__ uint32_t window_slots2_unchecked(uint32_t w) {
+  uint32_t neg, a, b, slot;
+  asm(
+      "v_pk_ashrrev_i16 %[neg], 15, %[w] op_sel_hi:[0,1]\n\t"
+      "v_pk_sub_u16 %[a], %[w], %[k1]\n\t"
+      "v_pk_sub_u16 %[b], %[k2], %[w]\n\t"
+      "v_bfi_b32 %[slot], %[neg], %[a], %[b]"
+      : [neg] "=&v"(neg), [a] "=&v"(a), [b] "=&v"(b), [slot] "=&v"(slot)
+      : [w] "v"(w), [k1] "v"(0x9F7E9F7Eu), [k2] "v"(0x47804780u));
+  return slot;
+}
+
+// Nonzero unless every one of the 8 BF16 values of a vector has magnitude in
+// [2^-24, 65536] (patterns 0x3380..0x4780 after the sign is cleared): values
+// of either sign in that range lie in the window. A sufficient test only; the
+// values it rejects are then slotted one by one.
+__device__ __forceinline__ uint32_t vector_outside_core(const uint32_t (&w)[4]) {
+  uint32_t d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t m = w[i] & 0x7FFF7FFFu;
+    asm("v_pk_sub_u16 %0, %1, %2" : "=v"(d[i]) : "v"(m), "v"(0x33803380u));  // wraps below 0x3380
+  }
+  uint32_t e0, e1, e, out;
+  asm(
+      "v_pk_max_u16 %[e0], %[d0], %[d1]\n\t"
+      "v_pk_max_u16 %[e1], %[d2], %[d3]\n\t"
+      "v_pk_max_u16 %[e], %[e0], %[e1]\n\t"
+      "v_pk_sub_u16 %[out], %[e], %[span] clamp"
+      : [e0] "=&v"(e0), [e1] "=&v"(e1), [e] "=&v"(e), [out] "=&v"(out)
+      : [d0] "v"(d[0]), [d1] "v"(d[1]), [d2] "v"(d[2]), [d3] "v"(d[3]), [span] "v"(0x14001400u));
+  return out;
+}
+
 // Counts tokens into the window while a pass streams them. Per lane: the
 // number of -inf tokens and whether any other token fell outside the window.
 struct WindowHook {
@@ -273,6 +344,37 @@ struct WindowHook {
       ++ninf;
     } else {
       odd = true;
+    }
+  }
+
+  // One by one: the exact slot of each value, or the outside tally.
+  __device__ __forceinline__ void each(const uint32_t (&w)[4]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t b = (w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+      const uint32_t slot = window_slot(b);
+      if (slot < static_cast<uint32_t>(kWin)) {
+        atomicAdd(&win[slot], 1u);
+      } else {
+        outside(b);
+      }
+    }
+  }
+
+  // A vector of 8 real columns as loaded (column 2i in the low half of word i).
+  __device__ __forceinline__ void full(const u32x4& v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t slots[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) slots[i] = window_slots2_unchecked(w[i]);
+    if (vector_outside_core(w) == 0u) {  // all 8 values in the window
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        atomicAdd(&win[slots[i] & 0xFFFFu], 1u);
+        atomicAdd(&win[slots[i] >> 16], 1u);
+      }
+    } else {  // rare: a value that may lie outside the window
+      each(w);
     }
   }
 
@@ -357,11 +459,21 @@ __device__ __forceinline__ void window_pass(NucLds& L, const uint16_t* __restric
   hook.publish(L);
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_min(T v) {
-#pragma unroll
-  for (int d = kWave / 2; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d, kWave));
-  return v;
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ int dpp_or_self(int v) {  // own value where no source lane / row masked off
+  return __builtin_amdgcn_update_dpp(v, v, Ctrl, RowMask, 0xF, false);
+}
+
+// Minimum over the wave, in every lane: rotations inside each row of 16 lanes,
+// then the row_bcast steps carry the running minimum to lane 63.
+__device__ __forceinline__ int wave_min(int v) {
+  v = min(v, dpp_or_self<0x121>(v));
+  v = min(v, dpp_or_self<0x122>(v));
+  v = min(v, dpp_or_self<0x124>(v));
+  v = min(v, dpp_or_self<0x128>(v));
+  v = min(v, dpp_or_self<0x142, 0xA>(v));
+  v = min(v, dpp_or_self<0x143, 0xC>(v));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Block-wide inclusive scan of (count, mass) over the 512 threads, in thread
@@ -442,16 +554,23 @@ __device__ __forceinline__ bool support_fast(NucLds& L, int64_t vocab_real, uint
   // in 512-slot rounds from the top and stop once a round starts below
   // 2^-42 (slots are in decreasing value order, so every later term is 0)
   const uint32_t total_c = static_cast<uint32_t>(vocab_real) - ninf_n;
+  const int r_first = jtop / kNucThreads;
+  int r_end = r_first + 1;  // block-uniform: rounds [r_first, r_end) can hold mass
+  while (r_end < kWinPerThread &&
+         !(fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(r_end * kNucThreads)) << 16), c, nr) <
+           -42.0f))
+    ++r_end;
+  uint32_t cnt[kWinPerThread];
+#pragma unroll
+  for (int r = 0; r < kWinPerThread; ++r) cnt[r] = (r >= r_first && r < r_end) ? L.u.win[r * kNucThreads + tid] : 0u;
   u64 tm = 0;
-  for (int r = jtop / kNucThreads; r < kWinPerThread; ++r) {
-    const int jfirst = r * kNucThreads;
-    if (jfirst > jtop &&
-        fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(jfirst)) << 16), c, nr) < -42.0f)
-      break;  // block-uniform
-    uint32_t cj;
-    u64 mj;
-    class_at(jfirst + tid, cj, mj);
-    tm += mj;
+#pragma unroll
+  for (int r = 0; r < kWinPerThread; ++r) {
+    if (cnt[r]) {
+      const int j = r * kNucThreads + tid;
+      const float t = fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(j)) << 16), c, nr);
+      if (t >= -42.0f) tm += static_cast<u64>(cnt[r]) * fixed40(__builtin_amdgcn_exp2f(t));
+    }
   }
   tm = wave_total(tm);
   __syncthreads();
