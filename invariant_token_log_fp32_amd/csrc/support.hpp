@@ -187,6 +187,7 @@ struct NucLds {
   uint32_t cnt_k;    // cumulative count through the top-k boundary
   u64 z_k;           // mass of the top-k set
   int kappa;         // support: fast = last kept class index, general = smallest kept key
+  int kappa_hi;      // fast: class reached by the upper threshold of a bracketed top-p scan
   uint32_t cnt_s;
   u64 z_s;
   // general path scan state
@@ -511,7 +512,7 @@ __device__ __forceinline__ void block_incl_scan(NucLds& L, uint32_t& c, u64& m, 
 // L.cnt_s / L.z_s the support's count and mass, and thread 0's `tclass` the
 // target's class.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool support_fast(NucLds& L, int64_t vocab_real, uint32_t bt, int& tclass) {
+__device__ __forceinline__ bool support_fast(NucLds& L, int64_t vocab_real, int shard_width, uint32_t bt, int& tclass) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
@@ -550,40 +551,47 @@ __device__ __forceinline__ bool support_fast(NucLds& L, int64_t vocab_real, uint
     }
   };
 
-  // totals: every real token is in the window or is -inf; masses are summed
-  // in 512-slot rounds from the top and stop once a round starts below
-  // 2^-42 (slots are in decreasing value order, so every later term is 0)
   const uint32_t total_c = static_cast<uint32_t>(vocab_real) - ninf_n;
-  const int r_first = jtop / kNucThreads;
-  int r_end = r_first + 1;  // block-uniform: rounds [r_first, r_end) can hold mass
-  while (r_end < kWinPerThread &&
-         !(fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(r_end * kNucThreads)) << 16), c, nr) <
-           -42.0f))
-    ++r_end;
-  uint32_t cnt[kWinPerThread];
+
+  // Exact total mass of the row (block-uniform result), computed only when a
+  // decision needs it. Every real token is in the window or is -inf; masses
+  // are summed in 512-slot rounds from the top and stop once a round starts
+  // below 2^-42 (slots are in decreasing value order, so every later term is 0).
+  auto exact_total = [&]() -> u64 {
+    const int r_first = jtop / kNucThreads;
+    int r_end = r_first + 1;  // block-uniform: rounds [r_first, r_end) can hold mass
+    while (r_end < kWinPerThread &&
+           !(fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(r_end * kNucThreads)) << 16), c, nr) <
+             -42.0f))
+      ++r_end;
+    uint32_t cnt[kWinPerThread];
 #pragma unroll
-  for (int r = 0; r < kWinPerThread; ++r) cnt[r] = (r >= r_first && r < r_end) ? L.u.win[r * kNucThreads + tid] : 0u;
-  u64 tm = 0;
+    for (int r = 0; r < kWinPerThread; ++r)
+      cnt[r] = (r >= r_first && r < r_end) ? L.u.win[r * kNucThreads + tid] : 0u;
+    u64 tm = 0;
 #pragma unroll
-  for (int r = 0; r < kWinPerThread; ++r) {
-    if (cnt[r]) {
-      const int j = r * kNucThreads + tid;
-      const float t = fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(j)) << 16), c, nr);
-      if (t >= -42.0f) tm += static_cast<u64>(cnt[r]) * fixed40(__builtin_amdgcn_exp2f(t));
+    for (int r = 0; r < kWinPerThread; ++r) {
+      if (cnt[r]) {
+        const int j = r * kNucThreads + tid;
+        const float t = fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(j)) << 16), c, nr);
+        if (t >= -42.0f) tm += static_cast<u64>(cnt[r]) * fixed40(__builtin_amdgcn_exp2f(t));
+      }
     }
-  }
-  tm = wave_total(tm);
-  __syncthreads();
-  if (lane == 0) L.red_u64[wv] = tm;
-  __syncthreads();
-  u64 total_m = 0;
-  for (int w = 0; w < kNucWaves; ++w) total_m += L.red_u64[w];
-  __syncthreads();
+    tm = wave_total(tm);
+    __syncthreads();
+    if (lane == 0) L.red_u64[wv] = tm;
+    __syncthreads();
+    u64 total_m = 0;
+    for (int w = 0; w < kNucWaves; ++w) total_m += L.red_u64[w];
+    __syncthreads();
+    return total_m;
+  };
 
   // top-k boundary by count (the -inf class when the window holds fewer than k)
   int jk = kWin;
   uint32_t cnt_k = total_c + ninf_n;
-  u64 z_k = total_m;
+  u64 z_k = 0;
+  bool z_k_known = false;  // otherwise z_k is the row's total mass, not yet summed
   if (L.k_active) {
     const uint64_t k = static_cast<uint64_t>(L.k);
     if (static_cast<uint64_t>(total_c) >= k) {
@@ -615,16 +623,21 @@ __device__ __forceinline__ bool support_fast(NucLds& L, int64_t vocab_real, uint
       jk = L.jk;
       cnt_k = L.cnt_k;
       z_k = L.z_k;
+      z_k_known = true;
       __syncthreads();
     }
   }
 
-  // top-p boundary by mass inside the top-k set
-  int kappa = jk;
-  uint32_t cnt_s = cnt_k;
-  u64 z_s = z_k;
-  if (L.p_active) {
-    const u64 P = ceil_mul(L.p, z_k);
+  // top-p boundary by mass inside the top-k set: the first class whose
+  // cumulative mass reaches P = ceil(p * z_k). Scanning for thresholds
+  // p_lo <= P <= p_hi finds classes j_lo <= j* <= j_hi (cumulative masses only
+  // grow), so j_lo == j_hi decides j* exactly. Records the hits in L.kappa /
+  // L.cnt_s / L.z_s (p_lo) and L.kappa_hi (p_hi); -1 when not reached.
+  auto scan_p = [&](u64 p_lo, u64 p_hi) {
+    if (tid == 0) {
+      L.kappa = -1;
+      L.kappa_hi = -1;
+    }
     u64 carry_m = 0;
     uint32_t carry_c = 0;
     for (int r = jtop / kNucThreads; r < kWinPerThread; ++r) {
@@ -636,23 +649,69 @@ __device__ __forceinline__ bool support_fast(NucLds& L, int64_t vocab_real, uint
       u64 im = mj;
       uint32_t rc;
       u64 rm;
-      block_incl_scan(L, ic, im, rc, rm);
+      block_incl_scan(L, ic, im, rc, rm);  // its barriers order the writes above
       ic += carry_c;
       im += carry_m;
-      const bool hit = im >= P && (im - mj) < P && j <= jk;
-      if (hit) {
+      if (im >= p_lo && (im - mj) < p_lo && j <= jk) {
         L.kappa = j;
         L.cnt_s = ic;
         L.z_s = im;
       }
-      if (carry_m + rm >= P) break;  // block-uniform
+      if (im >= p_hi && (im - mj) < p_hi && j <= jk) L.kappa_hi = j;
+      if (carry_m + rm >= p_hi) break;  // block-uniform
       carry_c += rc;
       carry_m += rm;
     }
     __syncthreads();
+  };
+
+  int kappa = jk;
+  uint32_t cnt_s = cnt_k;
+  u64 z_s = z_k;
+  if (L.p_active) {
+    bool decided = false;
+    if (!z_k_known) {
+      // The shard summaries bound the total. Each l_s sums positive float32
+      // terms 2^(x*c - r_s) through at most `depth` roundings (a lane's
+      // vectors plus a partial one, 3 pairwise levels, 6 butterfly levels):
+      // relative error <= depth * 2^-24. A term and the token's integer
+      // weight floor(2^(x*c - R) * 2^40) differ by the rounding of their
+      // exponent arguments (half an ulp of |x*c - r_s| < 100, since a shard
+      // total reaches 2^100 only on the exact-maximum recompute, plus half an
+      // ulp of |x*c - R| <= 42 where the weight is nonzero: < 2^-17 relative),
+      // by v_exp_f32 (about 2^-23 each), by the floor (under one unit per
+      // token on a total of at least 2^39 units) and by terms whose weight
+      // floors to 0 (under 1/4 unit each). The bracket takes twice the sum.
+      const int depth = (shard_width / 8 + kWave) / kWave + 1 + 3 + 6;
+      const double eps = 2.0 * (static_cast<double>(depth) * 0x1p-24 + 0x1p-17 + 0x1p-22 +
+                                1.25 * static_cast<double>(vocab_real) * 0x1p-39);
+      double zf = 0.0;
+#pragma unroll
+      for (int sh = 0; sh < kShards; ++sh) {
+        const float l = L.sm[sh].l;
+        if (l > 0.0f) zf += ldexp(static_cast<double>(l), static_cast<int>(L.sm[sh].r - R) + 40);
+      }
+      const u64 z_lo = static_cast<u64>(zf * (1.0 - eps));
+      const u64 z_hi = static_cast<u64>(zf * (1.0 + eps)) + 1ull;
+      scan_p(ceil_mul(L.p, z_lo), ceil_mul(L.p, z_hi));
+      decided = (L.kappa >= 0) && (L.kappa == L.kappa_hi);  // block-uniform (LDS, after a barrier)
+    }
+    if (!decided) {
+      if (!z_k_known) {
+        z_k = exact_total();
+        z_k_known = true;
+      }
+      const u64 P = ceil_mul(L.p, z_k);
+      scan_p(P, P);
+    }
     kappa = L.kappa;
     cnt_s = L.cnt_s;
     z_s = L.z_s;
+  } else if (!z_k_known) {
+    // top-k keeps every finite token and top-p is off: the support is the
+    // whole vocabulary, whose policy output is the reference output (the
+    // support mass is not used)
+    z_s = 0;
   }
   __syncthreads();
   if (tid == 0) {
@@ -924,7 +983,7 @@ __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restric
     __syncthreads();
   }
   int tclass = 0;
-  const bool fast = support_fast(L, vocab_real, bt, tclass);
+  const bool fast = support_fast(L, vocab_real, shard_width, bt, tclass);
   bool in_support;
   if (!fast) {
     __syncthreads();
