@@ -199,6 +199,7 @@ struct NucLds {
   u64 scan_mass_above;
   union {
     uint32_t win[kWin + 1];  // + trash slot
+    u64 win_pairs[(kWin + 2) / 2];  // the window (and trash slot) as 64-bit pairs, for clearing
     NucGeneral gen;
   } u;
 };
@@ -437,7 +438,7 @@ struct WindowHook {
 
 template <typename Lds>
 __device__ __forceinline__ void window_clear(Lds& L) {
-  for (int i = threadIdx.x; i <= kWin; i += kNucThreads) L.u.win[i] = 0u;
+  for (int i = threadIdx.x; i < (kWin + 2) / 2; i += kNucThreads) L.u.win_pairs[i] = 0ull;
 }
 
 // One pass over the row that fills the window (when the streaming pass did not).
@@ -526,9 +527,18 @@ __device__ __forceinline__ bool support_fast(NucLds& L, int64_t vocab_real, int 
   }
   if (odd) return false;  // block-uniform
 
-  // the row maximum: first non-empty slot (thread t visits t, t + 512, ...)
+  // the row maximum: first non-empty slot (thread t visits t, t + 512, ...).
+  // Every shard summary's m is a token of the row (the maximum of its first
+  // chunk, or of the shard), so the row maximum's slot is at most the slot of
+  // the largest of them: only the rounds up to that slot are read.
+  float mb = -INFINITY;
+#pragma unroll
+  for (int sh = 0; sh < kShards; ++sh) mb = fmaxf(mb, L.sm[sh].m);
+  int r_last = -1;  // block-uniform
+  if (mb > -INFINITY)
+    r_last = min(static_cast<int>(window_slot(__float_as_uint(mb) >> 16)) / kNucThreads, kWinPerThread - 1);
   int jtop = kWin;
-  for (int i = kWinPerThread - 1; i >= 0; --i)
+  for (int i = r_last; i >= 0; --i)
     if (L.u.win[i * kNucThreads + tid]) jtop = i * kNucThreads + tid;
   jtop = wave_min(jtop);
   __syncthreads();  // red_* reads above are complete before reuse
