@@ -221,7 +221,7 @@ def main():
             rlk.logp_nucleus(lgs[i % 2], t, p, k, target, vocab_real=w.vocab_real, groups=args.groups,
                              policy_out=pol, ref_out=ref, workspace=wsn)
 
-        _, ms_n = time_calls(nstep, 10, 2)
+        _, ms_n = time_calls(nstep, 30, 5)
         ab = bytes_nucleus(w.n_rows, w.vocab_real)
         sec.append({"workload": "nucleus: same logits, top-p 0.95, top-k off, T 0.7", "entry_point":
                     "rlk_logp_nucleus", "ms_per_step": ms_n, "tokens_per_s": w.n_rows / (ms_n * 1e-3),
@@ -252,7 +252,7 @@ def main():
         lg_r = (torch.from_numpy(lg_r.view(np.int16)).to(dev),) * 2
         prm = dict(t=torch.from_numpy(wr.temperature).to(dev), p=torch.from_numpy(wr.top_p).to(dev),
                    k=torch.from_numpy(wr.top_k).to(dev), target=torch.from_numpy(tg_r).to(dev))
-        _, ms_r = time_calls(lambda i: nstep(i, lgs=lg_r, **prm), 10, 2)
+        _, ms_r = time_calls(lambda i: nstep(i, lgs=lg_r, **prm), 30, 5)
         sec.append({"workload": "per-request: 64 requests x 128 rows, T {0.7,1.0,1.3}, top-p {0.95,0.99}, "
                     "top-k {-1,128}", "entry_point": "rlk_logp_nucleus", "ms_per_step": ms_r,
                     "tokens_per_s": wr.n_rows / (ms_r * 1e-3), "achieved_GBs": ab / (ms_r * 1e-3) / 1e9,
