@@ -273,8 +273,10 @@ __device__ __forceinline__ void pass_chunk(const u32x4* __restrict__ base, int f
 // lane consumes its vectors in the same order and the reference comes from
 // the same group in both cases, so the sums are identical. Under such a hook
 // the chunks whose vectors are all in range load without bounds checks, and
-// after the chunk that fixed the reference they skip its check; the chunk
-// boundaries and the order of the terms are the same as in the guarded loop.
+// after the chunk that fixed the reference they skip its check; the vectors
+// after the last whole chunk go one per lane at a time once the reference is
+// set. The order of the terms in each accumulator is the same as in the
+// guarded loop.
 template <int U, typename Hook = NoHook>
 __device__ __forceinline__ void shard_pass(const u32x4* __restrict__ base, int nfull, int tail, int lane,
                                            float c, ShardAcc& st, Hook& hook) {
@@ -296,6 +298,19 @@ __device__ __forceinline__ void shard_pass(const u32x4* __restrict__ base, int n
 #pragma unroll
       for (int u = 0; u < kU; ++u) v[u] = __builtin_nontemporal_load(base + first + u * kWave + lane);
       st.template consume_late<kU, false, true>(v, c, hook, unused);
+    }
+    if (st.have_ref) {
+      // The rest of the vectors, one per lane at a time. With the reference
+      // set, the chunk grouping no longer matters: every accumulator still
+      // takes its lane's vectors in order, and the guarded chunk would only
+      // have added exact zeros for the missing ones.
+      const int one[1] = {0};
+      for (; first < nfull; first += kWave) {
+        if (first + lane < nfull) {
+          const u32x4 v[1] = {__builtin_nontemporal_load(base + first + lane)};
+          st.template consume_late<1, false, true>(v, c, hook, one);
+        }
+      }
     }
   }
   for (; first < nfull; first += kU * kWave) pass_chunk<kU>(base, first, nfull, lane, c, st, hook);
