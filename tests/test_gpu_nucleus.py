@@ -133,6 +133,32 @@ def test_tied_classes_without_zero():
     check(logits, vr, temps, top_p, top_k, targets, "ties without zero")
 
 
+def test_top_p_near_one_and_bracket_edges():
+    """Top-p values just below 1 (the upper end of the bracket the kernel puts
+    around a row's total mass can exceed the total, so the exact total must be
+    summed), a tiny top-p (the argmax class) and mid values, with top-k off, on
+    rows of 8 shards of 2400 columns (several 512-slot scan rounds) and the
+    benchmark's value distribution, with and without a spike."""
+    say("case: top-p near 1 and bracket edges")
+    vp, vr = 19200, 19137
+    n = 48
+    rng = np.random.default_rng(71)
+    logits = np.full((n, vp), datagen.BF16_NEG_INF, dtype=np.uint16)
+    for i in range(n):
+        bits, _, _ = datagen.row_values((71, i), vr, 2.5, 8.0 if i % 2 else None)
+        logits[i, :vr] = bits
+    p_vals = np.array([np.nextafter(np.float32(1), np.float32(0)), 1 - 2.0 ** -20, 0.9999, 0.999, 0.99, 0.95,
+                       0.5, 1e-7], dtype=np.float32)
+    top_p = p_vals[np.arange(n) % len(p_vals)]
+    temps = np.array([0.7, 1.3, 1.0], dtype=np.float32)[(np.arange(n) // len(p_vals)) % 3]
+    top_k = np.full(n, -1, dtype=np.int32)
+    targets = support_targets(logits, vr, temps, top_p, top_k, 72)
+    check(logits, vr, temps, top_p, top_k, targets, "top-p near 1", groups_list=(1, 8))
+    # targets just outside the support of the rows whose support is not everything
+    targets = rng.integers(0, vr, size=n).astype(np.int64)
+    check(logits, vr, temps, top_p, top_k, targets, "top-p near 1, uniform targets", groups_list=(1, 8))
+
+
 # BF16 patterns at and just past the ends of the value ranges a 16-bit rank
 # window can cover: the top (65536 and the next value), the smallest
 # magnitudes (2^-24 and the next smaller value, both signs) and two pairs of
