@@ -182,12 +182,10 @@ struct NucLds {
   u64 red_u64[kNucWaves];
   int red_flag[kNucWaves];
   // search results
-  int fast_ok;
   int jk;            // fast: class index of the top-k boundary; general: key inside bk
   uint32_t cnt_k;    // cumulative count through the top-k boundary
   u64 z_k;           // mass of the top-k set
   int kappa;         // support: fast = last kept class index, general = smallest kept key
-  int kappa_hi;      // fast: class reached by the upper threshold of a bracketed top-p scan
   uint32_t cnt_s;
   u64 z_s;
   // general path scan state
@@ -197,7 +195,7 @@ struct NucLds {
   int scan_bin;
   uint32_t scan_cnt_above;
   u64 scan_mass_above;
-  union {
+  union alignas(16) {
     uint32_t win[kWin + 1];  // + trash slot
     u64 win_pairs[(kWin + 2) / 2];  // the window (and trash slot) as 64-bit pairs, for clearing
     NucGeneral gen;
@@ -478,123 +476,154 @@ __device__ __forceinline__ int wave_min(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Block-wide inclusive scan of (count, mass) over the 512 threads, in thread
-// order; returns the block totals through tot_c / tot_m. Uses L.red_* (two
-// barriers inside).
-__device__ __forceinline__ void block_incl_scan(NucLds& L, uint32_t& c, u64& m, uint32_t& tot_c, u64& tot_m) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x / kWave;
-  c = wave_incl_scan<uint32_t>(c, lane);
-  m = wave_incl_scan<u64>(m, lane);
-  if (lane == kWave - 1) {
-    L.red_u32[wv][0] = c;
-    L.red_u64[wv] = m;
-  }
-  __syncthreads();
-  tot_c = 0;
-  tot_m = 0;
-  for (int w = 0; w < kNucWaves; ++w) {
-    const uint32_t wc = L.red_u32[w][0];
-    const u64 wm = L.red_u64[w];
-    if (w < wv) {
-      c += wc;
-      m += wm;
-    }
-    tot_c += wc;
-    tot_m += wm;
-  }
-  __syncthreads();
+// ---------------------------------------------------------------------------
+// Fast path, in one wavefront (no block barriers), for a row whose every real
+// token is in the window or is -inf (the hook totals say so). The row maximum
+// is the top non-empty slot, R = ceil(fl32(M*c)), and a class (slot) weighs
+// count * floor(2^(x*c - R) * 2^40): exactly the integers the general path
+// sums per token. Scans from the top find the top-k boundary (count >= k)
+// and then the top-p boundary (cumulative mass >= ceil(p * Z_k), an exact
+// integer test). Lane l reads the window four slots at a time (slots 4q ..
+// 4q+3, q = q0 + l), so a round covers 256 consecutive slots; prefix sums
+// come from a lane-local scan of its four slots plus a DPP scan of the lane
+// totals, and a crossing is located with a ballot. Every value it returns is
+// wave-uniform.
+// ---------------------------------------------------------------------------
+struct FastSupport {
+  float R;
+  int kappa;       // last kept class (window slot), or kWin for the -inf class
+  uint32_t cnt_s;  // tokens in the support
+  u64 z_s;         // support mass (2^-40 units relative to 2^R)
+};
+
+constexpr int kWinQuads = kWin / 4;
+
+__device__ __forceinline__ void window_quad(const NucLds& L, int q, uint32_t (&cnt)[4]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(&L.u.win[4 * q]);
+  cnt[0] = v.x;
+  cnt[1] = v.y;
+  cnt[2] = v.z;
+  cnt[3] = v.w;
 }
 
-// ---------------------------------------------------------------------------
-// Fast path on a filled window (L.red_* hold the hook totals). Returns
-// (block-uniformly) whether it decided the support; on success L.R is set,
-// L.kappa is the last kept class (window slot, or kWin for the -inf class),
-// L.cnt_s / L.z_s the support's count and mass, and thread 0's `tclass` the
-// target's class.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ bool support_fast(NucLds& L, int64_t vocab_real, int shard_width, uint32_t bt, int& tclass) {
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;
-  const float c = L.c;
+__device__ __forceinline__ u64 readlane_u64(u64 v, int l) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), l));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), l));
+  return (static_cast<u64>(hi) << 32) | lo;
+}
 
-  uint32_t ninf_n = 0;
-  bool odd = false;
-  for (int w = 0; w < kNucWaves; ++w) {
-    ninf_n += L.red_u32[w][1];
-    odd |= (L.red_flag[w] != 0);
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int l) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+}
+
+// One round of 64 quads from quad q0: per-slot counts and masses, and the
+// inclusive cumulative count and mass of each slot counted from the round's
+// first slot (lane-local prefix plus the exclusive DPP scan of the lanes).
+// Returns the round's totals through rc / rm.
+struct QuadRound {
+  uint32_t cnt[4];
+  u64 mass[4];
+  uint32_t cum_c[4];
+  u64 cum_m[4];
+};
+
+__device__ __forceinline__ void quad_round(const NucLds& L, int q0, float c, float nr, QuadRound& Q, uint32_t& rc,
+                                           u64& rm) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int q = q0 + lane;
+  if (q < kWinQuads) {
+    window_quad(L, q, Q.cnt);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Q.cnt[e] = 0u;
   }
-  if (odd) return false;  // block-uniform
+  uint32_t pc = 0;
+  u64 pm = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    u64 m = 0;
+    if (Q.cnt[e]) {
+      const int j = 4 * q + e;
+      const float t = fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(j)) << 16), c, nr);
+      if (t >= -42.0f) m = static_cast<u64>(Q.cnt[e]) * fixed40(__builtin_amdgcn_exp2f(t));
+    }
+    Q.mass[e] = m;
+    pc += Q.cnt[e];
+    pm += m;
+    Q.cum_c[e] = pc;
+    Q.cum_m[e] = pm;
+  }
+  const uint32_t ic = wave_incl_scan<uint32_t>(pc, lane);
+  const u64 im = wave_incl_scan<u64>(pm, lane);
+  const uint32_t ec = ic - pc;
+  const u64 em = im - pm;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    Q.cum_c[e] += ec;
+    Q.cum_m[e] += em;
+  }
+  rc = readlane_u32(ic, kWave - 1);
+  rm = readlane_u64(im, kWave - 1);
+}
 
-  // the row maximum: first non-empty slot (thread t visits t, t + 512, ...).
-  // Every shard summary's m is a token of the row (the maximum of its first
-  // chunk, or of the shard), so the row maximum's slot is at most the slot of
-  // the largest of them: only the rounds up to that slot are read.
+__device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_t vocab_real, int shard_width,
+                                                         bool k_active, int64_t k_in, bool p_active, float p,
+                                                         float c) {
+  const int lane = threadIdx.x & (kWave - 1);
+  FastSupport out;
+  uint32_t ninf_n = 0;
+  for (int w = 0; w < kNucWaves; ++w) ninf_n += L.red_u32[w][1];
+  const uint32_t total_c = static_cast<uint32_t>(vocab_real) - ninf_n;
+
+  // the row maximum: the first non-empty slot, at most the slot of the
+  // largest shard-summary m (each is a token of the row)
   float mb = -INFINITY;
 #pragma unroll
   for (int sh = 0; sh < kShards; ++sh) mb = fmaxf(mb, L.sm[sh].m);
-  int r_last = -1;  // block-uniform
-  if (mb > -INFINITY)
-    r_last = min(static_cast<int>(window_slot(__float_as_uint(mb) >> 16)) / kNucThreads, kWinPerThread - 1);
   int jtop = kWin;
-  for (int i = r_last; i >= 0; --i)
-    if (L.u.win[i * kNucThreads + tid]) jtop = i * kNucThreads + tid;
-  jtop = wave_min(jtop);
-  __syncthreads();  // red_* reads above are complete before reuse
-  if (lane == 0) L.red_u32[wv][0] = static_cast<uint32_t>(jtop);
-  __syncthreads();
-  jtop = kWin;
-  for (int w = 0; w < kNucWaves; ++w) jtop = min(jtop, static_cast<int>(L.red_u32[w][0]));
-  if (jtop == kWin) return false;  // no finite token (cannot happen on a searched row)
+  if (mb > -INFINITY) {
+    const int qb = min(static_cast<int>(window_slot(__float_as_uint(mb) >> 16)), kWin - 1) / 4;
+    for (int q0 = 0; q0 <= qb; q0 += kWave) {
+      const int q = q0 + lane;
+      int j = kWin;
+      if (q <= qb) {
+        uint32_t cnt[4];
+        window_quad(L, q, cnt);
+#pragma unroll
+        for (int e = 3; e >= 0; --e)
+          if (cnt[e]) j = 4 * q + e;
+      }
+      jtop = wave_min(j);
+      if (jtop < kWin) break;  // wave-uniform
+    }
+  }
+  out.kappa = kWin;
+  out.cnt_s = total_c + ninf_n;
+  out.z_s = 0;
+  out.R = 0.0f;
+  if (jtop == kWin) return out;  // no finite token: not reached on a searched row
   const float m = __uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(jtop)) << 16);
   const float R = ref_exponent(m, c);
   const float nr = -R;
+  out.R = R;
+  const int qfirst = jtop / 4;
 
-  // count and mass of class (slot) j; a term below 2^-42 is 0 in 2^-40 fixed point
-  auto class_at = [&](int j, uint32_t& cj, u64& mj) {
-    cj = L.u.win[j];
-    mj = 0;
-    if (cj) {
-      const float t = fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(j)) << 16), c, nr);
-      if (t >= -42.0f) mj = static_cast<u64>(cj) * fixed40(__builtin_amdgcn_exp2f(t));
-    }
-  };
-
-  const uint32_t total_c = static_cast<uint32_t>(vocab_real) - ninf_n;
-
-  // Exact total mass of the row (block-uniform result), computed only when a
-  // decision needs it. Every real token is in the window or is -inf; masses
-  // are summed in 512-slot rounds from the top and stop once a round starts
-  // below 2^-42 (slots are in decreasing value order, so every later term is 0).
+  // exact total mass: every slot with a nonzero weight lies before the first
+  // quad whose first slot is below 2^-42 (slots are in decreasing value order)
   auto exact_total = [&]() -> u64 {
-    const int r_first = jtop / kNucThreads;
-    int r_end = r_first + 1;  // block-uniform: rounds [r_first, r_end) can hold mass
-    while (r_end < kWinPerThread &&
-           !(fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(r_end * kNucThreads)) << 16), c, nr) <
-             -42.0f))
-      ++r_end;
-    uint32_t cnt[kWinPerThread];
-#pragma unroll
-    for (int r = 0; r < kWinPerThread; ++r)
-      cnt[r] = (r >= r_first && r < r_end) ? L.u.win[r * kNucThreads + tid] : 0u;
     u64 tm = 0;
-#pragma unroll
-    for (int r = 0; r < kWinPerThread; ++r) {
-      if (cnt[r]) {
-        const int j = r * kNucThreads + tid;
-        const float t = fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(j)) << 16), c, nr);
-        if (t >= -42.0f) tm += static_cast<u64>(cnt[r]) * fixed40(__builtin_amdgcn_exp2f(t));
-      }
+    for (int q0 = qfirst; q0 < kWinQuads; q0 += kWave) {
+      const int q0s = 4 * q0;
+      if (q0 > qfirst &&
+          fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(q0s)) << 16), c, nr) < -42.0f)
+        break;  // wave-uniform
+      QuadRound Q;
+      uint32_t rc;
+      u64 rm;
+      quad_round(L, q0, c, nr, Q, rc, rm);
+      tm += rm;
     }
-    tm = wave_total(tm);
-    __syncthreads();
-    if (lane == 0) L.red_u64[wv] = tm;
-    __syncthreads();
-    u64 total_m = 0;
-    for (int w = 0; w < kNucWaves; ++w) total_m += L.red_u64[w];
-    __syncthreads();
-    return total_m;
+    return tm;
   };
 
   // top-k boundary by count (the -inf class when the window holds fewer than k)
@@ -602,83 +631,104 @@ __device__ __forceinline__ bool support_fast(NucLds& L, int64_t vocab_real, int 
   uint32_t cnt_k = total_c + ninf_n;
   u64 z_k = 0;
   bool z_k_known = false;  // otherwise z_k is the row's total mass, not yet summed
-  if (L.k_active) {
-    const uint64_t k = static_cast<uint64_t>(L.k);
-    if (static_cast<uint64_t>(total_c) >= k) {
-      uint32_t carry_c = 0;
-      u64 carry_m = 0;
-      for (int r = jtop / kNucThreads; r < kWinPerThread; ++r) {  // rounds of 512 slots, from the top
-        const int j = r * kNucThreads + tid;
-        uint32_t cj;
-        u64 mj;
-        class_at(j, cj, mj);
-        uint32_t ic = cj;
-        u64 im = mj;
-        uint32_t rc;
-        u64 rm;
-        block_incl_scan(L, ic, im, rc, rm);
-        ic += carry_c;
-        im += carry_m;
-        const bool hit = static_cast<uint64_t>(ic) >= k && static_cast<uint64_t>(ic - cj) < k;
-        if (hit) {
-          L.jk = j;
-          L.cnt_k = ic;
-          L.z_k = im;
-        }
-        if (static_cast<uint64_t>(carry_c + rc) >= k) break;  // block-uniform
-        carry_c += rc;
-        carry_m += rm;
+  if (k_active && static_cast<uint64_t>(total_c) >= static_cast<uint64_t>(k_in)) {
+    const uint64_t k = static_cast<uint64_t>(k_in);
+    uint32_t carry_c = 0;
+    u64 carry_m = 0;
+    for (int q0 = qfirst; q0 < kWinQuads; q0 += kWave) {
+      QuadRound Q;
+      uint32_t rc;
+      u64 rm;
+      quad_round(L, q0, c, nr, Q, rc, rm);
+      int hit_e = -1;
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        const uint64_t cum = carry_c + Q.cum_c[e];
+        if (cum >= k && cum - Q.cnt[e] < k) hit_e = e;
       }
-      __syncthreads();
-      jk = L.jk;
-      cnt_k = L.cnt_k;
-      z_k = L.z_k;
-      z_k_known = true;
-      __syncthreads();
+      const u64 ball = __ballot(hit_e >= 0);
+      if (ball) {  // wave-uniform
+        const int hl = __builtin_ctzll(ball);
+        const int he = __builtin_amdgcn_readlane(hit_e, hl);
+        uint32_t hc = 0;
+        u64 hm = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e == he) {
+            hc = Q.cum_c[e];
+            hm = Q.cum_m[e];
+          }
+        jk = 4 * (q0 + hl) + he;
+        cnt_k = carry_c + readlane_u32(hc, hl);
+        z_k = carry_m + readlane_u64(hm, hl);
+        z_k_known = true;
+        break;
+      }
+      carry_c += rc;
+      carry_m += rm;
     }
   }
 
   // top-p boundary by mass inside the top-k set: the first class whose
   // cumulative mass reaches P = ceil(p * z_k). Scanning for thresholds
   // p_lo <= P <= p_hi finds classes j_lo <= j* <= j_hi (cumulative masses only
-  // grow), so j_lo == j_hi decides j* exactly. Records the hits in L.kappa /
-  // L.cnt_s / L.z_s (p_lo) and L.kappa_hi (p_hi); -1 when not reached.
-  auto scan_p = [&](u64 p_lo, u64 p_hi) {
-    if (tid == 0) {
-      L.kappa = -1;
-      L.kappa_hi = -1;
-    }
-    u64 carry_m = 0;
+  // grow), so j_lo == j_hi decides j* exactly.
+  struct Hit {
+    int j;
+    uint32_t cnt;
+    u64 mass;
+  };
+  auto scan_p = [&](u64 p_lo, u64 p_hi, Hit& lo, int& j_hi) {
+    lo.j = -1;
+    j_hi = -1;
     uint32_t carry_c = 0;
-    for (int r = jtop / kNucThreads; r < kWinPerThread; ++r) {
-      const int j = r * kNucThreads + tid;
-      uint32_t cj;
-      u64 mj;
-      class_at(j, cj, mj);
-      uint32_t ic = cj;
-      u64 im = mj;
+    u64 carry_m = 0;
+    for (int q0 = qfirst; q0 < kWinQuads; q0 += kWave) {
+      QuadRound Q;
       uint32_t rc;
       u64 rm;
-      block_incl_scan(L, ic, im, rc, rm);  // its barriers order the writes above
-      ic += carry_c;
-      im += carry_m;
-      if (im >= p_lo && (im - mj) < p_lo && j <= jk) {
-        L.kappa = j;
-        L.cnt_s = ic;
-        L.z_s = im;
+      quad_round(L, q0, c, nr, Q, rc, rm);
+      int e_lo = -1, e_hi = -1;
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        const u64 cum = carry_m + Q.cum_m[e];
+        const bool inside = 4 * (q0 + lane) + e <= jk;
+        if (inside && cum >= p_lo && cum - Q.mass[e] < p_lo) e_lo = e;
+        if (inside && cum >= p_hi && cum - Q.mass[e] < p_hi) e_hi = e;
       }
-      if (im >= p_hi && (im - mj) < p_hi && j <= jk) L.kappa_hi = j;
-      if (carry_m + rm >= p_hi) break;  // block-uniform
+      const u64 b_lo = __ballot(e_lo >= 0);
+      if (b_lo && lo.j < 0) {  // wave-uniform
+        const int hl = __builtin_ctzll(b_lo);
+        const int he = __builtin_amdgcn_readlane(e_lo, hl);
+        uint32_t hc = 0;
+        u64 hm = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e == he) {
+            hc = Q.cum_c[e];
+            hm = Q.cum_m[e];
+          }
+        lo.j = 4 * (q0 + hl) + he;
+        lo.cnt = carry_c + readlane_u32(hc, hl);
+        lo.mass = carry_m + readlane_u64(hm, hl);
+      }
+      const u64 b_hi = __ballot(e_hi >= 0);
+      if (b_hi) {  // wave-uniform
+        const int hl = __builtin_ctzll(b_hi);
+        j_hi = 4 * (q0 + hl) + __builtin_amdgcn_readlane(e_hi, hl);
+        break;
+      }
       carry_c += rc;
       carry_m += rm;
     }
-    __syncthreads();
   };
 
   int kappa = jk;
   uint32_t cnt_s = cnt_k;
   u64 z_s = z_k;
-  if (L.p_active) {
+  if (p_active) {
+    Hit lo;
+    int j_hi = -1;
     bool decided = false;
     if (!z_k_known) {
       // The shard summaries bound the total. Each l_s sums positive float32
@@ -703,36 +753,27 @@ __device__ __forceinline__ bool support_fast(NucLds& L, int64_t vocab_real, int 
       }
       const u64 z_lo = static_cast<u64>(zf * (1.0 - eps));
       const u64 z_hi = static_cast<u64>(zf * (1.0 + eps)) + 1ull;
-      scan_p(ceil_mul(L.p, z_lo), ceil_mul(L.p, z_hi));
-      decided = (L.kappa >= 0) && (L.kappa == L.kappa_hi);  // block-uniform (LDS, after a barrier)
+      scan_p(ceil_mul(p, z_lo), ceil_mul(p, z_hi), lo, j_hi);
+      decided = (lo.j >= 0) && (lo.j == j_hi);
     }
     if (!decided) {
       if (!z_k_known) {
         z_k = exact_total();
         z_k_known = true;
       }
-      const u64 P = ceil_mul(L.p, z_k);
-      scan_p(P, P);
+      const u64 P = ceil_mul(p, z_k);
+      scan_p(P, P, lo, j_hi);
     }
-    kappa = L.kappa;
-    cnt_s = L.cnt_s;
-    z_s = L.z_s;
-  } else if (!z_k_known) {
-    // top-k keeps every finite token and top-p is off: the support is the
-    // whole vocabulary, whose policy output is the reference output (the
-    // support mass is not used)
-    z_s = 0;
+    kappa = lo.j;
+    cnt_s = lo.cnt;
+    z_s = lo.mass;
   }
-  __syncthreads();
-  if (tid == 0) {
-    L.R = R;
-    L.kappa = kappa;
-    L.cnt_s = cnt_s;
-    L.z_s = z_s;
-    tclass = (bt == kNegInfBits) ? kWin : static_cast<int>(window_slot(bt));
-  }
-  __syncthreads();
-  return true;
+  // (top-p off and top-k keeping every finite token: the support is the whole
+  // vocabulary, whose policy output is the reference output; z_s is unused)
+  out.kappa = kappa;
+  out.cnt_s = cnt_s;
+  out.z_s = z_s;
+  return out;
 }
 
 // ---------------------------------------------------------------------------
@@ -930,9 +971,119 @@ __device__ __forceinline__ bool search_needed(float t, float p, int64_t k, int64
 }
 
 // ---------------------------------------------------------------------------
-// Whole-row driver: L.sm must hold the row's 8 shard summaries; when
-// `window_built` the window and the hook totals are already filled (the
-// streaming pass counted the row). Writes ref_out[row], policy_out[row] and,
+// Row drivers.
+// ---------------------------------------------------------------------------
+
+// Merge of the row's summaries and what it decides: the reference logprob,
+// the target's BF16 bits, and whether the row needs a support search
+// (status 0), takes the reference as its policy (1), or is invalid (-1: top-p
+// or top-k out of range; -2: the reference itself failed).
+struct RowStart {
+  float ref;
+  float lse;
+  uint32_t bt;
+  int status;
+};
+
+__device__ __forceinline__ RowStart row_start(const ShardSummary* __restrict__ sm, int64_t vocab_real,
+                                              int shard_width, float t, float p, int64_t k, int64_t tg) {
+  RowStart rs;
+  const bool tok = (tg >= 0) && (tg < vocab_real);
+  const RowMerge mr = merge_row(sm, t, tok, tg, shard_width);
+  rs.bt = 0;
+  // the target's BF16 bits ride in its shard's summary (a searched row has
+  // T > 0 and a successful merge, so that summary reported them)
+  if (tok && mr.ok && t > 0.0f) rs.bt = static_cast<uint32_t>(sm[tg / shard_width].aux) & 0xFFFFu;
+  rs.ref = mr.logp;
+  rs.lse = mr.lse;
+  const bool p_ok = (p > 0.0f) && (p <= 1.0f);
+  const bool k_ok = (k == -1) || (k >= 1 && k <= vocab_real);
+  if (!mr.ok) {
+    rs.status = -2;
+  } else if (!p_ok || !k_ok) {
+    rs.status = -1;
+  } else {
+    rs.status = search_needed(t, p, k, vocab_real) ? 0 : 1;
+  }
+  return rs;
+}
+
+// Outputs of a row that needs no search (status != 0).
+__device__ __forceinline__ void write_unsearched(int64_t row, const RowStart& rs, float* __restrict__ policy_out,
+                                                 rlk_support_state* __restrict__ state_out) {
+  rlk_support_state st;
+  st.lse_support = rs.lse;
+  st.threshold = -INFINITY;
+  st.status = (rs.status == 1) ? 1 : rs.status;
+  st.reserved = 0;
+  policy_out[row] = (rs.status == 1) ? rs.ref : NAN;
+  if (state_out) state_out[row] = st;
+}
+
+// Policy logprob and support record of a searched row. `fast`: kappa is a
+// window slot (kWin = the -inf class); otherwise a key16 (general path).
+__device__ __forceinline__ void write_policy(int64_t row, int64_t vocab_real, bool fast, int kappa, uint32_t cnt_s,
+                                             u64 z_s, float R, const RowStart& rs, float t,
+                                             float* __restrict__ policy_out, rlk_support_state* __restrict__ state_out) {
+  const uint32_t bt = rs.bt;
+  const int tclass = (bt == kNegInfBits) ? kWin : static_cast<int>(window_slot(bt));
+  const bool in_support = fast ? (tclass <= kappa) : (static_cast<int>(key16(bt)) >= kappa);
+  const float zt = __uint_as_float(bt << 16) / t;  // IEEE float32 division
+  const bool whole = static_cast<int64_t>(cnt_s) == vocab_real;
+  const double lse_s = (static_cast<double>(R) + (log2(static_cast<double>(z_s)) - 40.0)) * kLn2;
+  float pol;
+  if (!in_support) {
+    pol = -INFINITY;
+  } else if (whole) {
+    pol = rs.ref;
+  } else {
+    pol = static_cast<float>(static_cast<double>(zt) - lse_s);
+  }
+  policy_out[row] = pol;
+  if (state_out) {
+    rlk_support_state st;
+    st.lse_support = whole ? rs.lse : static_cast<float>(lse_s);
+    st.threshold = whole ? -INFINITY
+                         : (fast ? (kappa >= kWin ? -INFINITY : slot_value(kappa))
+                                 : key_value(static_cast<uint32_t>(kappa)));
+    st.status = in_support ? 1 : 0;
+    st.reserved = 0;
+    state_out[row] = st;
+  }
+}
+
+// Whole row in wavefront 0 alone, for a row whose window is complete (every
+// real token in the window or -inf) or that needs no search: no block
+// barriers, so the other wavefronts of the workgroup may already have ended.
+// Every lane computes the same merge; lane 0 writes.
+__device__ __forceinline__ void nucleus_row_wave(const NucLds& L, int64_t row, int64_t vocab_real, int shard_width,
+                                                 float t, float p, int64_t k, int64_t tg,
+                                                 float* __restrict__ policy_out, float* __restrict__ ref_out,
+                                                 float* __restrict__ lse_out,
+                                                 rlk_support_state* __restrict__ state_out) {
+  const bool lead = (threadIdx.x == 0);
+  const RowStart rs = row_start(L.sm, vocab_real, shard_width, t, p, k, tg);
+  if (lead) {
+    ref_out[row] = rs.ref;
+    if (lse_out) lse_out[row] = rs.lse;
+  }
+  if (rs.status != 0) {
+    if (lead) write_unsearched(row, rs, policy_out, state_out);
+    return;
+  }
+  const bool k_active = (k != -1) && (k < vocab_real);
+  const bool p_active = (p < 1.0f);
+  const FastSupport fs = support_fast_wave(L, vocab_real, shard_width, k_active, k, p_active, p, kLog2e / t);
+  if (lead) write_policy(row, vocab_real, true, fs.kappa, fs.cnt_s, fs.z_s, fs.R, rs, t, policy_out, state_out);
+}
+
+// ---------------------------------------------------------------------------
+// Whole-row driver for all threads of the block: L.sm must hold the row's 8
+// shard summaries; when `window_built` the window and the hook totals are
+// already filled (the streaming pass counted the row). After the window is
+// complete, a row whose tokens all lie in it continues in wavefront 0 alone
+// (support_fast_wave; the other wavefronts return); other rows take the
+// general path with the whole block. Writes ref_out[row], policy_out[row] and,
 // when given, lse_out[row] and state_out[row].
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restrict__ rowp, int64_t row,
@@ -941,46 +1092,24 @@ __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restric
                                             float* __restrict__ ref_out, float* __restrict__ lse_out,
                                             rlk_support_state* __restrict__ state_out) {
   const int tid = threadIdx.x;
-  float ref = NAN, zt = NAN, lse = NAN;
-  uint32_t bt = 0;
+  RowStart rs;
+  rs.ref = NAN;
+  rs.lse = NAN;
+  rs.bt = 0;
+  rs.status = -2;
   if (tid == 0) {
-    const bool tok = (tg >= 0) && (tg < vocab_real);
-    const RowMerge mr = merge_row(L.sm, t, tok, tg, shard_width);
-    // the target's BF16 bits ride in its shard's summary (a searched row has
-    // T > 0 and a successful merge, so that summary reported them)
-    if (tok && mr.ok && t > 0.0f) bt = static_cast<uint32_t>(L.sm[tg / shard_width].aux) & 0xFFFFu;
-    const float xt = __uint_as_float(bt << 16);
-    ref = mr.logp;
-    lse = mr.lse;
-    ref_out[row] = ref;
-    if (lse_out) lse_out[row] = lse;
-    const bool p_ok = (p > 0.0f) && (p <= 1.0f);
-    const bool k_ok = (k == -1) || (k >= 1 && k <= vocab_real);
-    L.search = 0;
-    float pol = ref;
-    rlk_support_state st;
-    st.lse_support = lse;
-    st.threshold = -INFINITY;
-    st.status = 1;
-    st.reserved = 0;
-    if (!mr.ok) {
-      pol = NAN;
-      st.status = -2;
-    } else if (!p_ok || !k_ok) {
-      pol = NAN;
-      st.status = -1;
-    } else if (search_needed(t, p, k, vocab_real)) {
-      L.search = 1;
+    rs = row_start(L.sm, vocab_real, shard_width, t, p, k, tg);
+    ref_out[row] = rs.ref;
+    if (lse_out) lse_out[row] = rs.lse;
+    L.search = (rs.status == 0);
+    if (rs.status == 0) {
       L.k_active = (k != -1) && (k < vocab_real);
       L.p_active = (p < 1.0f);
       L.k = k;
       L.p = p;
       L.c = kLog2e / t;
-      zt = xt / t;
-    }
-    if (!L.search) {
-      policy_out[row] = pol;
-      if (state_out) state_out[row] = st;
+    } else {
+      write_unsearched(row, rs, policy_out, state_out);
     }
   }
   __syncthreads();
@@ -992,39 +1121,18 @@ __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restric
     window_pass(L, rowp, vocab_real);
     __syncthreads();
   }
-  int tclass = 0;
-  const bool fast = support_fast(L, vocab_real, shard_width, bt, tclass);
-  bool in_support;
-  if (!fast) {
-    __syncthreads();
-    support_general(L, rowp, vocab_real);
-    in_support = (tid == 0) && static_cast<int>(key16(bt)) >= L.kappa;
-  } else {
-    in_support = (tid == 0) && tclass <= L.kappa;
+  bool odd = false;  // block-uniform: a real token outside the window
+  for (int w = 0; w < kNucWaves; ++w) odd |= (L.red_flag[w] != 0);
+  if (!odd) {
+    if (tid >= kWave) return;
+    const FastSupport fs =
+        support_fast_wave(L, vocab_real, shard_width, L.k_active != 0, L.k, L.p_active != 0, L.p, L.c);
+    if (tid == 0) write_policy(row, vocab_real, true, fs.kappa, fs.cnt_s, fs.z_s, fs.R, rs, t, policy_out, state_out);
+    return;
   }
-  if (tid == 0) {
-    const bool whole = static_cast<int64_t>(L.cnt_s) == vocab_real;
-    const double lse_s = (static_cast<double>(L.R) + (log2(static_cast<double>(L.z_s)) - 40.0)) * kLn2;
-    float pol;
-    if (!in_support) {
-      pol = -INFINITY;
-    } else if (whole) {
-      pol = ref;
-    } else {
-      pol = static_cast<float>(static_cast<double>(zt) - lse_s);
-    }
-    policy_out[row] = pol;
-    if (state_out) {
-      rlk_support_state st;
-      st.lse_support = whole ? lse : static_cast<float>(lse_s);
-      st.threshold = whole ? -INFINITY
-                           : (fast ? (L.kappa >= kWin ? -INFINITY : slot_value(L.kappa))
-                                   : key_value(static_cast<uint32_t>(L.kappa)));
-      st.status = in_support ? 1 : 0;
-      st.reserved = 0;
-      state_out[row] = st;
-    }
-  }
+  __syncthreads();  // the flags above are read before the general path reuses the block scratch
+  support_general(L, rowp, vocab_real);
+  if (tid == 0) write_policy(row, vocab_real, false, L.kappa, L.cnt_s, L.z_s, L.R, rs, t, policy_out, state_out);
 }
 
 }  // namespace rlk
