@@ -519,7 +519,8 @@ __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int l) {
 // One round of 64 quads from quad q0: per-slot counts and masses, and the
 // inclusive cumulative count and mass of each slot counted from the round's
 // first slot (lane-local prefix plus the exclusive DPP scan of the lanes).
-// Returns the round's totals through rc / rm.
+// Returns the round's totals through rc / rm, and false (wave-uniform, with
+// zero totals and Q left unset) when all 256 slots are empty.
 struct QuadRound {
   uint32_t cnt[4];
   u64 mass[4];
@@ -527,7 +528,7 @@ struct QuadRound {
   u64 cum_m[4];
 };
 
-__device__ __forceinline__ void quad_round(const NucLds& L, int q0, float c, float nr, QuadRound& Q, uint32_t& rc,
+__device__ __forceinline__ bool quad_round(const NucLds& L, int q0, float c, float nr, QuadRound& Q, uint32_t& rc,
                                            u64& rm) {
   const int lane = threadIdx.x & (kWave - 1);
   const int q = q0 + lane;
@@ -536,6 +537,11 @@ __device__ __forceinline__ void quad_round(const NucLds& L, int q0, float c, flo
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) Q.cnt[e] = 0u;
+  }
+  if (__ballot((Q.cnt[0] | Q.cnt[1] | Q.cnt[2] | Q.cnt[3]) != 0u) == 0ull) {  // wave-uniform
+    rc = 0u;
+    rm = 0ull;
+    return false;
   }
   uint32_t pc = 0;
   u64 pm = 0;
@@ -564,6 +570,7 @@ __device__ __forceinline__ void quad_round(const NucLds& L, int q0, float c, flo
   }
   rc = readlane_u32(ic, kWave - 1);
   rm = readlane_u64(im, kWave - 1);
+  return true;
 }
 
 __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_t vocab_real, int shard_width,
@@ -608,11 +615,12 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
   out.R = R;
   const int qfirst = jtop / 4;
 
-  // exact total mass: every slot with a nonzero weight lies before the first
-  // quad whose first slot is below 2^-42 (slots are in decreasing value order)
-  auto exact_total = [&]() -> u64 {
+  // exact mass of the slots from quad q_start on: every slot with a nonzero
+  // weight lies before the first quad whose first slot is below 2^-42 (slots
+  // are in decreasing value order)
+  auto exact_mass_from = [&](int q_start) -> u64 {
     u64 tm = 0;
-    for (int q0 = qfirst; q0 < kWinQuads; q0 += kWave) {
+    for (int q0 = q_start; q0 < kWinQuads; q0 += kWave) {
       const int q0s = 4 * q0;
       if (q0 > qfirst &&
           fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(q0s)) << 16), c, nr) < -42.0f)
@@ -639,7 +647,7 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
       QuadRound Q;
       uint32_t rc;
       u64 rm;
-      quad_round(L, q0, c, nr, Q, rc, rm);
+      if (!quad_round(L, q0, c, nr, Q, rc, rm)) continue;  // no token in these 256 slots
       int hit_e = -1;
 #pragma unroll
       for (int e = 3; e >= 0; --e) {
@@ -672,27 +680,33 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
   // top-p boundary by mass inside the top-k set: the first class whose
   // cumulative mass reaches P = ceil(p * z_k). Scanning for thresholds
   // p_lo <= P <= p_hi finds classes j_lo <= j* <= j_hi (cumulative masses only
-  // grow), so j_lo == j_hi decides j* exactly.
+  // grow), so j_lo == j_hi decides j* exactly. A scan runs from a position
+  // (round start and the count and mass of every slot before it) and leaves
+  // the position after the round where it found p_hi's crossing (or at the
+  // end of the window); `lo_pos` is the start of the round holding j_lo.
   struct Hit {
     int j;
     uint32_t cnt;
     u64 mass;
   };
-  auto scan_p = [&](u64 p_lo, u64 p_hi, Hit& lo, int& j_hi) {
+  struct ScanPos {
+    int q0;
+    uint32_t c;
+    u64 m;
+  };
+  auto scan_p = [&](ScanPos& pos, u64 p_lo, u64 p_hi, Hit& lo, ScanPos& lo_pos, int& j_hi) {
     lo.j = -1;
     j_hi = -1;
-    uint32_t carry_c = 0;
-    u64 carry_m = 0;
-    for (int q0 = qfirst; q0 < kWinQuads; q0 += kWave) {
+    for (; pos.q0 < kWinQuads; pos.q0 += kWave) {
       QuadRound Q;
       uint32_t rc;
       u64 rm;
-      quad_round(L, q0, c, nr, Q, rc, rm);
+      if (!quad_round(L, pos.q0, c, nr, Q, rc, rm)) continue;  // no token in these 256 slots
       int e_lo = -1, e_hi = -1;
 #pragma unroll
       for (int e = 3; e >= 0; --e) {
-        const u64 cum = carry_m + Q.cum_m[e];
-        const bool inside = 4 * (q0 + lane) + e <= jk;
+        const u64 cum = pos.m + Q.cum_m[e];
+        const bool inside = 4 * (pos.q0 + lane) + e <= jk;
         if (inside && cum >= p_lo && cum - Q.mass[e] < p_lo) e_lo = e;
         if (inside && cum >= p_hi && cum - Q.mass[e] < p_hi) e_hi = e;
       }
@@ -708,18 +722,20 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
             hc = Q.cum_c[e];
             hm = Q.cum_m[e];
           }
-        lo.j = 4 * (q0 + hl) + he;
-        lo.cnt = carry_c + readlane_u32(hc, hl);
-        lo.mass = carry_m + readlane_u64(hm, hl);
+        lo.j = 4 * (pos.q0 + hl) + he;
+        lo.cnt = pos.c + readlane_u32(hc, hl);
+        lo.mass = pos.m + readlane_u64(hm, hl);
+        lo_pos = pos;
       }
+      pos.c += rc;
+      pos.m += rm;
       const u64 b_hi = __ballot(e_hi >= 0);
       if (b_hi) {  // wave-uniform
         const int hl = __builtin_ctzll(b_hi);
-        j_hi = 4 * (q0 + hl) + __builtin_amdgcn_readlane(e_hi, hl);
+        j_hi = 4 * (pos.q0 + hl) + __builtin_amdgcn_readlane(e_hi, hl);
+        pos.q0 += kWave;
         break;
       }
-      carry_c += rc;
-      carry_m += rm;
     }
   };
 
@@ -728,6 +744,8 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
   u64 z_s = z_k;
   if (p_active) {
     Hit lo;
+    ScanPos lo_pos = {qfirst, 0u, 0ull};
+    ScanPos pos = {qfirst, 0u, 0ull};
     int j_hi = -1;
     bool decided = false;
     if (!z_k_known) {
@@ -753,16 +771,21 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
       }
       const u64 z_lo = static_cast<u64>(zf * (1.0 - eps));
       const u64 z_hi = static_cast<u64>(zf * (1.0 + eps)) + 1ull;
-      scan_p(ceil_mul(p, z_lo), ceil_mul(p, z_hi), lo, j_hi);
+      ScanPos lo_pos_b = lo_pos;
+      scan_p(pos, ceil_mul(p, z_lo), ceil_mul(p, z_hi), lo, lo_pos_b, j_hi);
       decided = (lo.j >= 0) && (lo.j == j_hi);
+      if (!decided) {
+        // the exact total: the scanned slots' mass plus the mass below them
+        z_k = pos.m + exact_mass_from(pos.q0);
+        z_k_known = true;
+        // P >= ceil(p * z_lo), so the exact crossing is not above j_lo: the
+        // exact scan restarts at the round holding j_lo
+        pos = (lo.j >= 0) ? lo_pos_b : ScanPos{qfirst, 0u, 0ull};
+      }
     }
     if (!decided) {
-      if (!z_k_known) {
-        z_k = exact_total();
-        z_k_known = true;
-      }
       const u64 P = ceil_mul(p, z_k);
-      scan_p(P, P, lo, j_hi);
+      scan_p(pos, P, P, lo, lo_pos, j_hi);
     }
     kappa = lo.j;
     cnt_s = lo.cnt;
