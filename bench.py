@@ -136,7 +136,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build runs the hot path on a single MI355X "
+        print("bench.py measures one GPU: the library runs the hot path on a single MI355X "
               "(rows are independent, so N GPUs would each run this same benchmark on their own rows); "
               "run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
