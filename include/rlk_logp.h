@@ -141,8 +141,9 @@ typedef struct rlk_support_state {
  *   workspace      rlk_logp_workspace_bytes(n_rows, layout, 1) bytes, 16-byte
  *                  aligned; may be NULL when that size is 0 (groups == 1).
  * Greedy rows (temperature 0) put a point mass on the lowest-index maximum for
- * both outputs. The support decision is taken on integer masses, so it is the
- * same for any batch or grouping. */
+ * both outputs. The support decision is taken on integer masses (64-bit, in
+ * units of 2^-40 of the row's largest weight), so it is the same for any batch
+ * or grouping; vocab_real must stay below 2^24 (else RLK_ERR_SHAPE). */
 int32_t rlk_logp_nucleus(const uint16_t* logits, int64_t n_rows, const rlk_vocab_layout* layout,
                          const float* temperature, const float* top_p, const int32_t* top_k,
                          const int64_t* target, float* policy_out, float* ref_out,

@@ -100,6 +100,9 @@ def test_full_rejects_bad_arguments(lib, kw, code):
     (dict(ws=P + 4, L=lay(groups=2)), ALIGN), (dict(logits=None), NULL),
     (dict(L=lay(groups=5)), GROUPS), (dict(n=-3), SHAPE), (dict(L=lay(vr=2000)), SHAPE),
     (dict(lse=P + 0x502), ALIGN), (dict(state=P + 0x508), ALIGN),
+    (dict(L=lay(vp=1 << 24, vr=1 << 24, stride=1 << 24)), SHAPE),
+    (dict(L=lay(vp=(1 << 24) + 1024, vr=(1 << 24) + 7, stride=(1 << 24) + 1024)), SHAPE),
+    (dict(n=0, L=lay(vp=1 << 25, vr=1 << 25, stride=1 << 25)), SHAPE),
 ])
 def test_nucleus_rejects_bad_arguments(lib, kw, code):
     assert nuc(lib, **kw) == code
