@@ -24,7 +24,10 @@
 // shard-waves count while they stream the row for the reference logprob, so
 // the support costs no extra pass; otherwise one pass builds it. The row
 // maximum is the top non-empty rank, class masses are count * weight, and
-// the thresholds come from prefix sums over the window.
+// the thresholds come from prefix sums over the window, computed by one
+// wavefront while the rest of the workgroup has finished. When top-k is off,
+// the top-p threshold ceil(p * Z) is first bracketed from the float shard
+// sums, so the total Z is summed only when the bracket cannot decide.
 // General path, for rows with a token outside the window (including any
 // |x| < 2^-24): an exact-maximum pass, then a 4096-bin histogram of
 // (count, mass) over key >> 4, then the 16 keys of each boundary bin, each
@@ -169,7 +172,7 @@ struct NucGeneral {
 
 struct NucLds {
   ShardSummary sm[kShards];
-  // row state, written by thread 0 before the support search
+  // row state, written by thread 0 before a block-wide support search
   int search;
   int k_active;
   int p_active;
@@ -179,15 +182,12 @@ struct NucLds {
   float R;
   // block reductions
   uint32_t red_u32[kNucWaves][2];
-  u64 red_u64[kNucWaves];
   int red_flag[kNucWaves];
-  // search results
-  int jk;            // fast: class index of the top-k boundary; general: key inside bk
-  uint32_t cnt_k;    // cumulative count through the top-k boundary
-  u64 z_k;           // mass of the top-k set
-  int kappa;         // support: fast = last kept class index, general = smallest kept key
-  uint32_t cnt_s;
-  u64 z_s;
+  // general path results
+  int jk;            // key of the top-k boundary inside bin bk
+  int kappa;         // smallest kept key
+  uint32_t cnt_s;    // tokens in the support
+  u64 z_s;           // support mass
   // general path scan state
   int bk;
   uint32_t rc;
