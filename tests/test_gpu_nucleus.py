@@ -162,8 +162,10 @@ def test_top_p_near_one_and_bracket_edges():
 # BF16 patterns at and just past the ends of the value ranges a 16-bit rank
 # window can cover: the top (65536 and the next value), the smallest
 # magnitudes (2^-24 and the next smaller value, both signs) and two pairs of
-# large negative values (-4.24e9 / -4.26e9 and -1.823e19 / -1.830e19).
-EDGE_BITS = [0x4780, 0x4781, 0x3380, 0x337F, 0xB380, 0xB37F, 0xCF7D, 0xCF7E, 0xDF7D, 0xDF7E]
+# large negative values (-4.24e9 / -4.26e9 and -1.823e19 / -1.830e19); and
+# values inside it around +-256.
+EDGE_BITS = [0x4380, 0x4381, 0xC37D, 0xC37E, 0x437E, 0x3380, 0x337F, 0xB380, 0xB37F,
+             0x4780, 0x4781, 0xCF7D, 0xCF7E, 0xDF7D, 0xDF7E]
 
 
 def test_window_edge_values():
