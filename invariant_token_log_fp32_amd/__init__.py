@@ -168,6 +168,34 @@ def _per_row(value, n, dtype, device, name):
     return value
 
 
+def _out(value, shape, dtype, device, name):
+    """A caller-supplied output tensor, checked (the C ABI cannot see buffer
+    sizes, so a short or mistyped buffer must never reach it), or a new one."""
+    torch = _torch()
+    if value is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if value.dtype != dtype or value.device != device or tuple(value.shape) != tuple(shape) or \
+            not value.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}")
+    return value
+
+
+def _workspace(value, need, device, name="workspace"):
+    """(tensor or None, size in bytes) of a caller-supplied workspace, checked,
+    or a new one of `need` bytes."""
+    torch = _torch()
+    if value is None:
+        if need == 0:
+            return None, 0
+        value = torch.empty(need, dtype=torch.uint8, device=device)
+    if value.device != device or not value.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+    nbytes = value.numel() * value.element_size()
+    if nbytes < need:
+        raise ValueError(f"{name} holds {nbytes} bytes, {need} needed")
+    return value, nbytes
+
+
 def _stream_handle(stream, device):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream(device)
@@ -191,19 +219,17 @@ def logp_full(logits, temperature: Union[float, "torch.Tensor"], target, *, voca
     vp = int(vocab_padded if vocab_padded is not None else logits.shape[1])
     temperature = _per_row(temperature, n, torch.float32, dev, "temperature")
     target = _per_row(target, n, torch.int64, dev, "target")
-    out = out if out is not None else torch.empty(n, dtype=torch.float32, device=dev)
-    if return_lse and lse_out is None:
-        lse_out = torch.empty(n, dtype=torch.float32, device=dev)
+    out = _out(out, (n,), torch.float32, dev, "out")
+    if return_lse or lse_out is not None:
+        lse_out = _out(lse_out, (n,), torch.float32, dev, "lse_out")
     lay = make_layout(vp, vocab_real, stride, groups)
     lib = load_library()
     need = int(lib.rlk_logp_workspace_bytes(n, ctypes.byref(lay), 0))
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     st = lib.rlk_logp_full(
         logits.data_ptr(), n, ctypes.byref(lay), temperature.data_ptr(), target.data_ptr(),
         out.data_ptr(), lse_out.data_ptr() if lse_out is not None else None,
-        workspace.data_ptr() if workspace is not None else None,
-        workspace.numel() if workspace is not None else 0, _stream_handle(stream, dev))
+        workspace.data_ptr() if workspace is not None else None, ws_bytes, _stream_handle(stream, dev))
     if st != RLK_OK:
         raise RlkError(st, "rlk_logp_full")
     return (out, lse_out) if return_lse else out
@@ -227,23 +253,22 @@ def logp_nucleus(logits, temperature, top_p, top_k, target, *, vocab_real: int,
     top_p = _per_row(top_p, n, torch.float32, dev, "top_p")
     top_k = _per_row(top_k, n, torch.int32, dev, "top_k")
     target = _per_row(target, n, torch.int64, dev, "target")
-    policy_out = policy_out if policy_out is not None else torch.empty(n, dtype=torch.float32, device=dev)
-    ref_out = ref_out if ref_out is not None else torch.empty(n, dtype=torch.float32, device=dev)
-    if return_state:
-        lse_out = lse_out if lse_out is not None else torch.empty(n, dtype=torch.float32, device=dev)
-        state_out = state_out if state_out is not None else torch.empty((n, 4), dtype=torch.int32, device=dev)
+    policy_out = _out(policy_out, (n,), torch.float32, dev, "policy_out")
+    ref_out = _out(ref_out, (n,), torch.float32, dev, "ref_out")
+    if return_state or lse_out is not None:
+        lse_out = _out(lse_out, (n,), torch.float32, dev, "lse_out")
+    if return_state or state_out is not None:
+        state_out = _out(state_out, (n, 4), torch.int32, dev, "state_out")
     lay = make_layout(vp, vocab_real, stride, groups)
     lib = load_library()
     need = int(lib.rlk_logp_workspace_bytes(n, ctypes.byref(lay), 1))
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace, ws_bytes = _workspace(workspace, need, dev)
     st = lib.rlk_logp_nucleus(
         logits.data_ptr(), n, ctypes.byref(lay), temperature.data_ptr(), top_p.data_ptr(),
         top_k.data_ptr(), target.data_ptr(), policy_out.data_ptr(), ref_out.data_ptr(),
         lse_out.data_ptr() if lse_out is not None else None,
         state_out.data_ptr() if state_out is not None else None,
-        workspace.data_ptr() if workspace is not None else None,
-        workspace.numel() if workspace is not None else 0, _stream_handle(stream, dev))
+        workspace.data_ptr() if workspace is not None else None, ws_bytes, _stream_handle(stream, dev))
     if st != RLK_OK:
         raise RlkError(st, "rlk_logp_nucleus")
     if return_state:
@@ -282,11 +307,14 @@ def logp_backward(logits, temperature, target, *, vocab_real: int, vocab_padded:
     if grad_policy is not None:
         grad_policy = _per_row(grad_policy, n, torch.float32, dev, "grad_policy")
         policy_logp = _per_row(policy_logp, n, torch.float32, dev, "policy_logp")
-        if support_state.dtype != torch.int32 or support_state.shape != (n, 4) or not support_state.is_contiguous():
-            raise ValueError(f"support_state must be a contiguous int32 tensor of shape ({n}, 4)")
+        if support_state is None or support_state.dtype != torch.int32 or support_state.shape != (n, 4) or \
+                not support_state.is_contiguous() or support_state.device != dev:
+            raise ValueError(f"support_state must be a contiguous int32 tensor of shape ({n}, 4) on {dev}")
     if out is None:
         out = torch.empty((n, vp), dtype=torch.bfloat16, device=dev)
     out_stride = _check_logits(out)
+    if out.device != dev or out.shape[0] != n or out.shape[1] < vp or (out_stride % 8) != 0:
+        raise ValueError(f"out must hold {n} rows of at least {vp} BF16 columns, row stride a multiple of 8, on {dev}")
     lay = make_layout(vp, vocab_real, stride, 1)
 
     def ptr(t):
@@ -315,11 +343,11 @@ def logp_shard_summaries(logits_slice, temperature, target, *, rank: int, groups
     lay = make_layout(vocab_padded, vocab_real, vocab_padded, groups)
     lib = load_library()
     need = int(lib.rlk_logp_summary_bytes(n, ctypes.byref(lay)))
-    if out is None:
-        out = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    out, out_bytes = _workspace(out if out is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=dev),
+                                need, dev, "out")
     st = lib.rlk_logp_shard_summaries(
         logits_slice.data_ptr(), n, ctypes.byref(lay), int(rank), int(stride), temperature.data_ptr(),
-        target.data_ptr(), out.data_ptr(), out.numel(), _stream_handle(stream, dev))
+        target.data_ptr(), out.data_ptr(), out_bytes, _stream_handle(stream, dev))
     if st != RLK_OK:
         raise RlkError(st, "rlk_logp_shard_summaries")
     return out
@@ -333,10 +361,12 @@ def logp_merge(summaries, temperature, target, *, n_rows: int, groups: int, voca
     dev = summaries.device
     temperature = _per_row(temperature, n_rows, torch.float32, dev, "temperature")
     target = _per_row(target, n_rows, torch.int64, dev, "target")
-    out = out if out is not None else torch.empty(n_rows, dtype=torch.float32, device=dev)
-    if return_lse and lse_out is None:
-        lse_out = torch.empty(n_rows, dtype=torch.float32, device=dev)
+    out = _out(out, (n_rows,), torch.float32, dev, "out")
+    if return_lse or lse_out is not None:
+        lse_out = _out(lse_out, (n_rows,), torch.float32, dev, "lse_out")
     lay = make_layout(vocab_padded, vocab_real, vocab_padded, groups)
+    if not summaries.is_contiguous():
+        raise ValueError("summaries must be contiguous")
     nbytes = summaries.numel() * summaries.element_size()
     st = load_library().rlk_logp_merge(
         summaries.data_ptr(), nbytes, int(n_rows), ctypes.byref(lay), temperature.data_ptr(), target.data_ptr(),
@@ -354,8 +384,9 @@ def _bins_tensor(bins, device):
     torch = _torch()
     if bins is None:
         return torch.empty(NORM_BIN_WORDS, dtype=torch.int64, device=device)
-    if bins.dtype not in (torch.int64, torch.uint64) or bins.numel() != NORM_BIN_WORDS or not bins.is_contiguous():
-        raise ValueError(f"bins must be a contiguous 64-bit tensor of {NORM_BIN_WORDS} words")
+    if bins.dtype not in (torch.int64, torch.uint64) or bins.numel() != NORM_BIN_WORDS or not bins.is_contiguous() \
+            or bins.device != device:
+        raise ValueError(f"bins must be a contiguous 64-bit tensor of {NORM_BIN_WORDS} words on {device}")
     return bins
 
 
@@ -368,6 +399,7 @@ def _f32_flat(x):
 
 def l2norm_zero(bins, stream=None):
     """Clear an accumulator (rlk_l2norm_zero)."""
+    bins = _bins_tensor(bins, bins.device)
     st = load_library().rlk_l2norm_zero(bins.data_ptr(), _stream_handle(stream, bins.device))
     if st != RLK_OK:
         raise RlkError(st, "rlk_l2norm_zero")
@@ -377,6 +409,7 @@ def l2norm_zero(bins, stream=None):
 def l2norm_accumulate(x, bins, stream=None):
     """Add the float32 squares of ``x`` to ``bins`` (rlk_l2norm_accumulate)."""
     x = _f32_flat(x)
+    bins = _bins_tensor(bins, x.device)
     st = load_library().rlk_l2norm_accumulate(x.data_ptr() if x.numel() else None, x.numel(), bins.data_ptr(),
                                               _stream_handle(stream, bins.device))
     if st != RLK_OK:
@@ -388,8 +421,9 @@ def l2norm_finalize(bins, sumsq_out=None, norm_out=None, stream=None):
     """(sum of squares float64 [1], norm float32 [1]) from ``bins`` (rlk_l2norm_finalize)."""
     torch = _torch()
     dev = bins.device
-    sumsq_out = sumsq_out if sumsq_out is not None else torch.empty(1, dtype=torch.float64, device=dev)
-    norm_out = norm_out if norm_out is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    bins = _bins_tensor(bins, dev)
+    sumsq_out = _out(sumsq_out, (1,), torch.float64, dev, "sumsq_out")
+    norm_out = _out(norm_out, (1,), torch.float32, dev, "norm_out")
     st = load_library().rlk_l2norm_finalize(bins.data_ptr(), sumsq_out.data_ptr(), norm_out.data_ptr(),
                                             _stream_handle(stream, dev))
     if st != RLK_OK:
@@ -416,8 +450,8 @@ def l2norm(xs, *, workspace=None, sumsq_out=None, norm_out=None, stream=None):
     dev = x.device
     ws = workspace if workspace is not None else torch.zeros(NORM_BIN_WORDS, dtype=torch.int64, device=dev)
     ws = _bins_tensor(ws, dev)
-    sumsq_out = sumsq_out if sumsq_out is not None else torch.empty(1, dtype=torch.float64, device=dev)
-    norm_out = norm_out if norm_out is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    sumsq_out = _out(sumsq_out, (1,), torch.float64, dev, "sumsq_out")
+    norm_out = _out(norm_out, (1,), torch.float32, dev, "norm_out")
     st = load_library().rlk_l2norm(x.data_ptr() if x.numel() else None, x.numel(), ws.data_ptr(),
                                    sumsq_out.data_ptr(), norm_out.data_ptr(), _stream_handle(stream, dev))
     if st != RLK_OK:
@@ -454,6 +488,11 @@ def linear(hidden, weight, *, vocab_padded: int, out=None, stream=None):
     if out is None:
         out = torch.empty((n, vocab_padded), dtype=torch.bfloat16, device=hidden.device)
     ldo = _check_logits(out)
+    if out.device != hidden.device or out.shape[0] != n or out.shape[1] < vocab_padded or (ldo % 8) != 0:
+        raise ValueError(f"out must hold {n} rows of at least {vocab_padded} BF16 columns, row stride a multiple "
+                         f"of 8, on {hidden.device}")
+    if weight.device != hidden.device:
+        raise ValueError("hidden and weight must be on the same device")
     lay = make_layout(vocab_padded, vr, ldo)
     st = load_library().rlk_linear(hidden.data_ptr(), n, d, ldh, weight.data_ptr(), ldw, ctypes.byref(lay),
                                    out.data_ptr(), _stream_handle(stream, hidden.device))
@@ -476,18 +515,18 @@ def linear_logp(hidden, weight, temperature, target, *, vocab_padded: int, retur
         raise ValueError("hidden and weight must have the same d_model")
     temperature = _per_row(temperature, n, torch.float32, dev, "temperature")
     target = _per_row(target, n, torch.int64, dev, "target")
-    out = out if out is not None else torch.empty(n, dtype=torch.float32, device=dev)
-    if return_lse and lse_out is None:
-        lse_out = torch.empty(n, dtype=torch.float32, device=dev)
+    out = _out(out, (n,), torch.float32, dev, "out")
+    if return_lse or lse_out is not None:
+        lse_out = _out(lse_out, (n,), torch.float32, dev, "lse_out")
     lay = make_layout(vocab_padded, vr, vocab_padded)
     lib = load_library()
     need = int(lib.rlk_linear_logp_workspace_bytes(n, ctypes.byref(lay)))
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    workspace, ws_bytes = _workspace(
+        workspace if workspace is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=dev), need, dev)
     st = lib.rlk_linear_logp(hidden.data_ptr(), n, d, ldh, weight.data_ptr(), ldw, ctypes.byref(lay),
                              temperature.data_ptr(), target.data_ptr(), out.data_ptr(),
                              lse_out.data_ptr() if lse_out is not None else None, workspace.data_ptr(),
-                             workspace.numel(), _stream_handle(stream, dev))
+                             ws_bytes, _stream_handle(stream, dev))
     if st != RLK_OK:
         raise RlkError(st, "rlk_linear_logp")
     return (out, lse_out) if return_lse else out
@@ -508,11 +547,11 @@ def linear_logp_summaries(hidden, weight_shard, temperature, target, *, rank: in
     lay = make_layout(vocab_padded, vocab_real, vocab_padded, groups)
     lib = load_library()
     need = int(lib.rlk_linear_logp_summary_bytes(n, ctypes.byref(lay)))
-    if out is None:
-        out = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    out, out_bytes = _workspace(out if out is not None else torch.empty(max(need, 16), dtype=torch.uint8, device=dev),
+                                need, dev, "out")
     st = lib.rlk_linear_logp_summaries(hidden.data_ptr(), n, d, ldh, weight_shard.data_ptr(), ldw, ctypes.byref(lay),
                                        int(rank), temperature.data_ptr(), target.data_ptr(), out.data_ptr(),
-                                       out.numel(), _stream_handle(stream, dev))
+                                       out_bytes, _stream_handle(stream, dev))
     if st != RLK_OK:
         raise RlkError(st, "rlk_linear_logp_summaries")
     return out
@@ -526,10 +565,12 @@ def linear_logp_merge(summaries, temperature, target, *, n_rows: int, groups: in
     dev = summaries.device
     temperature = _per_row(temperature, n_rows, torch.float32, dev, "temperature")
     target = _per_row(target, n_rows, torch.int64, dev, "target")
-    out = out if out is not None else torch.empty(n_rows, dtype=torch.float32, device=dev)
-    if return_lse and lse_out is None:
-        lse_out = torch.empty(n_rows, dtype=torch.float32, device=dev)
+    out = _out(out, (n_rows,), torch.float32, dev, "out")
+    if return_lse or lse_out is not None:
+        lse_out = _out(lse_out, (n_rows,), torch.float32, dev, "lse_out")
     lay = make_layout(vocab_padded, vocab_real, vocab_padded, groups)
+    if not summaries.is_contiguous():
+        raise ValueError("summaries must be contiguous")
     nbytes = summaries.numel() * summaries.element_size()
     st = load_library().rlk_linear_logp_merge(
         summaries.data_ptr(), nbytes, int(n_rows), ctypes.byref(lay), temperature.data_ptr(), target.data_ptr(),

@@ -48,7 +48,9 @@ def check(logits, vr, temps, top_p, top_k, targets, what, vp=None, groups_list=G
         pol, ref, full = run_nucleus(logits, vr, temps, top_p, top_k, targets, groups, vp)
         assert ref.tobytes() == full.tobytes(), f"{what}: reference bytes differ from rlk_logp_full"
         assert_close(ref, want_ref, tol=tol, what=f"{what} ref g{groups}")
-        n_amb = assert_nucleus_close(pol, want_pol, infos, tol=tol, what=f"{what} policy g{groups}")
+        n_amb, n_alt = assert_nucleus_close(pol, want_pol, infos, tol=tol, what=f"{what} policy g{groups}")
+        if n_amb:
+            say(f"{what} g{groups}: {n_amb} rows in the ambiguity band, {n_alt} matched a neighbouring cut")
         if first is None:
             first = pol.tobytes()
         assert pol.tobytes() == first, f"{what}: policy bytes differ between groups"
@@ -253,45 +255,119 @@ def qwen_logits():
     return w, logits, targets
 
 
+def general_path_rows(logits, vocab_real, chunk=512):
+    """Rows that the kernel sends to its general path, found from the BF16 bits:
+    a real token with magnitude below 2^-24 (biased exponent below 103, zeros
+    included) or a finite value outside [-4.24e9, 65536] (the 16-bit rank
+    window, patterns 0xCF7D..0x4780 for negatives and positives)."""
+    out = []
+    for r0 in range(0, logits.shape[0], chunk):
+        b = logits[r0:r0 + chunk, :vocab_real]
+        mag = b & np.uint16(0x7FFF)
+        tiny = mag < np.uint16(0x3380)
+        neg = (b & np.uint16(0x8000)) != 0
+        big = (mag > np.uint16(0x4780)) & ~neg & (mag < np.uint16(0x7F80))
+        far_neg = neg & (b > np.uint16(0xCF7D)) & (b < np.uint16(0xFF80))
+        hit = (tiny | big | far_neg).any(axis=1)
+        out.extend((np.flatnonzero(hit) + r0).tolist())
+    return np.array(out, dtype=np.int64)
+
+
+def test_general_path_row_predicate():
+    """The host predicate above on values at and past each end of the window."""
+    vr = 16
+    rows = np.full((len(EDGE_BITS), vr), datagen.f32_to_bf16_bits(np.float32([1.0]))[0], dtype=np.uint16)
+    for i, b in enumerate(EDGE_BITS):
+        rows[i, 3] = b
+    got = set(general_path_rows(rows, vr).tolist())
+    outside = {0x4781, 0x337F, 0xB37F, 0xCF7E, 0xDF7D, 0xDF7E}
+    want = {i for i, b in enumerate(EDGE_BITS) if b in outside}
+    assert got == want
+
+
+def compare_rows(logits, w, tg, pol, ref, rows, what):
+    want_pol, want_ref, infos = O.nucleus_logp(logits[rows], w.vocab_real, w.temperature[rows], w.top_p[rows],
+                                               w.top_k[rows], tg[rows])
+    assert_close(ref[rows], want_ref, tol=row_tolerance(logits[rows], w.vocab_real, w.temperature[rows]),
+                 what=f"{what} ref")
+    n_amb, n_alt = assert_nucleus_close(pol[rows], want_pol, infos,
+                                        tol=row_tolerance(logits[rows], w.vocab_real, w.temperature[rows]),
+                                        what=f"{what} policy")
+    say(f"{what}: {len(rows)} rows, {n_amb} in the ambiguity band, {n_alt} matched a neighbouring cut")
+    return n_amb, n_alt
+
+
 def test_full_size_nucleus_sampled(qwen_logits):
-    """8192 x 152576, T = 0.7, top-p 0.95, top-k off; sampled rows get targets
-    from their oracle nucleus; reference bytes equal rlk_logp_full's."""
-    import torch
+    """8192 x 152576, T = 0.7, top-p 0.95, top-k off, in the benchmark's launch
+    configuration: 40 sampled rows and every row that takes the general path
+    get targets from their oracle nucleus; reference bytes equal
+    rlk_logp_full's. No sampled row may match only a neighbouring top-p cut."""
     w, logits, targets = qwen_logits
     rows = np.random.default_rng(3003).choice(w.n_rows, 40, replace=False)
+    gen = general_path_rows(logits, w.vocab_real)
+    say(f"general-path rows in the workload: {len(gen)}")
+    assert len(gen) >= 10
     tg = targets.copy()
-    tg[rows] = support_targets(logits[rows], w.vocab_real, w.temperature[rows], w.top_p[rows], w.top_k[rows],
-                               3003)
+    sel = np.union1d(rows, gen)
+    tg[sel] = support_targets(logits[sel], w.vocab_real, w.temperature[sel], w.top_p[sel], w.top_k[sel], 3003)
     say("case: nucleus full size, groups 1")
     pol, ref, full = run_nucleus(logits, w.vocab_real, w.temperature, w.top_p, w.top_k, tg)
     assert ref.tobytes() == full.tobytes()
-    want_pol, want_ref, infos = O.nucleus_logp(logits[rows], w.vocab_real, w.temperature[rows], w.top_p[rows],
-                                               w.top_k[rows], tg[rows])
-    assert_close(ref[rows], want_ref, what="nucleus full ref")
-    n_amb = assert_nucleus_close(pol[rows], want_pol, infos, what="nucleus full policy")
-    say(f"ambiguous sampled rows: {n_amb}")
-    assert np.isfinite(pol[rows]).all()
-    del torch
+    assert np.isfinite(pol[sel]).all()
+    _, n_alt = compare_rows(logits, w, tg, pol, ref, rows, "nucleus full, sampled rows")
+    assert n_alt == 0
+    compare_rows(logits, w, tg, pol, ref, gen, "nucleus full, general-path rows")
 
 
 def test_per_request_sampled():
     """64 requests x 128 rows, T in {0.7, 1.0, 1.3}, top-p in {0.95, 0.99},
-    top-k in {-1, 128}; two sampled rows per request."""
+    top-k in {-1, 128}; two sampled rows per request, plus every row that takes
+    the general path."""
     w = datagen.per_request()
     say("generating per-request workload")
     logits, targets = w.generate()
     rng = np.random.default_rng(4004)
     rows = np.array([r * 128 + int(rng.integers(0, 128)) for r in range(64)] +
                     [r * 128 + int(rng.integers(0, 128)) for r in range(64)])
+    gen = general_path_rows(logits, w.vocab_real)
+    say(f"general-path rows in the workload: {len(gen)}")
+    assert len(gen) >= 10
+    sel = np.union1d(rows, gen)
     tg = targets.copy()
-    tg[rows] = support_targets(logits[rows], w.vocab_real, w.temperature[rows], w.top_p[rows], w.top_k[rows],
-                               4005)
+    tg[sel] = support_targets(logits[sel], w.vocab_real, w.temperature[sel], w.top_p[sel], w.top_k[sel], 4005)
     for groups in (1, 4):
         say(f"case: per-request groups {groups}")
         pol, ref, full = run_nucleus(logits, w.vocab_real, w.temperature, w.top_p, w.top_k, tg, groups)
         assert ref.tobytes() == full.tobytes()
-        want_pol, want_ref, infos = O.nucleus_logp(logits[rows], w.vocab_real, w.temperature[rows],
-                                                   w.top_p[rows], w.top_k[rows], tg[rows])
-        assert_close(ref[rows], want_ref, what="per-request ref")
-        n_amb = assert_nucleus_close(pol[rows], want_pol, infos, what="per-request policy")
-        say(f"ambiguous sampled rows: {n_amb}")
+        compare_rows(logits, w, tg, pol, ref, np.unique(rows), f"per-request g{groups}, sampled rows")
+        compare_rows(logits, w, tg, pol, ref, gen, f"per-request g{groups}, general-path rows")
+
+
+def test_full_width_general_path_rows():
+    """64 rows of 151936 real columns (benchmark's value distribution) with
+    zeros, values below 2^-24 and, in some rows, a value below -4.24e9 injected:
+    every row takes the general path (exact-maximum pass, 4096-bin histogram of
+    counts and 64-bit masses, 16-key sub-passes, and its top-k branch), at
+    top-k 128 or off, top-p 0.95 or 0.99, T 0.7 or 1.3."""
+    vp, vr = datagen.QWEN3_VOCAB_PADDED, datagen.QWEN3_VOCAB_REAL
+    n = 64
+    rng = np.random.default_rng(8008)
+    logits = np.full((n, vp), datagen.BF16_NEG_INF, dtype=np.uint16)
+    for i in range(n):
+        bits, _, _ = datagen.row_values((8008, i), vr, 2.5, 8.0 if i % 4 == 0 else None)
+        cols = rng.choice(vr, 40, replace=False)
+        bits[cols[:20]] = 0x0000
+        bits[cols[20:30]] = 0x8000
+        bits[cols[30:35]] = datagen.f32_to_bf16_bits(np.float32([1e-9]))[0]
+        bits[cols[35:40]] = datagen.f32_to_bf16_bits(np.float32([-1e-9]))[0]
+        if i % 8 == 3:
+            bits[int(rng.integers(0, vr))] = datagen.f32_to_bf16_bits(np.float32([-5e9]))[0]
+        logits[i, :vr] = bits
+    assert len(general_path_rows(logits, vr)) == n
+    temps = np.array([0.7, 1.3], np.float32)[np.arange(n) % 2]
+    top_p = np.array([0.95, 0.99], np.float32)[(np.arange(n) // 2) % 2]
+    top_k = np.array([-1, 128], np.int32)[(np.arange(n) // 4) % 2]
+    tg = support_targets(logits, vr, temps, top_p, top_k, 8009)
+    tg[::8] = rng.integers(0, vr, size=len(tg[::8]))     # some targets outside the support
+    say("case: full-width general-path rows")
+    check(logits, vr, temps, top_p, top_k, tg, "general path, full width", groups_list=(1, 8))
