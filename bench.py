@@ -15,7 +15,8 @@ Prints one JSON line. `value` is tokens/s over the K timed steps (wall clock
 between two device synchronisations); `roofline.achieved` is the algorithmic
 bytes of one launch divided by the average launch time measured with HIP
 events on the launch stream over the same region. `cpu_baseline` times the
-CPU oracle (float64 numpy, one core) on a bounded sample of the same rows.
+CPU oracle (float64 numpy) on bounded samples of the full-vocab, top-p 0.95 and
+per-request workloads, on every usable host core and on one core.
 `secondary` reports rlk_logp_nucleus on the top-p 0.95 workload, the
 backward (rlk_logp_backward) on it, rlk_logp_nucleus on the per-request
 workload (64 requests x 128 rows) and on the invariance-stress workload (64
@@ -33,6 +34,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -86,20 +89,95 @@ def bytes_backward(n_rows: int, vocab_real: int, vocab_padded: int, policy: bool
     return n_rows * (vocab_real * 2 + vocab_padded * 2 + 4 + 8 + 4 + 4 + 4 + (24 if policy else 0))
 
 
-def cpu_baseline(workload, logits, targets, rows: int):
+# Rows the forked oracle workers read: (logits, vocab_real, T, top_p, top_k, targets, kind).
+_CPU_ROWS = None
+
+
+def _oracle_chunk(lo, hi):
+    """The oracle over rows [lo, hi) of _CPU_ROWS (in a forked worker or in-process)."""
     from oracle import logp as O
-    rows = min(rows, workload.n_rows)
-    t0 = time.perf_counter()
-    for i in range(rows):
-        O.ref_logp_row(logits[i], workload.vocab_real, float(workload.temperature[i]), int(targets[i]))
-    dt = time.perf_counter() - t0
+    logits, vr, tt, pp, kk, tg, kind = _CPU_ROWS
+    if kind == "ref":
+        O.ref_logp(logits[lo:hi], vr, tt[lo:hi], tg[lo:hi])
+    else:
+        O.nucleus_logp(logits[lo:hi], vr, tt[lo:hi], pp[lo:hi], kk[lo:hi], tg[lo:hi])
+    return hi - lo
+
+
+def _noop(_):
+    return 0
+
+
+def _time_oracle(kind, logits, w, rows, targets, workers, chunk=64):
+    """Wall time of the oracle over the sample (generation excluded), on `workers`
+    forked processes (rows in 64-row chunks) or in this process when workers == 1."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    global _CPU_ROWS
+    _CPU_ROWS = (logits, w.vocab_real, w.temperature[rows], w.top_p[rows], w.top_k[rows], targets, kind)
+    n = len(rows)
+    if workers == 1:
+        t0 = time.perf_counter()
+        _oracle_chunk(0, n)
+        return time.perf_counter() - t0
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("fork")) as ex:
+        list(ex.map(_noop, range(workers)))          # workers started before the clock
+        t0 = time.perf_counter()
+        done = sum(ex.map(_oracle_chunk, range(0, n, chunk), [min(i + chunk, n) for i in range(0, n, chunk)]))
+        dt = time.perf_counter() - t0
+    assert done == n
+    return dt
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(scale: float = 1.0):
+    """The CPU oracle (float64 numpy, as it stands) timed on bounded samples of the
+    full-vocabulary, top-p 0.95 and per-request workloads, on every usable host
+    core (a forked process per core, at most 16) and on one core. Runs before the
+    GPU is touched, so the forked workers never inherit a device context."""
+    import datagen
+    workers = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else
+                         (os.cpu_count() or 1)))
+    legs = [
+        ("full-vocab reference logprob (8192 x 152576 workload, T 0.7)", "ref", datagen.full(), 256, 512),
+        ("top-p 0.95 policy + reference logprob (same logits)", "nucleus", datagen.nucleus(), 64, 64),
+        ("per-request T/top-p/top-k policy + reference logprob (64 x 128 rows)", "nucleus", datagen.per_request(),
+         64, 64),
+    ]
+    out = []
+    for name, kind, w, rows_per_core_multi, rows_single in legs:
+        n_multi = max(workers, int(rows_per_core_multi * workers * scale))
+        n_single = max(1, min(n_multi, int(rows_single * scale)))
+        # a spread of rows (every request of the per-request workload is represented)
+        rows = np.linspace(0, w.n_rows - 1, n_multi).astype(np.int64)
+        logits, targets = w.generate(rows=rows.tolist())
+        one = np.linspace(0, n_multi - 1, n_single).astype(np.int64)   # the one-core sample, spread alike
+        for cores, sel in ((workers, np.arange(n_multi)), (1, one)):
+            dt = _time_oracle(kind, logits[sel], w, rows[sel], targets[sel], cores)
+            out.append({"workload": name, "cores": cores, "rows": int(len(sel)), "seconds": dt,
+                        "tokens_per_s": len(sel) / dt})
+        del logits
+    head = out[0]
     return {
-        "value": rows / dt,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": head["cores"],
         "kind": "oracle",
-        "sample": f"rows 0..{rows - 1} of the same 8192-row workload (full 151936-column rows), "
-                  f"float64 numpy reference logprob, one core, {dt:.1f} s",
+        "cpu_model": cpu_model(),
+        "sample": (f"{head['rows']} rows spread over the 8192-row full-vocab workload (whole 151936-column rows), "
+                   f"float64 numpy oracle, {head['cores']} forked processes, {head['seconds']:.1f} s; "
+                   "the other legs are listed under 'workloads'"),
+        "workloads": out,
     }
 
 
@@ -127,7 +205,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--groups", type=int, default=1, help="physical blocks per row (1, 2, 4 or 8)")
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle sample size for cpu_baseline")
+    ap.add_argument("--cpu-scale", type=float, default=1.0, help="scales the oracle samples of cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -141,13 +219,16 @@ def main():
               "run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import datagen
     import invariant_token_log_fp32_amd as rlk
 
-    rlk.load_library()  # fails loudly when the HIP library is missing
+    if not os.path.exists(rlk.LIB_PATH):
+        rlk.load_library()  # raises: the HIP library is missing
+    # the oracle's forked workers start before anything touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_scale)
+    rlk.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -379,8 +460,8 @@ def main():
         del hid, wt, lgt, lws
         result["secondary"] = sec
 
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, logits, targets, args.cpu_rows)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
 
     print(json.dumps(result), flush=True)
 

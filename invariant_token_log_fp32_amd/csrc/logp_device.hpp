@@ -283,6 +283,32 @@ __device__ __forceinline__ void shard_pass(const u32x4* __restrict__ base, int n
   static_assert(U % kRefGroup == 0, "chunks hold whole reference groups");
   constexpr int kU = Hook::kLateWiden ? kRefGroup : U;
   int first = 0;
+  if constexpr (!Hook::kLateWiden) {
+    // Whole chunks load without bounds checks (no -inf defaults to select);
+    // the reference check stays per group, so the order of the terms and the
+    // group that fixes the reference are those of the guarded loop.
+    constexpr int kStep = U * kWave;
+    const int nmain = nfull - nfull % kStep;
+    int all8[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) all8[u] = 8;
+    for (; first < nmain; first += kStep) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(base + first + u * kWave + lane);
+      st.template consume<U>(v, c, hook, all8);
+    }
+    if (st.have_ref) {
+      // The rest one per lane at a time, as under a late-widening hook.
+      const int one[1] = {8};
+      for (; first < nfull; first += kWave) {
+        if (first + lane < nfull) {
+          const u32x4 v[1] = {__builtin_nontemporal_load(base + first + lane)};
+          st.template consume<1>(v, c, hook, one);
+        }
+      }
+    }
+  }
   if constexpr (Hook::kLateWiden) {
     constexpr int kStep = kU * kWave;
     const int nmain = nfull - nfull % kStep;

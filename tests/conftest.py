@@ -20,3 +20,11 @@ def _library_built():
     if not os.path.exists(LIB_PATH):
         from invariant_token_log_fp32_amd import build
         build.build()
+
+
+def pytest_terminal_summary(terminalreporter):
+    gpu_util = sys.modules.get("gpu_util")
+    if gpu_util is not None and gpu_util.REPORT:
+        terminalreporter.write_sep("-", "counts reported by the GPU tests")
+        for line in gpu_util.REPORT:
+            terminalreporter.write_line(line)

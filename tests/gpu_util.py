@@ -9,9 +9,19 @@ import numpy as np
 TOL = 2e-5
 
 
+# Lines that the test session prints in its terminal summary (counts that a
+# passing run should still show: ambiguity-band rows, general-path rows).
+REPORT = []
+
+
 def say(msg):
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+def report(msg):
+    say(msg)
+    REPORT.append(msg)
 
 
 def device():

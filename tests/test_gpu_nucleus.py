@@ -21,7 +21,7 @@ import datagen
 import invariant_token_log_fp32_amd as rlk
 from oracle import logp as O
 
-from gpu_util import TOL, assert_close, assert_nucleus_close, row_tolerance, say, to_host, upload, upload_logits
+from gpu_util import TOL, assert_close, assert_nucleus_close, report, row_tolerance, say, to_host, upload, upload_logits
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,7 @@ def check(logits, vr, temps, top_p, top_k, targets, what, vp=None, groups_list=G
         assert_close(ref, want_ref, tol=tol, what=f"{what} ref g{groups}")
         n_amb, n_alt = assert_nucleus_close(pol, want_pol, infos, tol=tol, what=f"{what} policy g{groups}")
         if n_amb:
-            say(f"{what} g{groups}: {n_amb} rows in the ambiguity band, {n_alt} matched a neighbouring cut")
+            report(f"{what} g{groups}: {n_amb} rows in the ambiguity band, {n_alt} matched a neighbouring cut")
         if first is None:
             first = pol.tobytes()
         assert pol.tobytes() == first, f"{what}: policy bytes differ between groups"
@@ -293,7 +293,7 @@ def compare_rows(logits, w, tg, pol, ref, rows, what):
     n_amb, n_alt = assert_nucleus_close(pol[rows], want_pol, infos,
                                         tol=row_tolerance(logits[rows], w.vocab_real, w.temperature[rows]),
                                         what=f"{what} policy")
-    say(f"{what}: {len(rows)} rows, {n_amb} in the ambiguity band, {n_alt} matched a neighbouring cut")
+    report(f"{what}: {len(rows)} rows, {n_amb} in the ambiguity band, {n_alt} matched a neighbouring cut")
     return n_amb, n_alt
 
 
