@@ -70,7 +70,8 @@ enum {
   RLK_ERR_SHAPE = -3,     /* n_rows (0 .. 2^22) or a layout field out of range */
   RLK_ERR_GROUPS = -4,    /* groups is not 1, 2, 4 or 8 */
   RLK_ERR_WORKSPACE = -5, /* workspace missing or smaller than rlk_logp_workspace_bytes() */
-  RLK_ERR_HIP = -6        /* the HIP runtime reported an error when launching */
+  RLK_ERR_HIP = -6,       /* the HIP runtime reported an error when launching */
+  RLK_ERR_SCRATCH = -7    /* n_rows above RLK_NOALLOC_MAX_ROWS in rlk_logp_nucleus_noalloc */
 };
 
 /* Row layout of the logits [CFG-TOPOLOGY], [REPRO-CANON].
@@ -149,6 +150,29 @@ int32_t rlk_logp_nucleus(const uint16_t* logits, int64_t n_rows, const rlk_vocab
                          const int64_t* target, float* policy_out, float* ref_out,
                          float* lse_out, rlk_support_state* support_out,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Rows that rlk_logp_nucleus_noalloc handles with groups > 1 (its static
+ * scratch holds their shard summaries: 128 bytes per row, 4 MiB per GPU). */
+#define RLK_NOALLOC_MAX_ROWS 32768
+
+/* rlk_logp_nucleus without a workspace argument, for callers that cannot
+ * allocate device memory (code under hipGraph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, outputs and bytes as
+ * rlk_logp_nucleus; the caller still provides every input and output.
+ * With groups > 1 the shard summaries go to a static device array of
+ * RLK_NOALLOC_MAX_ROWS rows that the library keeps on each GPU it runs on
+ * until the process ends (its address is looked up on the first call on a
+ * device, with the current device; nothing is allocated). Every call on one
+ * GPU shares that array, so calls that overlap on one GPU (concurrent streams
+ * or host threads) race and must be serialised by the caller; a call writes
+ * every summary it reads, so nothing needs clearing between calls.
+ * Returns RLK_ERR_SCRATCH when groups > 1 and n_rows > RLK_NOALLOC_MAX_ROWS,
+ * RLK_ERR_HIP when the scratch address cannot be obtained, otherwise what
+ * rlk_logp_nucleus returns. With groups == 1 no scratch is used. */
+int32_t rlk_logp_nucleus_noalloc(const uint16_t* logits, int64_t n_rows, const rlk_vocab_layout* layout,
+                                 const float* temperature, const float* top_p, const int32_t* top_k,
+                                 const int64_t* target, float* policy_out, float* ref_out,
+                                 float* lse_out, rlk_support_state* support_out, hipStream_t stream);
 
 /* Gradient of sum_i (grad_ref[i] * ref_i + grad_policy[i] * policy_i) with
  * respect to the BF16 logits, as BF16 (round to nearest even), for training

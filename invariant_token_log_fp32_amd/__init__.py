@@ -20,7 +20,7 @@ __all__ = [
     "summary_bytes", "logp_full", "logp_nucleus", "logp_shard_summaries", "logp_merge", "logp_backward",
     "support_state_fields", "l2norm", "l2norm_zero", "l2norm_accumulate", "l2norm_finalize", "NORM_BIN_WORDS",
     "linear", "linear_logp", "linear_logp_workspace_bytes", "linear_logp_summaries", "linear_logp_merge",
-    "RlkError", "N_SHARDS",
+    "logp_nucleus_noalloc", "NOALLOC_MAX_ROWS", "RlkError", "N_SHARDS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,11 +29,12 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "rlk_logp.h")
 HEADER_PATHS = [HEADER_PATH] + [os.path.join(os.path.dirname(_PKG), "include", n) for n in ("rlk_norm.h", "rlk_linear.h")]
 N_SHARDS = 8
 NORM_BIN_WORDS = 264  # uint64 words of rlk_norm_bins
+NOALLOC_MAX_ROWS = 32768  # RLK_NOALLOC_MAX_ROWS
 
 RLK_OK = 0
 STATUS_NAMES = {
     0: "RLK_OK", -1: "RLK_ERR_NULL", -2: "RLK_ERR_ALIGN", -3: "RLK_ERR_SHAPE",
-    -4: "RLK_ERR_GROUPS", -5: "RLK_ERR_WORKSPACE", -6: "RLK_ERR_HIP",
+    -4: "RLK_ERR_GROUPS", -5: "RLK_ERR_WORKSPACE", -6: "RLK_ERR_HIP", -7: "RLK_ERR_SCRATCH",
 }
 
 
@@ -72,6 +73,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rlk_logp_full.restype = i32
     lib.rlk_logp_nucleus.argtypes = [vp, i64, lay, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.rlk_logp_nucleus.restype = i32
+    lib.rlk_logp_nucleus_noalloc.argtypes = [vp, i64, lay, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.rlk_logp_nucleus_noalloc.restype = i32
     lib.rlk_logp_workspace_bytes.argtypes = [i64, lay, i32]
     lib.rlk_logp_workspace_bytes.restype = sz
     lib.rlk_status_string.argtypes = [i32]
@@ -273,6 +276,39 @@ def logp_nucleus(logits, temperature, top_p, top_k, target, *, vocab_real: int,
         raise RlkError(st, "rlk_logp_nucleus")
     if return_state:
         return policy_out, ref_out, lse_out, state_out
+    return policy_out, ref_out
+
+
+def logp_nucleus_noalloc(logits, temperature, top_p, top_k, target, *, vocab_real: int,
+                         vocab_padded: Optional[int] = None, groups: int = 1, policy_out=None, ref_out=None,
+                         lse_out=None, state_out=None, stream=None):
+    """rlk_logp_nucleus_noalloc: rlk_logp_nucleus without a workspace (the
+    library's static per-GPU scratch holds the shard summaries when groups > 1,
+    for at most NOALLOC_MAX_ROWS rows). Calls that overlap on one GPU race.
+    Returns (policy, reference); lse_out / state_out are filled when given."""
+    torch = _torch()
+    stride = _check_logits(logits)
+    n = logits.shape[0]
+    dev = logits.device
+    vp = int(vocab_padded if vocab_padded is not None else logits.shape[1])
+    temperature = _per_row(temperature, n, torch.float32, dev, "temperature")
+    top_p = _per_row(top_p, n, torch.float32, dev, "top_p")
+    top_k = _per_row(top_k, n, torch.int32, dev, "top_k")
+    target = _per_row(target, n, torch.int64, dev, "target")
+    policy_out = _out(policy_out, (n,), torch.float32, dev, "policy_out")
+    ref_out = _out(ref_out, (n,), torch.float32, dev, "ref_out")
+    if lse_out is not None:
+        lse_out = _out(lse_out, (n,), torch.float32, dev, "lse_out")
+    if state_out is not None:
+        state_out = _out(state_out, (n, 4), torch.int32, dev, "state_out")
+    lay = make_layout(vp, vocab_real, stride, groups)
+    st = load_library().rlk_logp_nucleus_noalloc(
+        logits.data_ptr(), n, ctypes.byref(lay), temperature.data_ptr(), top_p.data_ptr(), top_k.data_ptr(),
+        target.data_ptr(), policy_out.data_ptr(), ref_out.data_ptr(),
+        lse_out.data_ptr() if lse_out is not None else None,
+        state_out.data_ptr() if state_out is not None else None, _stream_handle(stream, dev))
+    if st != RLK_OK:
+        raise RlkError(st, "rlk_logp_nucleus_noalloc")
     return policy_out, ref_out
 
 

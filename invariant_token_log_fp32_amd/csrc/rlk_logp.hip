@@ -31,6 +31,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "backward.hpp"
 #include "logp_device.hpp"
 #include "rlk_logp.h"
@@ -315,6 +317,33 @@ static size_t workspace_bytes(int64_t n_rows, const rlk_vocab_layout* L, bool /*
 
 static int32_t launched() { return hipGetLastError() == hipSuccess ? RLK_OK : RLK_ERR_HIP; }
 
+// ----------------------------------------------------------------------------
+// Static scratch of rlk_logp_nucleus_noalloc: the shard summaries of up to
+// kScratchRows rows (groups > 1), in a device array that every GPU the library
+// runs on holds until the process ends. In host code `scratch` is only a
+// stand-in for the symbol; its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+// ----------------------------------------------------------------------------
+constexpr int64_t kScratchRows = RLK_NOALLOC_MAX_ROWS;
+static __device__ __align__(256) ShardSummary scratch[kScratchRows * kShards];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (nullptr on a HIP error).
+static ShardSummary* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return static_cast<ShardSummary*>(g_scratch_ptr[dev]);
+}
+
 // groups > 1: every rank's summaries of the full rows, rank-major, into ws.
 static int32_t launch_all_ranks(const uint16_t* logits, int64_t n_rows, const rlk_vocab_layout* L,
                                 const float* temperature, const int64_t* target, ShardSummary* ws,
@@ -341,6 +370,7 @@ const char* rlk_status_string(int32_t status) {
     case RLK_ERR_GROUPS: return "groups must be 1, 2, 4 or 8";
     case RLK_ERR_WORKSPACE: return "workspace or summary buffer missing or too small";
     case RLK_ERR_HIP: return "HIP runtime error while launching";
+    case RLK_ERR_SCRATCH: return "n_rows exceeds the static scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }
@@ -421,6 +451,32 @@ int32_t rlk_logp_nucleus(const uint16_t* logits, int64_t n_rows, const rlk_vocab
       logits, layout->row_stride, n_rows, kShards / G, S, layout->vocab_real, temperature, top_p, top_k, target, ws,
       policy_out, ref_out, lse_out, support_out);
   return launched();
+}
+
+int32_t rlk_logp_nucleus_noalloc(const uint16_t* logits, int64_t n_rows, const rlk_vocab_layout* layout,
+                                 const float* temperature, const float* top_p, const int32_t* top_k,
+                                 const int64_t* target, float* policy_out, float* ref_out, float* lse_out,
+                                 rlk_support_state* support_out, hipStream_t stream) {
+  using namespace rlk;
+  int32_t st = check_layout(n_rows, layout);
+  if (st != RLK_OK) return st;
+  if (layout->vocab_real >= kMaxNucleusVocab) return RLK_ERR_SHAPE;
+  if (layout->groups > 1 && n_rows > kScratchRows) return RLK_ERR_SCRATCH;
+  if (n_rows == 0) return RLK_OK;
+  if (layout->groups == 1)  // no scratch: the one-launch kernel
+    return rlk_logp_nucleus(logits, n_rows, layout, temperature, top_p, top_k, target, policy_out, ref_out,
+                            lse_out, support_out, nullptr, 0, stream);
+  // the argument checks of rlk_logp_nucleus, before the scratch is looked up
+  if (!logits || !temperature || !top_p || !top_k || !target || !policy_out || !ref_out) return RLK_ERR_NULL;
+  if (!aligned(logits, 16) || !aligned(temperature, 4) || !aligned(top_p, 4) || !aligned(top_k, 4) ||
+      !aligned(target, 8) || !aligned(policy_out, 4) || !aligned(ref_out, 4) || (lse_out && !aligned(lse_out, 4)) ||
+      (support_out && !aligned(support_out, 16)))
+    return RLK_ERR_ALIGN;
+  ShardSummary* ws = scratch_on_current_device();
+  if (ws == nullptr) return RLK_ERR_HIP;
+  return rlk_logp_nucleus(logits, n_rows, layout, temperature, top_p, top_k, target, policy_out, ref_out, lse_out,
+                          support_out, ws, static_cast<size_t>(kScratchRows) * kShards * sizeof(ShardSummary),
+                          stream);
 }
 
 int32_t rlk_logp_shard_summaries(const uint16_t* logits_slice, int64_t n_rows, const rlk_vocab_layout* layout,

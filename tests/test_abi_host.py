@@ -13,7 +13,7 @@ import pytest
 import invariant_token_log_fp32_amd as rlk
 from invariant_token_log_fp32_amd import VocabLayout
 
-OK, NULL, ALIGN, SHAPE, GROUPS, WS, HIP = 0, -1, -2, -3, -4, -5, -6
+OK, NULL, ALIGN, SHAPE, GROUPS, WS, HIP, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 P = 0x10000  # fake 64 KiB-aligned device address
 
 
@@ -52,7 +52,8 @@ def test_every_declared_function_is_exported(lib):
                           "rlk_logp_shard_summaries", "rlk_logp_merge", "rlk_logp_summary_bytes",
                           "rlk_logp_backward", "rlk_l2norm", "rlk_l2norm_zero", "rlk_l2norm_accumulate",
                           "rlk_l2norm_finalize", "rlk_linear", "rlk_linear_logp", "rlk_linear_logp_workspace_bytes",
-                          "rlk_linear_logp_summaries", "rlk_linear_logp_merge", "rlk_linear_logp_summary_bytes"}
+                          "rlk_linear_logp_summaries", "rlk_linear_logp_merge", "rlk_linear_logp_summary_bytes",
+                          "rlk_logp_nucleus_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -308,3 +309,30 @@ def test_linear_logp_summary_sizes(lib):
         assert lib.rlk_linear_logp_summary_bytes(8192, ctypes.byref(L)) == 8192 * (1192 // g) * 16
     L = lay(vp=1088, vr=1000, groups=8)
     assert lib.rlk_linear_logp_summary_bytes(8, ctypes.byref(L)) == 0
+
+
+def noalloc(lib, logits=P, n=4, L=None, t=P + 0x100, p=P + 0x140, k=P + 0x180, tg=P + 0x200, pol=P + 0x300,
+            ref=P + 0x400, lse=None, state=None):
+    L = L if L is not None else lay()
+    return lib.rlk_logp_nucleus_noalloc(logits, n, ctypes.byref(L) if L is not False else None, t, p, k, tg, pol,
+                                        ref, lse, state, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(L=False), NULL), (dict(logits=None), NULL), (dict(pol=None), NULL), (dict(ref=None), NULL),
+    (dict(logits=P + 2), ALIGN), (dict(state=P + 8), ALIGN), (dict(n=-1), SHAPE),
+    (dict(L=lay(groups=3)), GROUPS), (dict(L=lay(vp=1 << 25, vr=1 << 24)), SHAPE),
+    (dict(n=rlk.NOALLOC_MAX_ROWS + 1, L=lay(groups=2)), SCRATCH),
+    (dict(n=rlk.NOALLOC_MAX_ROWS + 1, L=lay(groups=8)), SCRATCH),
+])
+def test_noalloc_rejects_bad_arguments(lib, kw, code):
+    assert noalloc(lib, **kw) == code
+
+
+def test_noalloc_limits_and_status(lib):
+    assert noalloc(lib, n=0, L=lay(groups=4)) == OK
+    assert noalloc(lib, n=0, logits=None, pol=None, ref=None) == OK
+    assert "static scratch" in rlk.status_string(SCRATCH)
+    assert rlk.STATUS_NAMES[SCRATCH] == "RLK_ERR_SCRATCH"
+    text = open(rlk.HEADER_PATH).read()
+    assert f"#define RLK_NOALLOC_MAX_ROWS {rlk.NOALLOC_MAX_ROWS}" in text
