@@ -17,22 +17,26 @@
 // the support does not depend on the schedule of any atomic; the test
 // "cumulative >= p * Z" is evaluated exactly as cumulative >= ceil(p * Z).
 //
-// Fast path: every token is counted per compressed 16-bit rank (LDS u32
-// atomics) in a fixed window of 12288 ranks that covers every BF16 value from
-// -4.24e9 to 65536 with magnitude at least 2^-24 (the rank keeps the order of
-// the values; -inf tokens are counted apart, mass 0). With groups == 1 the
+// Fast path: every token is counted (LDS u32 atomics) in a window of classes:
+// the BF16 values of magnitude in [2^-24, 65536) of either sign, interleaved
+// by magnitude (slot 2*(m - m_lo) + sign, m the 15-bit magnitude pattern),
+// plus one class for +-0; -inf tokens are counted apart (mass 0). The slots of
+// two tokens come from three packed 16-bit instructions, and one maximum over
+// a vector's eight slots tells whether all of them lie in the window. Classes
+// are visited in value order (positive slots from the top, then the zero
+// class, then negative slots from the bottom). With groups == 1 the
 // shard-waves count while they stream the row for the reference logprob, so
 // the support costs no extra pass; otherwise one pass builds it. The row
-// maximum is the top non-empty rank, class masses are count * weight, and
-// the thresholds come from prefix sums over the window, computed by one
+// maximum is the first non-empty class, class masses are count * weight, and
+// the thresholds come from prefix sums over the classes, computed by one
 // wavefront while the rest of the workgroup has finished. When top-k is off,
 // the top-p threshold ceil(p * Z) is first bracketed from the float shard
 // sums, so the total Z is summed only when the bracket cannot decide.
-// General path, for rows with a token outside the window (including any
-// |x| < 2^-24): an exact-maximum pass, then a 4096-bin histogram of
-// (count, mass) over key >> 4, then the 16 keys of each boundary bin, each
-// from another pass over the row. Both paths produce the same integers and
-// therefore the same output bytes.
+// General path, for rows with a token outside the window (a nonzero value of
+// magnitude below 2^-24, or 65536 and beyond): an exact-maximum pass, then a
+// 4096-bin histogram of (count, mass) over key >> 4, then the 16 keys of each
+// boundary bin, each from another pass over the row. Both paths produce the
+// same integers and therefore the same output bytes.
 #pragma once
 
 #include "logp_device.hpp"
@@ -44,10 +48,21 @@ constexpr int kNucThreads = 512;
 constexpr int kNucWaves = kNucThreads / kWave;
 constexpr int kBinsA = 4096;
 constexpr int kSub = 16;
-constexpr int kWin = 12288;                        // 48 KB of counts: three rows per CU
-constexpr int kWinPerThread = kWin / kNucThreads;  // 24
-constexpr uint32_t kWinHi = 0x6081u;               // rank of 65536.0: window slot 0
-constexpr uint32_t kTinyExp = 103;                 // biased exponent: |x| < 2^-24
+// The window: magnitudes kMagLo .. kMagLo + kNMag - 1 (2^-24 <= |x| < 65536)
+// of both signs, interleaved, then the zero class. 40 KB of counts: three rows
+// per CU with the general path's histogram in the same LDS.
+constexpr uint32_t kMagLo = 0x3380u;               // magnitude pattern of 2^-24
+constexpr int kNMag = 5120;                        // 40 binades of 128 BF16 values
+constexpr int kWin = 2 * kNMag;                    // interleaved slots
+constexpr int kZeroSlot = kWin;                    // the +-0 class
+constexpr int kWinWords = kWin + 2;                // + zero slot + pad (64-bit clearing)
+constexpr uint32_t kSlotOut = 0xFFFFFFFFu;         // window_slot() of a token outside the window
+// Classes in value order ("ranks"): positives from the top (rank kNMag - 1 - k
+// for magnitude index k), the zero class, negatives from the top (rank
+// kNMag + 1 + k); kNoRank stands for the -inf class below all of them.
+constexpr int kZeroRank = kNMag;
+constexpr int kRanks = kWin + 1;
+constexpr int kNoRank = kRanks;
 constexpr uint32_t kNegInfBits = 0xFF80u;
 
 typedef unsigned long long u64;
@@ -58,33 +73,36 @@ __device__ __forceinline__ uint32_t key16(uint32_t b) {
   return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
 }
 
-// Compressed rank of a BF16 pattern with |x| >= 2^-24, finite: negative values
-// rank 0xFFFF - b (at most 0x4C7F), positive values b + 0x1901 (at least
-// 0x4C81); the order of the ranks is the order of the values.
-__device__ __forceinline__ uint32_t crank16(uint32_t b) { return (b & 0x8000u) ? (0xFFFFu - b) : (b + 0x1901u); }
-
-// Inverse of crank16.
-__device__ __forceinline__ uint32_t crank_bits(uint32_t r) { return (r < 0x4C80u) ? (0xFFFFu - r) : (r - 0x1901u); }
-
-// BF16 value of window slot j (j < kWin).
-__device__ __forceinline__ float slot_value(int j) {
-  return __uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(j)) << 16);
-}
-
 // BF16 value of a key16 (the +0 key for the folded zeros).
 __device__ __forceinline__ float key_value(uint32_t key) {
   const uint32_t b = (key & 0x8000u) ? (key & 0x7FFFu) : (~key & 0xFFFFu);
   return __uint_as_float(b << 16);
 }
 
-// Window slot of a BF16 pattern (kWinHi - rank), or kWin (the trash slot) for
-// -inf, NaN, +-inf, |x| < 2^-24 and values outside the window.
+// Window slot of a BF16 pattern: 2 * (m - kMagLo) + sign for magnitudes in the
+// window, kZeroSlot for +-0, kSlotOut for everything else (-inf, NaN, +-inf,
+// nonzero magnitudes below 2^-24, magnitudes of 65536 and beyond).
 __device__ __forceinline__ uint32_t window_slot(uint32_t b) {
-  const uint32_t ex = b & 0x7F80u;
-  const bool normal = (ex - (kTinyExp << 7)) < (0x7F80u - (kTinyExp << 7));
-  const uint32_t idx = kWinHi - crank16(b);
-  return (normal && idx < static_cast<uint32_t>(kWin)) ? idx : static_cast<uint32_t>(kWin);
+  const uint32_t m = b & 0x7FFFu;
+  if (m == 0u) return static_cast<uint32_t>(kZeroSlot);
+  const uint32_t k = m - kMagLo;  // wraps below kMagLo
+  return (k < static_cast<uint32_t>(kNMag)) ? (2u * k + (b >> 15)) : kSlotOut;
 }
+
+// Rank (value order) of a window slot.
+__device__ __forceinline__ int slot_rank(uint32_t slot) {
+  if (slot == static_cast<uint32_t>(kZeroSlot)) return kZeroRank;
+  const int k = static_cast<int>(slot >> 1);
+  return (slot & 1u) ? (kNMag + 1 + k) : (kNMag - 1 - k);
+}
+
+// BF16 pattern and value of the class at a rank (rank < kRanks).
+__device__ __forceinline__ uint32_t rank_bits(int r) {
+  if (r < kNMag) return kMagLo + static_cast<uint32_t>(kNMag - 1 - r);
+  if (r == kZeroRank) return 0u;
+  return 0x8000u | (kMagLo + static_cast<uint32_t>(r - kNMag - 1));
+}
+__device__ __forceinline__ float rank_value(int r) { return __uint_as_float(rank_bits(r) << 16); }
 
 // floor(w * 2^40) for 0 <= w < 2^24 (NaN excluded). Every step is exact: a =
 // w * 2^40 is a power-of-two scaling (0 when w is 0 or below the normal range,
@@ -196,8 +214,8 @@ struct NucLds {
   uint32_t scan_cnt_above;
   u64 scan_mass_above;
   union alignas(16) {
-    uint32_t win[kWin + 1];  // + trash slot
-    u64 win_pairs[(kWin + 2) / 2];  // the window (and trash slot) as 64-bit pairs, for clearing
+    uint32_t win[kWinWords];        // interleaved slots, the zero class, a pad word
+    u64 win_pairs[kWinWords / 2];   // the same as 64-bit pairs, for clearing
     NucGeneral gen;
   } u;
 };
@@ -268,64 +286,33 @@ __device__ __forceinline__ void row_pass_vec(const uint16_t* __restrict__ rowp, 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
-// Window slots of the two BF16 values packed in one 32-bit word, computed on
-// 16-bit integer lane pairs (low half = first value):
-//   negative b: slot = b - 0x9F7E, in the window iff slot - 0x1402 <= 0x1BFD
-//   positive b: slot = 0x4780 - b, in the window iff slot <= 0x1400
-// `outside` is nonzero iff a half lies outside the window; halves inside get
-// exactly window_slot() (checked against it on all 65536 patterns).
-__device__ __forceinline__ uint32_t window_slots2(uint32_t w, uint32_t& outside) {
-  uint32_t neg, a, b, slot, lo, d, span;
-  asm(
-      "v_pk_ashrrev_i16 %[neg], 15, %[w] op_sel_hi:[0,1]\n\t"
-      "v_pk_sub_u16 %[a], %[w], %[k1]\n\t"
-      "v_pk_sub_u16 %[b], %[k2], %[w]\n\t"
-      "v_bfi_b32 %[slot], %[neg], %[a], %[b]\n\t"
-      "v_and_b32 %[lo], %[k3], %[neg]\n\t"
-      "v_pk_sub_u16 %[d], %[slot], %[lo]\n\t"
-      "v_bfi_b32 %[span], %[neg], %[k4], %[k5]\n\t"
-      "v_pk_sub_u16 %[out], %[d], %[span] clamp"
-      : [neg] "=&v"(neg), [a] "=&v"(a), [b] "=&v"(b), [slot] "=&v"(slot), [lo] "=&v"(lo), [d] "=&v"(d),
-        [span] "=&v"(span), [out] "=&v"(outside)
-      : [w] "v"(w), [k1] "v"(0x9F7E9F7Eu), [k2] "v"(0x47804780u), [k3] "v"(0x14021402u), [k4] "v"(0x1BFD1BFDu),
-        [k5] "v"(0x14001400u));
+// Window slots of the two BF16 values packed in one 32-bit word (low half =
+// first value), on 16-bit integer lane pairs: the sign bit, then
+// 2 * b + sign (the product drops the sign bit, leaving 2 * m + sign), then
+// minus 2 * kMagLo. A half lies in the window exactly when its result is below
+// kWin: magnitudes below kMagLo wrap to 0x9900 and above, magnitudes of
+// kMagLo + kNMag and beyond give kWin .. 0x98FF (no wrap). Halves in the
+// window get exactly window_slot() (checked against it on all 65536 patterns).
+__device__ __forceinline__ uint32_t window_slots2(uint32_t w) {
+  uint32_t sgn, u, slot;
+  asm("v_pk_lshrrev_b16 %[sgn], %[c15], %[w]\n\t"
+      "v_pk_mad_u16 %[u], %[w], %[c2], %[sgn]\n\t"
+      "v_pk_sub_u16 %[slot], %[u], %[lo]"
+      : [sgn] "=&v"(sgn), [u] "=&v"(u), [slot] "=&v"(slot)
+      : [w] "v"(w), [c15] "v"(0x000F000Fu), [c2] "v"(0x00020002u), [lo] "v"(0x67006700u));
   return slot;
 }
 
-// Window slots of the two BF16 values packed in one 32-bit word, without the
-// range check: equal to window_slot() for every half whose value lies in the
-// window.
-__device__ __forceinline__ uint32_t window_slots2_unchecked(uint32_t w) {
-  uint32_t neg, a, b, slot;
-  asm(
-      "v_pk_ashrrev_i16 %[neg], 15, %[w] op_sel_hi:[0,1]\n\t"
-      "v_pk_sub_u16 %[a], %[w], %[k1]\n\t"
-      "v_pk_sub_u16 %[b], %[k2], %[w]\n\t"
-      "v_bfi_b32 %[slot], %[neg], %[a], %[b]"
-      : [neg] "=&v"(neg), [a] "=&v"(a), [b] "=&v"(b), [slot] "=&v"(slot)
-      : [w] "v"(w), [k1] "v"(0x9F7E9F7Eu), [k2] "v"(0x47804780u));
-  return slot;
-}
-
-// Nonzero unless every one of the 8 BF16 values of a vector has magnitude in
-// [2^-24, 65536] (patterns 0x3380..0x4780 after the sign is cleared): values
-// of either sign in that range lie in the window. A sufficient test only; the
-// values it rejects are then slotted one by one.
-__device__ __forceinline__ uint32_t vector_outside_core(const uint32_t (&w)[4]) {
-  uint32_t d[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t m = w[i] & 0x7FFF7FFFu;
-    asm("v_pk_sub_u16 %0, %1, %2" : "=v"(d[i]) : "v"(m), "v"(0x33803380u));  // wraps below 0x3380
-  }
+// Nonzero unless all 8 slots of a vector (4 words of slot pairs) are below
+// kWin: the packed maximum of the 8, then a saturating subtraction of kWin - 1.
+__device__ __forceinline__ uint32_t slots_outside(const uint32_t (&sl)[4]) {
   uint32_t e0, e1, e, out;
-  asm(
-      "v_pk_max_u16 %[e0], %[d0], %[d1]\n\t"
-      "v_pk_max_u16 %[e1], %[d2], %[d3]\n\t"
+  asm("v_pk_max_u16 %[e0], %[s0], %[s1]\n\t"
+      "v_pk_max_u16 %[e1], %[s2], %[s3]\n\t"
       "v_pk_max_u16 %[e], %[e0], %[e1]\n\t"
-      "v_pk_sub_u16 %[out], %[e], %[span] clamp"
+      "v_pk_sub_u16 %[out], %[e], %[top] clamp"
       : [e0] "=&v"(e0), [e1] "=&v"(e1), [e] "=&v"(e), [out] "=&v"(out)
-      : [d0] "v"(d[0]), [d1] "v"(d[1]), [d2] "v"(d[2]), [d3] "v"(d[3]), [span] "v"(0x14001400u));
+      : [s0] "v"(sl[0]), [s1] "v"(sl[1]), [s2] "v"(sl[2]), [s3] "v"(sl[3]), [top] "v"(0x27FF27FFu));
   return out;
 }
 
@@ -339,25 +326,15 @@ struct WindowHook {
 
   __device__ __forceinline__ explicit WindowHook(uint32_t* w) : win(w), ninf(0), odd(false) {}
 
-  __device__ __forceinline__ void outside(uint32_t b) {
-    if (b == kNegInfBits) {
+  // One token: its exact slot (zero class included), or the outside tally.
+  __device__ __forceinline__ void one(uint32_t b) {
+    const uint32_t slot = window_slot(b);
+    if (slot != kSlotOut) {
+      atomicAdd(&win[slot], 1u);
+    } else if (b == kNegInfBits) {
       ++ninf;
     } else {
       odd = true;
-    }
-  }
-
-  // One by one: the exact slot of each value, or the outside tally.
-  __device__ __forceinline__ void each(const uint32_t (&w)[4]) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t b = (w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-      const uint32_t slot = window_slot(b);
-      if (slot < static_cast<uint32_t>(kWin)) {
-        atomicAdd(&win[slot], 1u);
-      } else {
-        outside(b);
-      }
     }
   }
 
@@ -366,59 +343,26 @@ struct WindowHook {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t slots[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) slots[i] = window_slots2_unchecked(w[i]);
-    if (vector_outside_core(w) == 0u) {  // all 8 values in the window
+    for (int i = 0; i < 4; ++i) slots[i] = window_slots2(w[i]);
+    if (slots_outside(slots) == 0u) {  // all 8 values in the window
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         atomicAdd(&win[slots[i] & 0xFFFFu], 1u);
         atomicAdd(&win[slots[i] >> 16], 1u);
       }
-    } else {  // rare: a value that may lie outside the window
-      each(w);
+    } else {  // rare: a zero, -inf or a value outside the window, taken one by one
+#pragma unroll
+      for (int e = 0; e < 8; ++e) one((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
     }
   }
 
-  // v: one vector of 8 BF16 columns as loaded (column 2i in the low half of
-  // word i); x: their float32 widenings; nvalid of them are real.
+  // v: one vector of 8 BF16 columns as loaded; x: their float32 widenings;
+  // nvalid of them are real (the first nvalid).
   __device__ __forceinline__ void operator()(const u32x4& v, const float (&x)[8], int nvalid) {
     if (nvalid == 8) {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint32_t slots[4];
-      uint32_t out = 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t o;
-        slots[i] = window_slots2(w[i], o);
-        out |= o;
-      }
-      if (out == 0u) {  // all 8 values in the window
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          atomicAdd(&win[slots[i] & 0xFFFFu], 1u);
-          atomicAdd(&win[slots[i] >> 16], 1u);
-        }
-      } else {  // rare: a value outside the window, taken one by one
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t b = (w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-          const uint32_t slot = window_slot(b);
-          if (slot < static_cast<uint32_t>(kWin)) {
-            atomicAdd(&win[slot], 1u);
-          } else {
-            outside(b);
-          }
-        }
-      }
+      full(v);
     } else {
-      for (int e = 0; e < nvalid; ++e) {
-        const uint32_t b = __float_as_uint(x[e]) >> 16;
-        const uint32_t slot = window_slot(b);
-        if (slot < static_cast<uint32_t>(kWin)) {
-          atomicAdd(&win[slot], 1u);
-        } else {
-          outside(b);
-        }
-      }
+      for (int e = 0; e < nvalid; ++e) one(__float_as_uint(x[e]) >> 16);
     }
   }
 
@@ -436,7 +380,7 @@ struct WindowHook {
 
 template <typename Lds>
 __device__ __forceinline__ void window_clear(Lds& L) {
-  for (int i = threadIdx.x; i < (kWin + 2) / 2; i += kNucThreads) L.u.win_pairs[i] = 0ull;
+  for (int i = threadIdx.x; i < kWinWords / 2; i += kNucThreads) L.u.win_pairs[i] = 0ull;
 }
 
 // One pass over the row that fills the window (when the streaming pass did not).
@@ -479,31 +423,71 @@ __device__ __forceinline__ int wave_min(int v) {
 // ---------------------------------------------------------------------------
 // Fast path, in one wavefront (no block barriers), for a row whose every real
 // token is in the window or is -inf (the hook totals say so). The row maximum
-// is the top non-empty slot, R = ceil(fl32(M*c)), and a class (slot) weighs
+// is the first non-empty class, R = ceil(fl32(M*c)), and a class weighs
 // count * floor(2^(x*c - R) * 2^40): exactly the integers the general path
-// sums per token. Scans from the top find the top-k boundary (count >= k)
+// sums per token. Scans in value order find the top-k boundary (count >= k)
 // and then the top-p boundary (cumulative mass >= ceil(p * Z_k), an exact
-// integer test). Lane l reads the window four slots at a time (slots 4q ..
-// 4q+3, q = q0 + l), so a round covers 256 consecutive slots; prefix sums
-// come from a lane-local scan of its four slots plus a DPP scan of the lane
-// totals, and a crossing is located with a ballot. Every value it returns is
-// wave-uniform.
+// integer test). The classes are visited in steps of 256 ranks: the positive
+// slots in 20 steps, the zero class alone, the negative slots in 20 steps. In
+// a step lane l holds ranks 4l .. 4l+3 (two 16-byte LDS reads cover the 8
+// interleaved slots of its 4 magnitudes); prefix sums come from a lane-local
+// scan plus a DPP scan of the lane totals, and a crossing is located with a
+// ballot. Every value it returns is wave-uniform.
 // ---------------------------------------------------------------------------
 struct FastSupport {
   float R;
-  int kappa;       // last kept class (window slot), or kWin for the -inf class
+  int kappa;       // rank of the last kept class, or kNoRank for the -inf class
   uint32_t cnt_s;  // tokens in the support
   u64 z_s;         // support mass (2^-40 units relative to 2^R)
 };
 
-constexpr int kWinQuads = kWin / 4;
+constexpr int kStepRanks = 4 * kWave;           // 256 ranks per step
+constexpr int kPosSteps = kNMag / kStepRanks;   // 20
+constexpr int kZeroStep = kPosSteps;
+constexpr int kSteps = 2 * kPosSteps + 1;
+static_assert(kNMag % kStepRanks == 0, "steps cover whole magnitude ranges");
 
-__device__ __forceinline__ void window_quad(const NucLds& L, int q, uint32_t (&cnt)[4]) {
-  const uint4 v = *reinterpret_cast<const uint4*>(&L.u.win[4 * q]);
-  cnt[0] = v.x;
-  cnt[1] = v.y;
-  cnt[2] = v.z;
-  cnt[3] = v.w;
+// Rank of element e of lane `lane` in step s (-1 for the unused elements of
+// the zero step).
+__device__ __forceinline__ int step_rank(int s, int lane, int e) {
+  if (s < kPosSteps) return s * kStepRanks + 4 * lane + e;
+  if (s == kZeroStep) return (lane == 0 && e == 0) ? kZeroRank : -1;
+  return kNMag + 1 + (s - kPosSteps - 1) * kStepRanks + 4 * lane + e;
+}
+
+// Step holding a rank (rank < kRanks).
+__device__ __forceinline__ int rank_step(int r) {
+  if (r < kNMag) return r / kStepRanks;
+  if (r == kZeroRank) return kZeroStep;
+  return kPosSteps + 1 + (r - kNMag - 1) / kStepRanks;
+}
+
+// Counts of the four ranks that `lane` holds in step s.
+__device__ __forceinline__ void step_counts(const NucLds& L, int s, int lane, uint32_t (&cnt)[4]) {
+  if (s == kZeroStep) {
+    cnt[0] = (lane == 0) ? L.u.win[kZeroSlot] : 0u;
+    cnt[1] = 0u;
+    cnt[2] = 0u;
+    cnt[3] = 0u;
+  } else if (s < kPosSteps) {
+    // ranks r .. r+3 are magnitude indices k .. k-3 (even slots 2k .. 2k-6)
+    const int g = 2 * (kNMag - 4) - 8 * (s * kWave + lane);
+    const uint4 a = *reinterpret_cast<const uint4*>(&L.u.win[g]);
+    const uint4 b = *reinterpret_cast<const uint4*>(&L.u.win[g + 4]);
+    cnt[0] = b.z;
+    cnt[1] = b.x;
+    cnt[2] = a.z;
+    cnt[3] = a.x;
+  } else {
+    // ranks r .. r+3 are negative magnitude indices k .. k+3 (odd slots)
+    const int g = 8 * ((s - kPosSteps - 1) * kWave + lane);
+    const uint4 a = *reinterpret_cast<const uint4*>(&L.u.win[g]);
+    const uint4 b = *reinterpret_cast<const uint4*>(&L.u.win[g + 4]);
+    cnt[0] = a.y;
+    cnt[1] = a.w;
+    cnt[2] = b.y;
+    cnt[3] = b.w;
+  }
 }
 
 __device__ __forceinline__ u64 readlane_u64(u64 v, int l) {
@@ -516,28 +500,22 @@ __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int l) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
 }
 
-// One round of 64 quads from quad q0: per-slot counts and masses, and the
-// inclusive cumulative count and mass of each slot counted from the round's
-// first slot (lane-local prefix plus the exclusive DPP scan of the lanes).
-// Returns the round's totals through rc / rm, and false (wave-uniform, with
-// zero totals and Q left unset) when all 256 slots are empty.
-struct QuadRound {
+// One step: per-class counts and masses, and the inclusive cumulative count
+// and mass of each class counted from the step's first class (lane-local
+// prefix plus the exclusive DPP scan of the lanes). Returns the step's totals
+// through rc / rm, and false (wave-uniform, with zero totals and Q left
+// unset) when all its classes are empty.
+struct StepRound {
   uint32_t cnt[4];
   u64 mass[4];
   uint32_t cum_c[4];
   u64 cum_m[4];
 };
 
-__device__ __forceinline__ bool quad_round(const NucLds& L, int q0, float c, float nr, QuadRound& Q, uint32_t& rc,
+__device__ __forceinline__ bool step_round(const NucLds& L, int s, float c, float nr, StepRound& Q, uint32_t& rc,
                                            u64& rm) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int q = q0 + lane;
-  if (q < kWinQuads) {
-    window_quad(L, q, Q.cnt);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Q.cnt[e] = 0u;
-  }
+  step_counts(L, s, lane, Q.cnt);
   if (__ballot((Q.cnt[0] | Q.cnt[1] | Q.cnt[2] | Q.cnt[3]) != 0u) == 0ull) {  // wave-uniform
     rc = 0u;
     rm = 0ull;
@@ -549,8 +527,7 @@ __device__ __forceinline__ bool quad_round(const NucLds& L, int q0, float c, flo
   for (int e = 0; e < 4; ++e) {
     u64 m = 0;
     if (Q.cnt[e]) {
-      const int j = 4 * q + e;
-      const float t = fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(j)) << 16), c, nr);
+      const float t = fmaf(rank_value(step_rank(s, lane, e)), c, nr);
       if (t >= -42.0f) m = static_cast<u64>(Q.cnt[e]) * fixed40(__builtin_amdgcn_exp2f(t));
     }
     Q.mass[e] = m;
@@ -582,60 +559,74 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
   for (int w = 0; w < kNucWaves; ++w) ninf_n += L.red_u32[w][1];
   const uint32_t total_c = static_cast<uint32_t>(vocab_real) - ninf_n;
 
-  // the row maximum: the first non-empty slot, at most the slot of the
-  // largest shard-summary m (each is a token of the row)
+  // the row maximum: the first non-empty class, at or above the class of the
+  // largest shard-summary m (each is a token of the row, so it lies in the
+  // window); two steps per iteration, reads first
   float mb = -INFINITY;
 #pragma unroll
   for (int sh = 0; sh < kShards; ++sh) mb = fmaxf(mb, L.sm[sh].m);
-  int jtop = kWin;
+  int jtop = kNoRank;
   if (mb > -INFINITY) {
-    const int qb = min(static_cast<int>(window_slot(__float_as_uint(mb) >> 16)), kWin - 1) / 4;
-    for (int q0 = 0; q0 <= qb; q0 += kWave) {
-      const int q = q0 + lane;
-      int j = kWin;
-      if (q <= qb) {
-        uint32_t cnt[4];
-        window_quad(L, q, cnt);
+    const uint32_t sl = window_slot(__float_as_uint(mb) >> 16);
+    const int sb = (sl == kSlotOut) ? kSteps - 1 : rank_step(slot_rank(sl));
+    for (int s0 = 0; s0 <= sb; s0 += 2) {
+      uint32_t c0[4], c1[4];
+      step_counts(L, s0, lane, c0);
+      const bool two = s0 + 1 <= sb;
+      if (two) {
+        step_counts(L, s0 + 1, lane, c1);
+      } else {
 #pragma unroll
-        for (int e = 3; e >= 0; --e)
-          if (cnt[e]) j = 4 * q + e;
+        for (int e = 0; e < 4; ++e) c1[e] = 0u;
+      }
+      int j = kNoRank;
+#pragma unroll
+      for (int e = 3; e >= 0; --e)
+        if (c1[e]) j = step_rank(s0 + 1, lane, e);
+#pragma unroll
+      for (int e = 3; e >= 0; --e)
+        if (c0[e]) j = step_rank(s0, lane, e);
+      // the first step's ranks all precede the second's, so the minimum over
+      // lanes of (step 0 hit, else step 1 hit) is the first non-empty rank
+      // only once step 0 is known empty in every lane
+      const bool hit0 = (c0[0] | c0[1] | c0[2] | c0[3]) != 0u;
+      if (__ballot(hit0)) {  // wave-uniform
+        jtop = wave_min(hit0 ? j : kNoRank);
+        break;
       }
       jtop = wave_min(j);
-      if (jtop < kWin) break;  // wave-uniform
+      if (jtop < kNoRank) break;  // wave-uniform
     }
   }
-  out.kappa = kWin;
+  out.kappa = kNoRank;
   out.cnt_s = total_c + ninf_n;
   out.z_s = 0;
   out.R = 0.0f;
-  if (jtop == kWin) return out;  // no finite token: not reached on a searched row
-  const float m = __uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(jtop)) << 16);
+  if (jtop == kNoRank) return out;  // no finite token: not reached on a searched row
+  const float m = rank_value(jtop);
   const float R = ref_exponent(m, c);
   const float nr = -R;
   out.R = R;
-  const int qfirst = jtop / 4;
+  const int sfirst = rank_step(jtop);
 
-  // exact mass of the slots from quad q_start on: every slot with a nonzero
-  // weight lies before the first quad whose first slot is below 2^-42 (slots
-  // are in decreasing value order)
-  auto exact_mass_from = [&](int q_start) -> u64 {
+  // exact mass of the classes from step s_start on: every class with a
+  // nonzero weight lies before the first step whose first class is below 2^-42
+  // (the classes are in decreasing value order)
+  auto exact_mass_from = [&](int s_start) -> u64 {
     u64 tm = 0;
-    for (int q0 = q_start; q0 < kWinQuads; q0 += kWave) {
-      const int q0s = 4 * q0;
-      if (q0 > qfirst &&
-          fmaf(__uint_as_float(crank_bits(kWinHi - static_cast<uint32_t>(q0s)) << 16), c, nr) < -42.0f)
-        break;  // wave-uniform
-      QuadRound Q;
+    for (int s = s_start; s < kSteps; ++s) {
+      if (s > sfirst && fmaf(rank_value(step_rank(s, 0, 0)), c, nr) < -42.0f) break;  // wave-uniform
+      StepRound Q;
       uint32_t rc;
       u64 rm;
-      quad_round(L, q0, c, nr, Q, rc, rm);
+      step_round(L, s, c, nr, Q, rc, rm);
       tm += rm;
     }
     return tm;
   };
 
   // top-k boundary by count (the -inf class when the window holds fewer than k)
-  int jk = kWin;
+  int jk = kNoRank;
   uint32_t cnt_k = total_c + ninf_n;
   u64 z_k = 0;
   bool z_k_known = false;  // otherwise z_k is the row's total mass, not yet summed
@@ -643,11 +634,11 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
     const uint64_t k = static_cast<uint64_t>(k_in);
     uint32_t carry_c = 0;
     u64 carry_m = 0;
-    for (int q0 = qfirst; q0 < kWinQuads; q0 += kWave) {
-      QuadRound Q;
+    for (int s = sfirst; s < kSteps; ++s) {
+      StepRound Q;
       uint32_t rc;
       u64 rm;
-      if (!quad_round(L, q0, c, nr, Q, rc, rm)) continue;  // no token in these 256 slots
+      if (!step_round(L, s, c, nr, Q, rc, rm)) continue;  // no token in this step
       int hit_e = -1;
 #pragma unroll
       for (int e = 3; e >= 0; --e) {
@@ -666,7 +657,7 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
             hc = Q.cum_c[e];
             hm = Q.cum_m[e];
           }
-        jk = 4 * (q0 + hl) + he;
+        jk = step_rank(s, hl, he);
         cnt_k = carry_c + readlane_u32(hc, hl);
         z_k = carry_m + readlane_u64(hm, hl);
         z_k_known = true;
@@ -681,32 +672,33 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
   // cumulative mass reaches P = ceil(p * z_k). Scanning for thresholds
   // p_lo <= P <= p_hi finds classes j_lo <= j* <= j_hi (cumulative masses only
   // grow), so j_lo == j_hi decides j* exactly. A scan runs from a position
-  // (round start and the count and mass of every slot before it) and leaves
-  // the position after the round where it found p_hi's crossing (or at the
-  // end of the window); `lo_pos` is the start of the round holding j_lo.
+  // (a step and the count and mass of every class before it) and leaves the
+  // position after the step where it found p_hi's crossing (or at the end of
+  // the classes); `lo_pos` is the start of the step holding j_lo.
   struct Hit {
     int j;
     uint32_t cnt;
     u64 mass;
   };
   struct ScanPos {
-    int q0;
+    int s;
     uint32_t c;
     u64 m;
   };
   auto scan_p = [&](ScanPos& pos, u64 p_lo, u64 p_hi, Hit& lo, ScanPos& lo_pos, int& j_hi) {
     lo.j = -1;
     j_hi = -1;
-    for (; pos.q0 < kWinQuads; pos.q0 += kWave) {
-      QuadRound Q;
+    for (; pos.s < kSteps; ++pos.s) {
+      StepRound Q;
       uint32_t rc;
       u64 rm;
-      if (!quad_round(L, pos.q0, c, nr, Q, rc, rm)) continue;  // no token in these 256 slots
+      if (!step_round(L, pos.s, c, nr, Q, rc, rm)) continue;  // no token in this step
       int e_lo = -1, e_hi = -1;
 #pragma unroll
       for (int e = 3; e >= 0; --e) {
         const u64 cum = pos.m + Q.cum_m[e];
-        const bool inside = 4 * (pos.q0 + lane) + e <= jk;
+        const int r = step_rank(pos.s, lane, e);
+        const bool inside = r >= 0 && r <= jk;
         if (inside && cum >= p_lo && cum - Q.mass[e] < p_lo) e_lo = e;
         if (inside && cum >= p_hi && cum - Q.mass[e] < p_hi) e_hi = e;
       }
@@ -722,7 +714,7 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
             hc = Q.cum_c[e];
             hm = Q.cum_m[e];
           }
-        lo.j = 4 * (pos.q0 + hl) + he;
+        lo.j = step_rank(pos.s, hl, he);
         lo.cnt = pos.c + readlane_u32(hc, hl);
         lo.mass = pos.m + readlane_u64(hm, hl);
         lo_pos = pos;
@@ -732,8 +724,8 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
       const u64 b_hi = __ballot(e_hi >= 0);
       if (b_hi) {  // wave-uniform
         const int hl = __builtin_ctzll(b_hi);
-        j_hi = 4 * (pos.q0 + hl) + __builtin_amdgcn_readlane(e_hi, hl);
-        pos.q0 += kWave;
+        j_hi = step_rank(pos.s, hl, __builtin_amdgcn_readlane(e_hi, hl));
+        ++pos.s;
         break;
       }
     }
@@ -744,8 +736,8 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
   u64 z_s = z_k;
   if (p_active) {
     Hit lo;
-    ScanPos lo_pos = {qfirst, 0u, 0ull};
-    ScanPos pos = {qfirst, 0u, 0ull};
+    ScanPos lo_pos = {sfirst, 0u, 0ull};
+    ScanPos pos = {sfirst, 0u, 0ull};
     int j_hi = -1;
     bool decided = false;
     if (!z_k_known) {
@@ -775,12 +767,12 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
       scan_p(pos, ceil_mul(p, z_lo), ceil_mul(p, z_hi), lo, lo_pos_b, j_hi);
       decided = (lo.j >= 0) && (lo.j == j_hi);
       if (!decided) {
-        // the exact total: the scanned slots' mass plus the mass below them
-        z_k = pos.m + exact_mass_from(pos.q0);
+        // the exact total: the scanned classes' mass plus the mass below them
+        z_k = pos.m + exact_mass_from(pos.s);
         z_k_known = true;
         // P >= ceil(p * z_lo), so the exact crossing is not above j_lo: the
-        // exact scan restarts at the round holding j_lo
-        pos = (lo.j >= 0) ? lo_pos_b : ScanPos{qfirst, 0u, 0ull};
+        // exact scan restarts at the step holding j_lo
+        pos = (lo.j >= 0) ? lo_pos_b : ScanPos{sfirst, 0u, 0ull};
       }
     }
     if (!decided) {
@@ -1044,13 +1036,13 @@ __device__ __forceinline__ void write_unsearched(int64_t row, const RowStart& rs
 }
 
 // Policy logprob and support record of a searched row. `fast`: kappa is a
-// window slot (kWin = the -inf class); otherwise a key16 (general path).
+// rank (kNoRank = the -inf class); otherwise a key16 (general path).
 __device__ __forceinline__ void write_policy(int64_t row, int64_t vocab_real, bool fast, int kappa, uint32_t cnt_s,
                                              u64 z_s, float R, const RowStart& rs, float t,
                                              float* __restrict__ policy_out, rlk_support_state* __restrict__ state_out) {
   const uint32_t bt = rs.bt;
-  const int tclass = (bt == kNegInfBits) ? kWin : static_cast<int>(window_slot(bt));
-  const bool in_support = fast ? (tclass <= kappa) : (static_cast<int>(key16(bt)) >= kappa);
+  const int trank = (bt == kNegInfBits) ? kNoRank : slot_rank(window_slot(bt));
+  const bool in_support = fast ? (trank <= kappa) : (static_cast<int>(key16(bt)) >= kappa);
   const float zt = __uint_as_float(bt << 16) / t;  // IEEE float32 division
   const bool whole = static_cast<int64_t>(cnt_s) == vocab_real;
   const double lse_s = (static_cast<double>(R) + (log2(static_cast<double>(z_s)) - 40.0)) * kLn2;
@@ -1067,7 +1059,7 @@ __device__ __forceinline__ void write_policy(int64_t row, int64_t vocab_real, bo
     rlk_support_state st;
     st.lse_support = whole ? rs.lse : static_cast<float>(lse_s);
     st.threshold = whole ? -INFINITY
-                         : (fast ? (kappa >= kWin ? -INFINITY : slot_value(kappa))
+                         : (fast ? (kappa >= kNoRank ? -INFINITY : rank_value(kappa))
                                  : key_value(static_cast<uint32_t>(kappa)));
     st.status = in_support ? 1 : 0;
     st.reserved = 0;

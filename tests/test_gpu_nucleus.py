@@ -161,13 +161,16 @@ def test_top_p_near_one_and_bracket_edges():
     check(logits, vr, temps, top_p, top_k, targets, "top-p near 1, uniform targets", groups_list=(1, 8))
 
 
-# BF16 patterns at and just past the ends of the value ranges a 16-bit rank
-# window can cover: the top (65536 and the next value), the smallest
-# magnitudes (2^-24 and the next smaller value, both signs) and two pairs of
-# large negative values (-4.24e9 / -4.26e9 and -1.823e19 / -1.830e19); and
+# BF16 patterns at and just past the ends of the support window's value
+# ranges: the top (65535.x is the largest magnitude inside, 65536 and the next
+# value outside, both signs), the smallest magnitudes (2^-24 inside, the next
+# smaller value outside, both signs), +-0 (a class of the window), large
+# negative values (-4.24e9 / -4.26e9 and -1.823e19 / -1.830e19, outside), and
 # values inside it around +-256.
 EDGE_BITS = [0x4380, 0x4381, 0xC37D, 0xC37E, 0x437E, 0x3380, 0x337F, 0xB380, 0xB37F,
-             0x4780, 0x4781, 0xCF7D, 0xCF7E, 0xDF7D, 0xDF7E]
+             0x477F, 0x4780, 0x4781, 0xC77F, 0xC780, 0x0000, 0x8000,
+             0xCF7D, 0xCF7E, 0xDF7D, 0xDF7E]
+OUTSIDE_WINDOW = {0x337F, 0xB37F, 0x4780, 0x4781, 0xC780, 0xCF7D, 0xCF7E, 0xDF7D, 0xDF7E}
 
 
 def test_window_edge_values():
@@ -255,20 +258,19 @@ def qwen_logits():
     return w, logits, targets
 
 
-def general_path_rows(logits, vocab_real, chunk=512):
+def general_path_rows(logits, vocab_real, chunk=512, zeros=False):
     """Rows that the kernel sends to its general path, found from the BF16 bits:
-    a real token with magnitude below 2^-24 (biased exponent below 103, zeros
-    included) or a finite value outside [-4.24e9, 65536] (the 16-bit rank
-    window, patterns 0xCF7D..0x4780 for negatives and positives)."""
+    a real token other than -inf and +-0 whose magnitude is below 2^-24 or at
+    least 65536 (NaN and +-inf included). With `zeros`, also the rows holding a
+    +-0, which the window's zero class takes."""
     out = []
     for r0 in range(0, logits.shape[0], chunk):
         b = logits[r0:r0 + chunk, :vocab_real]
         mag = b & np.uint16(0x7FFF)
-        tiny = mag < np.uint16(0x3380)
-        neg = (b & np.uint16(0x8000)) != 0
-        big = (mag > np.uint16(0x4780)) & ~neg & (mag < np.uint16(0x7F80))
-        far_neg = neg & (b > np.uint16(0xCF7D)) & (b < np.uint16(0xFF80))
-        hit = (tiny | big | far_neg).any(axis=1)
+        outside = ((mag < np.uint16(0x3380)) | (mag >= np.uint16(0x4780))) & (mag != 0) & (b != np.uint16(0xFF80))
+        if zeros:
+            outside |= mag == 0
+        hit = outside.any(axis=1)
         out.extend((np.flatnonzero(hit) + r0).tolist())
     return np.array(out, dtype=np.int64)
 
@@ -279,10 +281,11 @@ def test_general_path_row_predicate():
     rows = np.full((len(EDGE_BITS), vr), datagen.f32_to_bf16_bits(np.float32([1.0]))[0], dtype=np.uint16)
     for i, b in enumerate(EDGE_BITS):
         rows[i, 3] = b
+    rows[0, 5] = datagen.BF16_NEG_INF
     got = set(general_path_rows(rows, vr).tolist())
-    outside = {0x4781, 0x337F, 0xB37F, 0xCF7E, 0xDF7D, 0xDF7E}
-    want = {i for i, b in enumerate(EDGE_BITS) if b in outside}
-    assert got == want
+    assert got == {i for i, b in enumerate(EDGE_BITS) if b in OUTSIDE_WINDOW}
+    got = set(general_path_rows(rows, vr, zeros=True).tolist())
+    assert got == {i for i, b in enumerate(EDGE_BITS) if b in OUTSIDE_WINDOW or b in (0, 0x8000)}
 
 
 def compare_rows(logits, w, tg, pol, ref, rows, what):
@@ -299,13 +302,15 @@ def compare_rows(logits, w, tg, pol, ref, rows, what):
 
 def test_full_size_nucleus_sampled(qwen_logits):
     """8192 x 152576, T = 0.7, top-p 0.95, top-k off, in the benchmark's launch
-    configuration: 40 sampled rows and every row that takes the general path
-    get targets from their oracle nucleus; reference bytes equal
-    rlk_logp_full's. No sampled row may match only a neighbouring top-p cut."""
+    configuration: 40 sampled rows and every row holding a zero (the window's
+    zero class) or a token outside the window (the general path) get targets
+    from their oracle nucleus; reference bytes equal rlk_logp_full's. No
+    sampled row may match only a neighbouring top-p cut."""
     w, logits, targets = qwen_logits
     rows = np.random.default_rng(3003).choice(w.n_rows, 40, replace=False)
-    gen = general_path_rows(logits, w.vocab_real)
-    say(f"general-path rows in the workload: {len(gen)}")
+    gen = general_path_rows(logits, w.vocab_real, zeros=True)
+    report(f"nucleus full: {len(general_path_rows(logits, w.vocab_real))} general-path rows, "
+           f"{len(gen)} rows with a zero or a token outside the window")
     assert len(gen) >= 10
     tg = targets.copy()
     sel = np.union1d(rows, gen)
@@ -316,21 +321,22 @@ def test_full_size_nucleus_sampled(qwen_logits):
     assert np.isfinite(pol[sel]).all()
     _, n_alt = compare_rows(logits, w, tg, pol, ref, rows, "nucleus full, sampled rows")
     assert n_alt == 0
-    compare_rows(logits, w, tg, pol, ref, gen, "nucleus full, general-path rows")
+    compare_rows(logits, w, tg, pol, ref, gen, "nucleus full, rows with a zero or an outside token")
 
 
 def test_per_request_sampled():
     """64 requests x 128 rows, T in {0.7, 1.0, 1.3}, top-p in {0.95, 0.99},
-    top-k in {-1, 128}; two sampled rows per request, plus every row that takes
-    the general path."""
+    top-k in {-1, 128}; two sampled rows per request, plus every row holding a
+    zero or a token outside the window."""
     w = datagen.per_request()
     say("generating per-request workload")
     logits, targets = w.generate()
     rng = np.random.default_rng(4004)
     rows = np.array([r * 128 + int(rng.integers(0, 128)) for r in range(64)] +
                     [r * 128 + int(rng.integers(0, 128)) for r in range(64)])
-    gen = general_path_rows(logits, w.vocab_real)
-    say(f"general-path rows in the workload: {len(gen)}")
+    gen = general_path_rows(logits, w.vocab_real, zeros=True)
+    report(f"per-request: {len(general_path_rows(logits, w.vocab_real))} general-path rows, "
+           f"{len(gen)} rows with a zero or a token outside the window")
     assert len(gen) >= 10
     sel = np.union1d(rows, gen)
     tg = targets.copy()
@@ -340,7 +346,7 @@ def test_per_request_sampled():
         pol, ref, full = run_nucleus(logits, w.vocab_real, w.temperature, w.top_p, w.top_k, tg, groups)
         assert ref.tobytes() == full.tobytes()
         compare_rows(logits, w, tg, pol, ref, np.unique(rows), f"per-request g{groups}, sampled rows")
-        compare_rows(logits, w, tg, pol, ref, gen, f"per-request g{groups}, general-path rows")
+        compare_rows(logits, w, tg, pol, ref, gen, f"per-request g{groups}, rows with a zero or an outside token")
 
 
 def test_full_width_general_path_rows():
@@ -371,3 +377,50 @@ def test_full_width_general_path_rows():
     tg[::8] = rng.integers(0, vr, size=len(tg[::8]))     # some targets outside the support
     say("case: full-width general-path rows")
     check(logits, vr, temps, top_p, top_k, tg, "general path, full width", groups_list=(1, 8))
+
+
+def test_every_window_class_as_a_top_k_boundary():
+    """One row per class of the support window: each row holds every in-window
+    BF16 value once (both zeros included, column order shuffled per row) and
+    cuts top-k at a different class, so the support record's threshold must be
+    exactly the k-th largest value, for every class of the window in turn. A
+    sample of rows is compared with the oracle as well."""
+    import torch
+    mags = np.arange(0x3380, 0x4780, dtype=np.uint16)
+    vals_bits = np.concatenate([mags, mags | np.uint16(0x8000), np.array([0x0000, 0x8000], np.uint16)])
+    vals = datagen.bf16_bits_to_f32(vals_bits).astype(np.float64)
+    order = np.argsort(-vals, kind="stable")
+    sorted_vals = vals[order]
+    n_tok = len(vals_bits)                       # 10242 tokens, 10241 classes
+    vp = 10368                                   # multiple of 64
+    ks = np.arange(1, n_tok + 1)                 # k = n_tok disables top-k (threshold -inf)
+    n = len(ks)
+    rng = np.random.default_rng(91)
+    logits = np.full((n, vp), datagen.BF16_NEG_INF, dtype=np.uint16)
+    for i in range(n):
+        logits[i, :n_tok] = vals_bits[rng.permutation(n_tok)]
+    temps = np.ones(n, np.float32)
+    top_p = np.ones(n, np.float32)
+    top_k = ks.astype(np.int32)
+    am = np.argmax(datagen.bf16_bits_to_f32(logits[:, :n_tok]), axis=1).astype(np.int64)
+    say(f"case: every window class as a top-k boundary ({n} rows x {vp})")
+    lg = upload_logits(logits)
+    for groups in (1, 4):
+        pol, ref, lse, state = rlk.logp_nucleus(lg, upload(temps, torch.float32), upload(top_p, torch.float32),
+                                                upload(top_k, torch.int32), upload(am, torch.int64),
+                                                vocab_real=n_tok, groups=groups, return_state=True)
+        torch.cuda.synchronize()
+        _, thr, status = (to_host(a) for a in rlk.support_state_fields(state))
+        want_thr = sorted_vals[ks - 1]
+        want_thr = np.where(ks >= n_tok, -np.inf, want_thr)
+        bad = np.flatnonzero(thr.astype(np.float64) != want_thr)
+        assert bad.size == 0, f"groups {groups}: threshold wrong for k = {ks[bad[:5]]}: {thr[bad[:5]]} vs {want_thr[bad[:5]]}"
+        assert np.all(status == 1)
+        if groups == 1:
+            first = to_host(pol).tobytes()
+        else:
+            assert to_host(pol).tobytes() == first
+    sample = np.concatenate([np.arange(0, n, 97), [n - 1]])
+    want_pol, _, infos = O.nucleus_logp(logits[sample], n_tok, temps[sample], top_p[sample], top_k[sample], am[sample])
+    assert_nucleus_close(to_host(pol)[sample], want_pol, infos, what="window classes",
+                         tol=row_tolerance(logits[sample], n_tok, temps[sample]))

@@ -1,0 +1,80 @@
+"""Host check of the support window's slot arithmetic (no GPU).
+
+The nucleus kernel counts each BF16 token into a window of classes with
+magnitudes in [2^-24, 65536) of both signs, interleaved (slot
+2 * (m - 0x3380) + sign), plus a class for +-0. Two tokens packed in a 32-bit
+word get their slots from three packed 16-bit integer instructions (shift
+right by 15, multiply-add 2 * b + sign, subtract 2 * 0x3380); a slot below
+10240 means "in the window". This emulates those instructions' 16-bit
+wrap-around arithmetic on all 65536 patterns and checks:
+- the packed result equals the scalar definition for every in-window pattern
+  and is 10240 or more for every pattern outside (zeros, tiny and huge
+  magnitudes, infinities, NaN), in both halves of a word;
+- visiting the slots in the kernel's rank order (positive slots from the top,
+  the zero class, negative slots from the top) lists the in-window values in
+  strictly decreasing order, each exactly once.
+The classes are the BF16 values themselves (page "Configurable H100
+consistency runs", sampling paragraph: support over the real vocabulary; ties
+by value are one class).
+"""
+import numpy as np
+
+import datagen
+
+MAG_LO = 0x3380
+N_MAG = 5120
+WIN = 2 * N_MAG
+
+
+def packed_slots(words):
+    """v_pk_lshrrev_b16 15 / v_pk_mad_u16 (w, 2, sign) / v_pk_sub_u16 0x6700,
+    each on the two 16-bit halves independently, modulo 2^16."""
+    lo = (words & 0xFFFF).astype(np.uint32)
+    hi = (words >> 16).astype(np.uint32)
+
+    def half(b):
+        sgn = b >> 15
+        u = (b * 2 + sgn) & 0xFFFF
+        return (u - 2 * MAG_LO) & 0xFFFF
+
+    return half(lo), half(hi)
+
+
+def scalar_slot(b):
+    m = b & 0x7FFF
+    if m == 0:
+        return "zero"
+    k = m - MAG_LO
+    return 2 * k + (b >> 15) if 0 <= k < N_MAG else None
+
+
+def test_packed_slots_equal_the_scalar_map_on_every_pattern():
+    pats = np.arange(65536, dtype=np.uint32)
+    # every pattern in the low half with a varying high half, and the reverse
+    words = pats | (((pats * 40503) & 0xFFFF) << 16)
+    for words_, which in ((words, 0), (((pats << 16) | ((pats * 40503) & 0xFFFF)), 1)):
+        lo, hi = packed_slots(words_)
+        got = lo if which == 0 else hi
+        for b in range(65536):
+            want = scalar_slot(b)
+            g = int(got[b])
+            if want is None or want == "zero":
+                assert g >= WIN, hex(b)
+            else:
+                assert g == want, hex(b)
+
+
+def test_rank_order_is_value_order():
+    ranks = []
+    for k in range(N_MAG - 1, -1, -1):           # positive slots, largest magnitude first
+        ranks.append(MAG_LO + k)
+    ranks.append(0)                                # the zero class
+    for k in range(N_MAG):                         # negative slots, smallest magnitude first
+        ranks.append(0x8000 | (MAG_LO + k))
+    vals = datagen.bf16_bits_to_f32(np.array(ranks, dtype=np.uint16)).astype(np.float64)
+    assert np.all(np.diff(vals) < 0)
+    assert len(ranks) == WIN + 1
+    inside = [b for b in range(65536) if scalar_slot(b) not in (None, "zero")]
+    assert sorted(inside) == sorted(b for b in ranks if b != 0)
+    assert vals[0] == 65280.0 and vals[-1] == -65280.0
+    assert vals[N_MAG - 1] == 2.0 ** -24 and vals[N_MAG + 1] == -(2.0 ** -24)
