@@ -319,11 +319,23 @@ __device__ __forceinline__ void shard_pass(const u32x4* __restrict__ base, int n
       for (int u = 0; u < kU; ++u) v[u] = __builtin_nontemporal_load(base + first + u * kWave + lane);
       st.template consume_late<kU, true, true>(v, c, hook, unused);
     }
-    for (; first < nmain; first += kStep) {
+    if (first < nmain) {
+      // The next chunk's loads are issued before this chunk is consumed, so a
+      // wave keeps loads in flight while it works; the order of the terms is
+      // unchanged.
       u32x4 v[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) v[u] = __builtin_nontemporal_load(base + first + u * kWave + lane);
+      for (; first + kStep < nmain; first += kStep) {
+        u32x4 nv[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) nv[u] = __builtin_nontemporal_load(base + first + kStep + u * kWave + lane);
+        st.template consume_late<kU, false, true>(v, c, hook, unused);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) v[u] = nv[u];
+      }
       st.template consume_late<kU, false, true>(v, c, hook, unused);
+      first += kStep;
     }
     if (st.have_ref) {
       // The rest of the vectors, one per lane at a time. With the reference
