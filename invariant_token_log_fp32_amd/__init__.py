@@ -24,7 +24,9 @@ __all__ = [
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "librlk_logp.so")
+# RLK_LIBRARY names another build of the same library (the host-sanitizer build
+# that the CPU tests use); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("RLK_LIBRARY") or os.path.join(_PKG, "librlk_logp.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "rlk_logp.h")
 HEADER_PATHS = [HEADER_PATH] + [os.path.join(os.path.dirname(_PKG), "include", n) for n in ("rlk_norm.h", "rlk_linear.h")]
 N_SHARDS = 8

@@ -40,6 +40,34 @@ def hipcc() -> str:
     return exe
 
 
+# Host-side sanitizer build (CPU tests only): AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host code, i.e. the C ABI's argument
+# validation; the GPU code is built as usual.
+HOST_SANITIZER_FLAGS = [
+    "-O1", "-g",
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime (preloaded into a Python
+    process that loads the sanitized library), or '' when it is not found."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    for exe in (clang, "/opt/rocm/llvm/bin/clang", shutil.which("clang") or ""):
+        if exe and os.path.exists(exe):
+            res = subprocess.run([exe, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+            path = res.stdout.strip()
+            if res.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+                return path
+    return ""
+
+
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    """The library with HOST_SANITIZER_FLAGS, written to `out` (outside the package)."""
+    return build(HOST_SANITIZER_FLAGS, out=out, verbose=verbose)
+
+
 def build(extra_flags=(), out: str = LIB, verbose: bool = False) -> str:
     tmp = out + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-I", os.path.join(PKG, "csrc"), "-o", tmp, *SRCS]
