@@ -171,61 +171,79 @@ __device__ __forceinline__ u64 readlane64(u64 v, int lane) {
   return (static_cast<u64>(hi) << 32) | lo;
 }
 
+// The exact sum of the squares from the accumulator words, rounded once to
+// float64 (one wave; wave-uniform result). v[k] holds word k * 64 + lane (the
+// bins); n_nan / n_inf are the two count words. `stage` is 256 words of LDS.
+// Bin e weighs 2^(max(e,1) - 1) units of 2^-149. Lanes 0..7 first sum the 32
+// bins of group g = lane exactly into 128 bits (each bin is below 2^63 and is
+// shifted by at most 31 bits, so 32 of them stay below 2^100); the 8 group
+// sums are then added into a 384-bit integer at their offsets.
+__device__ __forceinline__ double exact_sum(const u64 (&v)[4], u64 n_nan, u64 n_inf, u64* stage) {
+  if (n_nan != 0ull) return NAN;
+  if (n_inf != 0ull) return INFINITY;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) stage[k * 64 + lane] = v[k];
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  u64 lo = 0ull, hi = 0ull;
+  if (lane < 8) {
+#pragma unroll 4
+    for (int j = 0; j < 32; ++j) {
+      const int e = 32 * lane + j;
+      const u64 b = stage[e];
+      const int sh = (lane == 0) ? (e > 0 ? e - 1 : 0) : j;  // (max(e,1) - 1) - (group offset)
+      const u64 add_lo = b << sh;
+      const u64 add_hi = sh ? (b >> (64 - sh)) : 0ull;
+      const u64 t = lo + add_lo;
+      hi += add_hi + (t < lo ? 1ull : 0ull);
+      lo = t;
+    }
+  }
+  Big a = {{0ull, 0ull, 0ull, 0ull, 0ull, 0ull}};
+#pragma unroll 1
+  for (int g = 0; g < 8; ++g) {
+    const int off = (g == 0) ? 0 : 32 * g - 1;  // group g's offset in units of 2^-149
+    const u64 glo = readlane64(lo, g);
+    const u64 ghi = readlane64(hi, g);
+    if (glo) big_add_shifted(a, glo, off);
+    if (ghi) big_add_shifted(a, ghi, off + 64);
+  }
+  int top = -1;
+#pragma unroll
+  for (int i = 0; i < 6; ++i)
+    if (a.w[i]) top = 64 * i + 63 - __clzll(static_cast<long long>(a.w[i]));
+  if (top < 0) return 0.0;
+  if (top < 53) return ldexp(static_cast<double>(a.w[0]), -149);  // exact: fewer than 54 bits
+  const int lo_bit = top - 52;
+  u64 mant = big_bits53(a, lo_bit);
+  const bool round = big_bit(a, lo_bit - 1) != 0ull;
+  const bool sticky = big_any_below(a, lo_bit - 1);
+  int ex = lo_bit - 149;
+  if (round && (sticky || (mant & 1ull))) {
+    ++mant;
+    if (mant == (1ull << 53)) {
+      mant >>= 1;
+      ++ex;
+    }
+  }
+  return ldexp(static_cast<double>(mant), ex);
+}
+
 // One wave of 64 lanes. Lane l reads words l, l + 64, l + 128, l + 192 (the
-// bins) and lane 0 the NaN / inf counts; the exact sum is formed wave-
-// uniformly from the nonzero bins, rounded once to float64, and lane 0 writes
-// fl64(S) and fl32(sqrt). With kClear every word is then set to 0.
+// bins) and lane 0 the NaN / inf counts; lane 0 writes fl64(S) and
+// fl32(sqrt). With kClear every word is then set to 0.
 template <bool kClear>
 __global__ __launch_bounds__(64) void k_norm_finalize(u64* __restrict__ bins, double* __restrict__ sumsq_out,
                                                       float* __restrict__ norm_out) {
+  __shared__ u64 stage[kBins];
   const int lane = threadIdx.x;
   u64 v[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) v[k] = bins[k * 64 + lane];
   const u64 n_nan = readlane64(lane == 0 ? bins[kBins] : 0ull, 0);
   const u64 n_inf = readlane64(lane == 0 ? bins[kBins + 1] : 0ull, 0);
-  double s;
-  if (n_nan != 0ull) {
-    s = NAN;
-  } else if (n_inf != 0ull) {
-    s = INFINITY;
-  } else {
-    Big a = {{0ull, 0ull, 0ull, 0ull, 0ull, 0ull}};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      u64 mask = __ballot(v[k] != 0ull);
-      while (mask) {  // uniform
-        const int idx = __builtin_ctzll(mask);
-        mask &= mask - 1ull;
-        const int e = k * 64 + idx;
-        // bin e weighs 2^(max(e,1) - 150) = 2^(max(e,1) - 1) units of 2^-149
-        big_add_shifted(a, readlane64(v[k], idx), (e > 0 ? e : 1) - 1);
-      }
-    }
-    int top = -1;
-#pragma unroll
-    for (int i = 0; i < 6; ++i)
-      if (a.w[i]) top = 64 * i + 63 - __clzll(static_cast<long long>(a.w[i]));
-    if (top < 0) {
-      s = 0.0;
-    } else if (top < 53) {
-      s = ldexp(static_cast<double>(a.w[0]), -149);  // exact: fewer than 54 bits
-    } else {
-      const int lo = top - 52;
-      u64 mant = big_bits53(a, lo);
-      const bool round = big_bit(a, lo - 1) != 0ull;
-      const bool sticky = big_any_below(a, lo - 1);
-      int ex = lo - 149;
-      if (round && (sticky || (mant & 1ull))) {
-        ++mant;
-        if (mant == (1ull << 53)) {
-          mant >>= 1;
-          ++ex;
-        }
-      }
-      s = ldexp(static_cast<double>(mant), ex);
-    }
-  }
+  const double s = exact_sum(v, n_nan, n_inf, stage);
   if (lane == 0) {
     if (sumsq_out) *sumsq_out = s;
     if (norm_out) *norm_out = static_cast<float>(sqrt(s));
@@ -235,29 +253,30 @@ __global__ __launch_bounds__(64) void k_norm_finalize(u64* __restrict__ bins, do
   }
 }
 
-// x is 4-byte aligned; elements [0, head) precede the first 16-byte boundary,
-// nvec 16-byte vectors follow, then `tail` (< 4) elements.
-__global__ __launch_bounds__(kThreads) void k_norm_accumulate(const float* __restrict__ x, int head, int64_t nvec,
-                                                              int tail, u64* __restrict__ out) {
-  __shared__ u64 wb[kWaves][kBins];
+// Streams this workgroup's share of x into the per-wave LDS bins (cleared
+// here) and the lane's NaN / inf counts. x is 4-byte aligned; elements
+// [0, head) precede the first 16-byte boundary, nvec 16-byte vectors follow,
+// then `tail` (< 4) elements.
+template <int kU>
+__device__ __forceinline__ void stream_squares(const float* __restrict__ x, int head, int64_t nvec, int tail,
+                                               u64 (&wb)[kWaves][kBins], Counts& c) {
   for (int i = threadIdx.x; i < kWaves * kBins; i += kThreads) (&wb[0][0])[i] = 0ull;
   __syncthreads();
   u64* __restrict__ mine = wb[threadIdx.x / 64];
-  Counts c = {0u, 0u};
   if (blockIdx.x == 0) {
     if (static_cast<int>(threadIdx.x) < head) add_square(x[threadIdx.x], mine, c);
     const int tt = static_cast<int>(threadIdx.x) - 64;
     if (tt >= 0 && tt < tail) add_square(x[head + 4 * nvec + tt], mine, c);
   }
   const f32x4* __restrict__ xv = reinterpret_cast<const f32x4*>(x + head);
-  const int64_t step = static_cast<int64_t>(gridDim.x) * kThreads * kUnroll;
+  const int64_t step = static_cast<int64_t>(gridDim.x) * kThreads * kU;
   Window win = {1u, 0ull};
   int iter = 0;
-  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads * kUnroll + threadIdx.x; base < nvec;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads * kU + threadIdx.x; base < nvec;
        base += step) {  // lanes past the end leave at the last step
-    f32x4 v[kUnroll];
+    f32x4 v[kU];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int64_t i = base + static_cast<int64_t>(u) * kThreads;
       v[u] = (i < nvec) ? __builtin_nontemporal_load(xv + i) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -267,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_accumulate(const float* __res
       // makes the register path the common one
       uint32_t em = 0u;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kU; ++u) {
         const float q[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -280,27 +299,39 @@ __global__ __launch_bounds__(kThreads) void k_norm_accumulate(const float* __res
       win.lo = win.lo > kMaxLo ? kMaxLo : win.lo;
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kU; ++u) {
       add_square_win(v[u].x, win, mine, c);
       add_square_win(v[u].y, win, mine, c);
       add_square_win(v[u].z, win, mine, c);
       add_square_win(v[u].w, win, mine, c);
     }
-    if (++iter == kFlushIters) {
+    iter += kU / 4;
+    if (iter >= kFlushIters) {  // at most 16 values per lane per unit of iter since the last flush
       flush(win, mine);
       iter = 1;  // keep the window
     }
   }
   flush(win, mine);
-  // NaN / inf counts: wave sums, one atomic per wave when nonzero
-  uint32_t cn = c.nan, ci = c.inf;
+}
+
+// Wave sums of the NaN / inf counts (wave-uniform).
+__device__ __forceinline__ void wave_counts(Counts& c) {
   for (int o = 32; o >= 1; o >>= 1) {
-    cn += __shfl_xor(cn, o);
-    ci += __shfl_xor(ci, o);
+    c.nan += __shfl_xor(c.nan, o);
+    c.inf += __shfl_xor(c.inf, o);
   }
+}
+
+__global__ __launch_bounds__(kThreads) void k_norm_accumulate(const float* __restrict__ x, int head, int64_t nvec,
+                                                              int tail, u64* __restrict__ out) {
+  __shared__ u64 wb[kWaves][kBins];
+  Counts c = {0u, 0u};
+  stream_squares<kUnroll>(x, head, nvec, tail, wb, c);
+  // NaN / inf counts: wave sums, one atomic per wave when nonzero
+  wave_counts(c);
   if ((threadIdx.x & 63) == 0) {
-    if (cn) atomicAdd(&out[kBins], static_cast<u64>(cn));
-    if (ci) atomicAdd(&out[kBins + 1], static_cast<u64>(ci));
+    if (c.nan) atomicAdd(&out[kBins], static_cast<u64>(c.nan));
+    if (c.inf) atomicAdd(&out[kBins + 1], static_cast<u64>(c.inf));
   }
   __syncthreads();
   for (int b = threadIdx.x; b < kBins; b += kThreads) {
