@@ -199,6 +199,22 @@ def time_calls(fn, steps, warmup):
     return wall, ev0.elapsed_time(ev1) / steps
 
 
+def time_blocks(fn, steps, warmup, blocks):
+    """Secondary legs: `warmup` calls, then `blocks` blocks of `steps` calls each,
+    timed with HIP events on the launch stream. Returns the median block's time
+    per call (ms) and every block's. The chip's clock moves for tens of
+    milliseconds after a change of load (the shader clock measured 2.14 ->
+    1.65 -> 1.9 GHz over the first ~30 launches of the full-vocabulary step), so
+    the median of several blocks, not one short block, describes a kernel."""
+    fn_i = iter(range(1 << 30))
+    _, first = time_calls(lambda i: fn(next(fn_i)), steps, warmup)
+    per = [first]
+    for _ in range(blocks - 1):
+        _, ms = time_calls(lambda i: fn(next(fn_i)), steps, 0)
+        per.append(ms)
+    return float(np.median(per)), per
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,10 +318,10 @@ def main():
             rlk.logp_nucleus(lgs[i % 2], t, p, k, target, vocab_real=w.vocab_real, groups=args.groups,
                              policy_out=pol, ref_out=ref, workspace=wsn)
 
-        _, ms_n = time_calls(nstep, 30, 5)
+        ms_n, blk_n = time_blocks(nstep, 20, 10, 5)
         ab = bytes_nucleus(w.n_rows, w.vocab_real)
         sec.append({"workload": "nucleus: same logits, top-p 0.95, top-k off, T 0.7", "entry_point":
-                    "rlk_logp_nucleus", "ms_per_step": ms_n, "tokens_per_s": w.n_rows / (ms_n * 1e-3),
+                    "rlk_logp_nucleus", "ms_per_step": ms_n, "ms_blocks": blk_n, "tokens_per_s": w.n_rows / (ms_n * 1e-3),
                     "achieved_GBs": ab / (ms_n * 1e-3) / 1e9, "frac": ab / (ms_n * 1e-3) / 1e9 / HBM_PEAK_GBS})
         # backward of both terms (and of the reference term alone) from the nucleus forward's statistics
         lse = torch.empty(w.n_rows, dtype=torch.float32, device=dev)
@@ -318,13 +334,13 @@ def main():
         grad = torch.empty((w.n_rows, w.vocab_padded), dtype=torch.bfloat16, device=dev)
         for policy in (True, False):
             kw = dict(policy_logp=pol, support_state=state, grad_policy=g_p) if policy else {}
-            _, ms_b = time_calls(lambda i: rlk.logp_backward(
+            ms_b, blk_b = time_blocks(lambda i: rlk.logp_backward(
                 bufs[0], temp, tg, vocab_real=w.vocab_real, ref_logp=ref, lse=lse, grad_ref=g_r, out=grad, **kw),
-                20, 5)
+                20, 5, 3)
             bb = bytes_backward(w.n_rows, w.vocab_real, w.vocab_padded, policy)
             sec.append({"workload": "backward: same logits, " + ("reference + top-p 0.95 policy terms" if policy
                         else "reference term only") + ", BF16 gradient 8192 x 152576",
-                        "entry_point": "rlk_logp_backward", "ms_per_step": ms_b,
+                        "entry_point": "rlk_logp_backward", "ms_per_step": ms_b, "ms_blocks": blk_b,
                         "tokens_per_s": w.n_rows / (ms_b * 1e-3), "algorithmic_bytes_per_launch": bb,
                         "achieved_GBs": bb / (ms_b * 1e-3) / 1e9, "frac": bb / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS})
         del grad
@@ -333,9 +349,9 @@ def main():
         lg_r = (torch.from_numpy(lg_r.view(np.int16)).to(dev),) * 2
         prm = dict(t=torch.from_numpy(wr.temperature).to(dev), p=torch.from_numpy(wr.top_p).to(dev),
                    k=torch.from_numpy(wr.top_k).to(dev), target=torch.from_numpy(tg_r).to(dev))
-        _, ms_r = time_calls(lambda i: nstep(i, lgs=lg_r, **prm), 30, 5)
+        ms_r, blk_r = time_blocks(lambda i: nstep(i, lgs=lg_r, **prm), 20, 10, 5)
         sec.append({"workload": "per-request: 64 requests x 128 rows, T {0.7,1.0,1.3}, top-p {0.95,0.99}, "
-                    "top-k {-1,128}", "entry_point": "rlk_logp_nucleus", "ms_per_step": ms_r,
+                    "top-k {-1,128}", "entry_point": "rlk_logp_nucleus", "ms_per_step": ms_r, "ms_blocks": blk_r,
                     "tokens_per_s": wr.n_rows / (ms_r * 1e-3), "achieved_GBs": ab / (ms_r * 1e-3) / 1e9,
                     "frac": ab / (ms_r * 1e-3) / 1e9 / HBM_PEAK_GBS})
         del lg_r

@@ -550,6 +550,25 @@ __device__ __forceinline__ bool step_round(const NucLds& L, int s, float c, floa
   return true;
 }
 
+// Count and mass of the four classes that `lane` holds in step s (lane-local).
+__device__ __forceinline__ void step_lane_sums(const NucLds& L, int s, int lane, float c, float nr, uint32_t& pc,
+                                               u64& pm) {
+  uint32_t cnt[4];
+  step_counts(L, s, lane, cnt);
+  pc = 0u;
+  pm = 0ull;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (cnt[e]) {
+      const float t = fmaf(rank_value(step_rank(s, lane, e)), c, nr);
+      if (t >= -42.0f) pm += static_cast<u64>(cnt[e]) * fixed40(__builtin_amdgcn_exp2f(t));
+      pc += cnt[e];
+    }
+  }
+}
+
+constexpr int kBatch = 4;  // steps whose counts the row-maximum scan reads at once
+
 __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_t vocab_real, int shard_width,
                                                          bool k_active, int64_t k_in, bool p_active, float p,
                                                          float c) {
@@ -561,7 +580,7 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
 
   // the row maximum: the first non-empty class, at or above the class of the
   // largest shard-summary m (each is a token of the row, so it lies in the
-  // window); two steps per iteration, reads first
+  // window); kBatch steps per iteration, their LDS reads issued together
   float mb = -INFINITY;
 #pragma unroll
   for (int sh = 0; sh < kShards; ++sh) mb = fmaxf(mb, L.sm[sh].m);
@@ -569,33 +588,33 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
   if (mb > -INFINITY) {
     const uint32_t sl = window_slot(__float_as_uint(mb) >> 16);
     const int sb = (sl == kSlotOut) ? kSteps - 1 : rank_step(slot_rank(sl));
-    for (int s0 = 0; s0 <= sb; s0 += 2) {
-      uint32_t c0[4], c1[4];
-      step_counts(L, s0, lane, c0);
-      const bool two = s0 + 1 <= sb;
-      if (two) {
-        step_counts(L, s0 + 1, lane, c1);
-      } else {
+    for (int s0 = 0; s0 <= sb; s0 += kBatch) {
+      uint32_t cn[kBatch][4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) c1[e] = 0u;
+      for (int b = 0; b < kBatch; ++b) {
+        if (s0 + b <= sb) {
+          step_counts(L, s0 + b, lane, cn[b]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) cn[b][e] = 0u;
+        }
       }
-      int j = kNoRank;
+      int hit = -1;  // first step of the batch with a token (wave-uniform)
 #pragma unroll
-      for (int e = 3; e >= 0; --e)
-        if (c1[e]) j = step_rank(s0 + 1, lane, e);
+      for (int b = kBatch - 1; b >= 0; --b)
+        if (__ballot((cn[b][0] | cn[b][1] | cn[b][2] | cn[b][3]) != 0u)) hit = b;
+      if (hit >= 0) {
+        int j = kNoRank;
 #pragma unroll
-      for (int e = 3; e >= 0; --e)
-        if (c0[e]) j = step_rank(s0, lane, e);
-      // the first step's ranks all precede the second's, so the minimum over
-      // lanes of (step 0 hit, else step 1 hit) is the first non-empty rank
-      // only once step 0 is known empty in every lane
-      const bool hit0 = (c0[0] | c0[1] | c0[2] | c0[3]) != 0u;
-      if (__ballot(hit0)) {  // wave-uniform
-        jtop = wave_min(hit0 ? j : kNoRank);
+        for (int b = 0; b < kBatch; ++b)
+          if (b == hit) {
+#pragma unroll
+            for (int e = 3; e >= 0; --e)
+              if (cn[b][e]) j = step_rank(s0 + b, lane, e);
+          }
+        jtop = wave_min(j);
         break;
       }
-      jtop = wave_min(j);
-      if (jtop < kNoRank) break;  // wave-uniform
     }
   }
   out.kappa = kNoRank;
@@ -609,20 +628,20 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
   out.R = R;
   const int sfirst = rank_step(jtop);
 
-  // exact mass of the classes from step s_start on: every class with a
-  // nonzero weight lies before the first step whose first class is below 2^-42
-  // (the classes are in decreasing value order)
+  // exact mass of the classes from step s_start on: lane-local sums over the
+  // steps, one wave reduction. Every class with a nonzero weight lies before
+  // the first step whose first class is below 2^-42 (the classes are in
+  // decreasing value order).
   auto exact_mass_from = [&](int s_start) -> u64 {
-    u64 tm = 0;
+    u64 acc = 0;
     for (int s = s_start; s < kSteps; ++s) {
       if (s > sfirst && fmaf(rank_value(step_rank(s, 0, 0)), c, nr) < -42.0f) break;  // wave-uniform
-      StepRound Q;
-      uint32_t rc;
-      u64 rm;
-      step_round(L, s, c, nr, Q, rc, rm);
-      tm += rm;
+      uint32_t pc;
+      u64 pm;
+      step_lane_sums(L, s, lane, c, nr, pc, pm);
+      acc += pm;
     }
-    return tm;
+    return wave_total<u64>(acc);
   };
 
   // top-k boundary by count (the -inf class when the window holds fewer than k)
