@@ -23,8 +23,8 @@
 // plus one class for +-0; -inf tokens are counted apart (mass 0). The slots of
 // two tokens come from three packed 16-bit instructions, and one maximum over
 // a vector's eight slots tells whether all of them lie in the window. Classes
-// are visited in value order (positive slots from the top, then the zero
-// class, then negative slots from the bottom). With groups == 1 the
+// are visited in value order (positive slots from the largest magnitude down,
+// the zero class, negative slots from the smallest magnitude up). With groups == 1 the
 // shard-waves count while they stream the row for the reference logprob, so
 // the support costs no extra pass; otherwise one pass builds it. The row
 // maximum is the first non-empty class, class masses are count * weight, and
