@@ -567,7 +567,38 @@ __device__ __forceinline__ void step_lane_sums(const NucLds& L, int s, int lane,
   }
 }
 
-constexpr int kBatch = 4;  // steps whose counts the row-maximum scan reads at once
+constexpr int kBatch = 4;       // steps whose LDS reads a scan issues together
+constexpr int kRoundSteps = 3;  // steps a top-p scan takes class by class before it skips ahead
+
+// Count and mass of the classes that `lane` holds in steps s .. s + kBatch - 1
+// (steps at or past s_end count zero), summed lane-locally; the LDS reads of
+// the kBatch steps are issued before any of them is used.
+__device__ __forceinline__ void batch_lane_sums(const NucLds& L, int s, int s_end, int lane, float c, float nr,
+                                                uint32_t (&pc)[kBatch], u64 (&pm)[kBatch]) {
+  uint32_t cn[kBatch][4];
+#pragma unroll
+  for (int b = 0; b < kBatch; ++b) {
+    if (s + b < s_end) {
+      step_counts(L, s + b, lane, cn[b]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cn[b][e] = 0u;
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < kBatch; ++b) {
+    pc[b] = 0u;
+    pm[b] = 0ull;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (cn[b][e]) {
+        const float t = fmaf(rank_value(step_rank(s + b, lane, e)), c, nr);
+        if (t >= -42.0f) pm[b] += static_cast<u64>(cn[b][e]) * fixed40(__builtin_amdgcn_exp2f(t));
+        pc[b] += cn[b][e];
+      }
+    }
+  }
+}
 
 __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_t vocab_real, int shard_width,
                                                          bool k_active, int64_t k_in, bool p_active, float p,
@@ -632,14 +663,20 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
   // steps, one wave reduction. Every class with a nonzero weight lies before
   // the first step whose first class is below 2^-42 (the classes are in
   // decreasing value order).
+  // The steps from s_end on hold no class of nonzero weight: the first step
+  // after sfirst whose first (largest) class weighs 0, found by one ballot
+  // with lane l testing step l.
+  const u64 zero_from = __ballot(lane > sfirst && lane < kSteps &&
+                                 fmaf(rank_value(step_rank(lane < kSteps ? lane : 0, 0, 0)), c, nr) < -42.0f);
+  const int s_end = zero_from ? __builtin_ctzll(zero_from) : kSteps;
   auto exact_mass_from = [&](int s_start) -> u64 {
     u64 acc = 0;
-    for (int s = s_start; s < kSteps; ++s) {
-      if (s > sfirst && fmaf(rank_value(step_rank(s, 0, 0)), c, nr) < -42.0f) break;  // wave-uniform
-      uint32_t pc;
-      u64 pm;
-      step_lane_sums(L, s, lane, c, nr, pc, pm);
-      acc += pm;
+    for (int s = s_start; s < s_end; s += kBatch) {
+      uint32_t pc[kBatch];
+      u64 pm[kBatch];
+      batch_lane_sums(L, s, s_end, lane, c, nr, pc, pm);
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) acc += pm[b];
     }
     return wave_total<u64>(acc);
   };
@@ -707,7 +744,43 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
   auto scan_p = [&](ScanPos& pos, u64 p_lo, u64 p_hi, Hit& lo, ScanPos& lo_pos, int& j_hi) {
     lo.j = -1;
     j_hi = -1;
-    for (; pos.s < kSteps; ++pos.s) {
+    for (int n_round = 0; pos.s < kSteps; ++pos.s, ++n_round) {
+      if (n_round >= kRoundSteps) {
+        // skip ahead: the totals of the next kBatch steps carry the position
+        // up to the step where the pending threshold is crossed (cumulative
+        // masses only grow, so no class before it can be the crossing)
+        const u64 thr = (lo.j < 0) ? p_lo : p_hi;
+        uint32_t pc[kBatch];
+        u64 pm[kBatch];
+        batch_lane_sums(L, pos.s, s_end, lane, c, nr, pc, pm);
+        const u64 tm_all = wave_total<u64>((pm[0] + pm[1]) + (pm[2] + pm[3]));
+        if (pos.m + tm_all < thr) {  // wave-uniform: no crossing in the batch
+          pos.m += tm_all;
+          pos.c += wave_total<uint32_t>((pc[0] + pc[1]) + (pc[2] + pc[3]));
+          pos.s += kBatch - 1;  // the loop's increment moves past the batch
+          if (pos.s + 1 >= s_end) pos.s = kSteps - 1;  // no weight below: the end of the classes
+          continue;
+        }
+        // the crossing lies in the batch: the steps before it by their totals
+        u64 run = pos.m;
+        uint32_t runc = 0u;
+        int skip = kBatch - 1;
+#pragma unroll
+        for (int b = 0; b < kBatch - 1; ++b) {
+          if (skip == kBatch - 1) {
+            const u64 tm = wave_total<u64>(pm[b]);
+            if (run + tm >= thr) {
+              skip = b;
+            } else {
+              run += tm;
+              runc += pc[b];
+            }
+          }
+        }
+        pos.m = run;
+        pos.c += wave_total<uint32_t>(runc);
+        pos.s += skip;  // the step holding the crossing, scanned class by class below
+      }
       StepRound Q;
       uint32_t rc;
       u64 rm;
