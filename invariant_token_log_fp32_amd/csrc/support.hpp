@@ -500,6 +500,32 @@ __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int l) {
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
 }
 
+// BF16 pattern of the class that `lane` holds as element e of step s (the
+// zero step's elements are all the zero class; only lane 0's first one is
+// counted there).
+__device__ __forceinline__ uint32_t step_bits(int s, int lane, int e) {
+  if (s < kPosSteps) return kMagLo + static_cast<uint32_t>(kNMag - 1 - (s * kStepRanks + 4 * lane + e));
+  if (s == kZeroStep) return 0u;
+  return 0x8000u | (kMagLo + static_cast<uint32_t>((s - kPosSteps - 1) * kStepRanks + 4 * lane + e));
+}
+
+// The weight of a class as floor(w * 2^40) = hi * 2^32 + lo (the integers
+// fixed40 forms, without its branches): w = 2^(x*c - R) is at most a little
+// above 1 for a class at or below the row maximum, so hi <= 256. For an empty
+// class above the maximum the parts may be anything; its count is 0.
+__device__ __forceinline__ void weight_parts(uint32_t b, float c, float nr, uint32_t& hi, uint32_t& lo) {
+  const float w = __builtin_amdgcn_exp2f(fmaf(__uint_as_float(b << 16), c, nr));
+  const float a = w * 0x1p40f;  // below 2^-86 for w under the normal range: both parts 0, as in fixed40
+  hi = __float2uint_rz(w * 0x1p8f);
+  lo = __float2uint_rz(fmaf(static_cast<float>(hi), -0x1p32f, a));
+}
+
+// count * floor(w * 2^40) for a count below 2^24 (hi <= 256, so the high part
+// is a 24-bit product).
+__device__ __forceinline__ u64 class_mass(uint32_t cnt, uint32_t hi, uint32_t lo) {
+  return (static_cast<u64>(__umul24(cnt, hi)) << 32) + static_cast<u64>(cnt) * lo;
+}
+
 // One step: per-class counts and masses, and the inclusive cumulative count
 // and mass of each class counted from the step's first class (lane-local
 // prefix plus the exclusive DPP scan of the lanes). Returns the step's totals
@@ -525,11 +551,9 @@ __device__ __forceinline__ bool step_round(const NucLds& L, int s, float c, floa
   u64 pm = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    u64 m = 0;
-    if (Q.cnt[e]) {
-      const float t = fmaf(rank_value(step_rank(s, lane, e)), c, nr);
-      if (t >= -42.0f) m = static_cast<u64>(Q.cnt[e]) * fixed40(__builtin_amdgcn_exp2f(t));
-    }
+    uint32_t hi, lo;
+    weight_parts(step_bits(s, lane, e), c, nr, hi, lo);
+    const u64 m = class_mass(Q.cnt[e], hi, lo);
     Q.mass[e] = m;
     pc += Q.cnt[e];
     pm += m;
@@ -548,23 +572,6 @@ __device__ __forceinline__ bool step_round(const NucLds& L, int s, float c, floa
   rc = readlane_u32(ic, kWave - 1);
   rm = readlane_u64(im, kWave - 1);
   return true;
-}
-
-// Count and mass of the four classes that `lane` holds in step s (lane-local).
-__device__ __forceinline__ void step_lane_sums(const NucLds& L, int s, int lane, float c, float nr, uint32_t& pc,
-                                               u64& pm) {
-  uint32_t cnt[4];
-  step_counts(L, s, lane, cnt);
-  pc = 0u;
-  pm = 0ull;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (cnt[e]) {
-      const float t = fmaf(rank_value(step_rank(s, lane, e)), c, nr);
-      if (t >= -42.0f) pm += static_cast<u64>(cnt[e]) * fixed40(__builtin_amdgcn_exp2f(t));
-      pc += cnt[e];
-    }
-  }
 }
 
 constexpr int kBatch = 4;       // steps whose LDS reads a scan issues together
@@ -587,16 +594,18 @@ __device__ __forceinline__ void batch_lane_sums(const NucLds& L, int s, int s_en
   }
 #pragma unroll
   for (int b = 0; b < kBatch; ++b) {
+    uint32_t sum_hi = 0u;  // sum of count * hi: below 2^24 * 256 over a row
+    u64 sum_lo = 0ull;
     pc[b] = 0u;
-    pm[b] = 0ull;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (cn[b][e]) {
-        const float t = fmaf(rank_value(step_rank(s + b, lane, e)), c, nr);
-        if (t >= -42.0f) pm[b] += static_cast<u64>(cn[b][e]) * fixed40(__builtin_amdgcn_exp2f(t));
-        pc[b] += cn[b][e];
-      }
+      uint32_t hi, lo;
+      weight_parts(step_bits(s + b, lane, e), c, nr, hi, lo);
+      sum_hi += __umul24(cn[b][e], hi);
+      sum_lo += static_cast<u64>(cn[b][e]) * lo;
+      pc[b] += cn[b][e];
     }
+    pm[b] = (static_cast<u64>(sum_hi) << 32) + sum_lo;
   }
 }
 
