@@ -174,15 +174,22 @@ __global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(6, 
     if ((threadIdx.x & (kWave - 1)) == 0) L.sm[wave] = s;
   }
   __syncthreads();
-  // A row with every token in the window (or no search at all) finishes in
-  // wavefront 0; the other wavefronts are done. A row with a token outside
-  // the window takes the general path with the whole block.
+  // A row with every token in the window finishes in wavefronts 0 (search)
+  // and 1 (merge), a row with no search in wavefront 0; the other wavefronts
+  // are done. A row with a token outside the window takes the general path
+  // with the whole block.
   bool odd = false;  // block-uniform
-  if (search_needed(t, p, k, vocab_real))
+  const bool searched = search_needed(t, p, k, vocab_real);
+  if (searched)
     for (int w = 0; w < kNucWaves; ++w) odd |= (L.red_flag[w] != 0);
   if (!odd) {
-    if (wave == 0)
+    if (searched) {
+      if (wave <= 1)
+        nucleus_row_pair(L, wave, row, vocab_real, shard_width, t, p, k, tg, policy_out, ref_out, lse_out,
+                         state_out);
+    } else if (wave == 0) {
       nucleus_row_wave(L, row, vocab_real, shard_width, t, p, k, tg, policy_out, ref_out, lse_out, state_out);
+    }
     return;
   }
   nucleus_row(L, rowp, row, vocab_real, shard_width, t, p, k, tg, true, policy_out, ref_out, lse_out, state_out);

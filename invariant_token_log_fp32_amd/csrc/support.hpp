@@ -213,6 +213,11 @@ struct NucLds {
   int scan_bin;
   uint32_t scan_cnt_above;
   u64 scan_mass_above;
+  // the row merge, handed from wavefront 1 to wavefront 0 (RowStart)
+  float rs_ref;
+  float rs_lse;
+  uint32_t rs_bt;
+  int rs_status;
   union alignas(16) {
     uint32_t win[kWinWords];        // interleaved slots, the zero class, a pad word
     u64 win_pairs[kWinWords / 2];   // the same as 64-bit pairs, for clearing
@@ -1191,6 +1196,47 @@ __device__ __forceinline__ void nucleus_row_wave(const NucLds& L, int64_t row, i
   const bool p_active = (p < 1.0f);
   const FastSupport fs = support_fast_wave(L, vocab_real, shard_width, k_active, k, p_active, p, kLog2e / t);
   if (lead) write_policy(row, vocab_real, true, fs.kappa, fs.cnt_s, fs.z_s, fs.R, rs, t, policy_out, state_out);
+}
+
+// A searched row whose window is complete, in two wavefronts: wavefront 1
+// merges the summaries and writes the reference outputs while wavefront 0
+// runs the support search, then wavefront 0 writes the policy outputs. The
+// other wavefronts of the workgroup have ended, and a barrier waits only for
+// the wavefronts still running.
+__device__ __forceinline__ void nucleus_row_pair(NucLds& L, int wave, int64_t row, int64_t vocab_real,
+                                                 int shard_width, float t, float p, int64_t k, int64_t tg,
+                                                 float* __restrict__ policy_out, float* __restrict__ ref_out,
+                                                 float* __restrict__ lse_out,
+                                                 rlk_support_state* __restrict__ state_out) {
+  const bool lead = (threadIdx.x & (kWave - 1)) == 0;
+  FastSupport fs;
+  if (wave == 1) {
+    const RowStart rs = row_start(L.sm, vocab_real, shard_width, t, p, k, tg);
+    if (lead) {
+      ref_out[row] = rs.ref;
+      if (lse_out) lse_out[row] = rs.lse;
+      L.rs_ref = rs.ref;
+      L.rs_lse = rs.lse;
+      L.rs_bt = rs.bt;
+      L.rs_status = rs.status;
+    }
+  } else {
+    const bool k_active = (k != -1) && (k < vocab_real);
+    const bool p_active = (p < 1.0f);
+    fs = support_fast_wave(L, vocab_real, shard_width, k_active, k, p_active, p, kLog2e / t);
+  }
+  __syncthreads();
+  if (wave == 0 && lead) {
+    RowStart rs;
+    rs.ref = L.rs_ref;
+    rs.lse = L.rs_lse;
+    rs.bt = L.rs_bt;
+    rs.status = L.rs_status;
+    if (rs.status != 0)
+      write_unsearched(row, rs, policy_out, state_out);
+    else
+      write_policy(row, vocab_real, true, fs.kappa, fs.cnt_s, fs.z_s, fs.R, rs, t, policy_out, state_out);
+  }
 }
 
 // ---------------------------------------------------------------------------
