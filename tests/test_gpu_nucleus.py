@@ -161,6 +161,40 @@ def test_top_p_near_one_and_bracket_edges():
     check(logits, vr, temps, top_p, top_k, targets, "top-p near 1, uniform targets", groups_list=(1, 8))
 
 
+def test_deep_top_p_scans():
+    """Rows whose probability mass spreads over most of the support window, so
+    that the top-p crossing lies many 256-class steps below the maximum: the
+    values are +-2^U(-24, 3) (a few zeros in every other row), at temperatures
+    2 and 8 where the masses of all tokens are within a small factor of each
+    other. The p grid puts the crossing in many different steps (and at each
+    position of a four-step batch of the scan's skip-ahead), with top-k off and
+    on (k = 12000, so the top-p threshold comes from the exact top-k mass)."""
+    say("case: deep top-p scans")
+    vp, vr = 19200, 19137
+    p_grid = np.array([0.05, 0.2, 0.35, 0.5, 0.65, 0.8, 0.95, 0.999], dtype=np.float32)
+    rows, T, P, K = [], [], [], []
+    rng = np.random.default_rng(83)
+    for temp in (2.0, 8.0):
+        for k in (-1, 12000):
+            for i, p in enumerate(p_grid):
+                r = np.full(vp, datagen.BF16_NEG_INF, dtype=np.uint16)
+                mag = np.exp2(rng.uniform(-24.0, 3.0, vr)).astype(np.float32)
+                sign = np.where(rng.random(vr) < 0.5, -1.0, 1.0).astype(np.float32)
+                r[:vr] = datagen.f32_to_bf16_bits(mag * sign)
+                if i % 2:
+                    r[rng.integers(0, vr, 5)] = 0
+                rows.append(r)
+                T.append(temp)
+                P.append(p)
+                K.append(k)
+    logits = np.stack(rows)
+    temps = np.array(T, np.float32)
+    top_p = np.array(P, np.float32)
+    top_k = np.array(K, np.int32)
+    targets = support_targets(logits, vr, temps, top_p, top_k, 84)
+    check(logits, vr, temps, top_p, top_k, targets, "deep top-p scans", groups_list=(1, 8))
+
+
 # BF16 patterns at and just past the ends of the support window's value
 # ranges: the top (65535.x is the largest magnitude inside, 65536 and the next
 # value outside, both signs), the smallest magnitudes (2^-24 inside, the next
