@@ -560,6 +560,8 @@ __global__ __launch_bounds__(kThreads) void k_linear(Geo g, const float* __restr
   while (true) {
     const int64_t row0 = m_t * BM;
     const int64_t col0 = g.col_base + n_t * BN;
+    Acc acc[kMB][kNB];
+    tile_logits(g, p, pn, more, par, smem, acc, fa, fb);
     float tr[kMB];
     int64_t tgr[kMB];
     if (kLogp) {
@@ -570,8 +572,6 @@ __global__ __launch_bounds__(kThreads) void k_linear(Geo g, const float* __restr
         tgr[i] = gr < g.n_rows ? target[gr] : -1;
       }
     }
-    Acc acc[kMB][kNB];
-    tile_logits(g, p, pn, more, par, smem, acc, fa, fb);
     if (kLogp)
       tile_summaries(g, row0, col0, acc, tr, tgr, ws);
     else
