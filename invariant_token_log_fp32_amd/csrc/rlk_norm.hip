@@ -16,8 +16,9 @@
 //                      at the end the copies are summed and added to the
 //                      device bins with u64 atomics. All sums are integer
 //                      sums, so the order of the atomics does not matter.
-//   k_norm_finalize    one wave: the nonzero bins (found by ballots) are
-//                      added into a 384-bit integer in units of 2^-149,
+//   k_norm_finalize    one wave: the bins are added exactly into a 384-bit
+//                      integer in units of 2^-149 (lane sums, then shuffle
+//                      trees over 128-bit group sums and 64-bit limbs),
 //                      rounded once to float64 (nearest even); then the
 //                      square root. The <true> instance also clears the
 //                      accumulator for the next one-call norm.
@@ -114,24 +115,6 @@ struct Big {
   u64 w[6];
 };
 
-__device__ __forceinline__ void big_add_shifted(Big& a, u64 v, int sh) {
-  const int limb = sh >> 6;
-  const int off = sh & 63;
-  const u64 lo = v << off;
-  const u64 hi = off ? (v >> (64 - off)) : 0ull;
-  u64 carry = 0ull;
-#pragma unroll
-  for (int i = 0; i < 6; ++i) {
-    const u64 add = (i == limb) ? lo : (i == limb + 1 ? hi : 0ull);
-    const u64 t = a.w[i] + add;
-    const u64 c1 = t < add;
-    const u64 t2 = t + carry;
-    const u64 c2 = t2 < carry;
-    a.w[i] = (i < limb) ? a.w[i] : t2;
-    carry = (i < limb) ? 0ull : c1 + c2;
-  }
-}
-
 // Limb i of a, 0 outside [0, 6).
 __device__ __forceinline__ u64 big_limb(const Big& a, int i) {
   u64 r = 0ull;
@@ -171,43 +154,83 @@ __device__ __forceinline__ u64 readlane64(u64 v, int lane) {
   return (static_cast<u64>(hi) << 32) | lo;
 }
 
+// Exponent of bin e's unit, in units of 2^-149: the bin counts 24-bit
+// significands of squares with biased exponent e, each worth 2^(max(e,1) - 150).
+__device__ __forceinline__ int bin_offset(int e) { return e > 0 ? e - 1 : 0; }
+
+// a += v << sh for 128-bit a and v, 0 <= sh < 64 (no overflow by the callers'
+// bounds).
+__device__ __forceinline__ void add_shl128(u64& a_lo, u64& a_hi, u64 v_lo, u64 v_hi, int sh) {
+  const u64 s_lo = v_lo << sh;
+  const u64 s_hi = sh ? ((v_hi << sh) | (v_lo >> (64 - sh))) : v_hi;
+  const u64 t = a_lo + s_lo;
+  a_hi += s_hi + (t < s_lo ? 1ull : 0ull);
+  a_lo = t;
+}
+
 // The exact sum of the squares from the accumulator words, rounded once to
-// float64 (one wave; wave-uniform result). v[k] holds word k * 64 + lane (the
-// bins); n_nan / n_inf are the two count words. `stage` is 256 words of LDS.
-// Bin e weighs 2^(max(e,1) - 1) units of 2^-149. Lanes 0..7 first sum the 32
-// bins of group g = lane exactly into 128 bits (each bin is below 2^63 and is
-// shifted by at most 31 bits, so 32 of them stay below 2^100); the 8 group
-// sums are then added into a 384-bit integer at their offsets.
-__device__ __forceinline__ double exact_sum(const u64 (&v)[4], u64 n_nan, u64 n_inf, u64* stage) {
+// float64 (one wave; wave-uniform result). Lane j holds bins 4j .. 4j+3 in
+// b[0..3]. Bin e weighs 2^(bin_offset(e)) units of 2^-149.
+//   1. Lane j sums its 4 bins at its own offset o_j = bin_offset(4j): shifts
+//      of at most 3 bits, so below 2^67 in 128 bits.
+//   2. Three shuffle levels add lane j + d into lane j (d = 1, 2, 4, shifted by
+//      o_{j+d} - o_j <= 16): lane 8g then holds group g's 32 bins at offset
+//      o_{8g}, below 2^98.
+//   3. Each group's 128 bits, shifted by o_{8g} mod 64, cover three of the six
+//      64-bit limbs of the 384-bit total; per limb, the 8 groups' pieces are
+//      added by three more shuffle levels (64-bit sums with carry counts), and
+//      lane 0 propagates the carries through the limbs.
+// Every step is integer arithmetic, so the total is exact.
+__device__ __forceinline__ double exact_sum(const u64 (&b)[4], u64 n_nan, u64 n_inf) {
   if (n_nan != 0ull) return NAN;
   if (n_inf != 0ull) return INFINITY;
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) stage[k * 64 + lane] = v[k];
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the wave's LDS writes are done
-  __builtin_amdgcn_wave_barrier();
+  const int o = bin_offset(4 * lane);
   u64 lo = 0ull, hi = 0ull;
-  if (lane < 8) {
-#pragma unroll 4
-    for (int j = 0; j < 32; ++j) {
-      const int e = 32 * lane + j;
-      const u64 b = stage[e];
-      const int sh = (lane == 0) ? (e > 0 ? e - 1 : 0) : j;  // (max(e,1) - 1) - (group offset)
-      const u64 add_lo = b << sh;
-      const u64 add_hi = sh ? (b >> (64 - sh)) : 0ull;
-      const u64 t = lo + add_lo;
-      hi += add_hi + (t < lo ? 1ull : 0ull);
-      lo = t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) add_shl128(lo, hi, b[i], 0ull, bin_offset(4 * lane + i) - o);
+#pragma unroll
+  for (int d = 1; d < 8; d <<= 1) {
+    const u64 p_lo = __shfl_down(lo, d);
+    const u64 p_hi = __shfl_down(hi, d);
+    if ((lane & (2 * d - 1)) == 0) add_shl128(lo, hi, p_lo, p_hi, bin_offset(4 * (lane + d)) - o);
+  }
+  // lane 8g: group g at offset o (0 for g = 0, 32g - 1 otherwise)
+  const int limb0 = o >> 6;
+  const int sh = o & 63;
+  const u64 q0 = lo << sh;
+  const u64 q1 = sh ? ((hi << sh) | (lo >> (64 - sh))) : hi;
+  const u64 q2 = sh ? (hi >> (64 - sh)) : 0ull;
+  const bool lead = (lane & 7) == 0;
+  u64 s_lo[6], s_c[6];
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const u64 piece = (k == limb0) ? q0 : (k == limb0 + 1 ? q1 : (k == limb0 + 2 ? q2 : 0ull));
+    s_lo[k] = lead ? piece : 0ull;
+    s_c[k] = 0ull;
+  }
+#pragma unroll
+  for (int d = 8; d < 64; d <<= 1) {
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const u64 p_lo = __shfl_down(s_lo[k], d);
+      const u64 p_c = __shfl_down(s_c[k], d);
+      if ((lane & (2 * d - 1)) == 0) {
+        const u64 t = s_lo[k] + p_lo;
+        s_c[k] += p_c + (t < p_lo ? 1ull : 0ull);
+        s_lo[k] = t;
+      }
     }
   }
-  Big a = {{0ull, 0ull, 0ull, 0ull, 0ull, 0ull}};
-#pragma unroll 1
-  for (int g = 0; g < 8; ++g) {
-    const int off = (g == 0) ? 0 : 32 * g - 1;  // group g's offset in units of 2^-149
-    const u64 glo = readlane64(lo, g);
-    const u64 ghi = readlane64(hi, g);
-    if (glo) big_add_shifted(a, glo, off);
-    if (ghi) big_add_shifted(a, ghi, off + 64);
+  Big a;
+  u64 carry = 0ull;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const u64 lk = readlane64(s_lo[k], 0);
+    const u64 ck = readlane64(s_c[k], 0);
+    const u64 t = lk + carry;
+    a.w[k] = t;
+    carry = ck + (t < carry ? 1ull : 0ull);
   }
   int top = -1;
 #pragma unroll
@@ -230,20 +253,19 @@ __device__ __forceinline__ double exact_sum(const u64 (&v)[4], u64 n_nan, u64 n_
   return ldexp(static_cast<double>(mant), ex);
 }
 
-// One wave of 64 lanes. Lane l reads words l, l + 64, l + 128, l + 192 (the
-// bins) and lane 0 the NaN / inf counts; lane 0 writes fl64(S) and
-// fl32(sqrt). With kClear every word is then set to 0.
+// One wave of 64 lanes. Lane l reads words 4l .. 4l+3 (the bins) and lane 0
+// the NaN / inf counts; lane 0 writes fl64(S) and fl32(sqrt). With kClear
+// every word is then set to 0.
 template <bool kClear>
 __global__ __launch_bounds__(64) void k_norm_finalize(u64* __restrict__ bins, double* __restrict__ sumsq_out,
                                                       float* __restrict__ norm_out) {
-  __shared__ u64 stage[kBins];
   const int lane = threadIdx.x;
   u64 v[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) v[k] = bins[k * 64 + lane];
+  for (int k = 0; k < 4; ++k) v[k] = bins[4 * lane + k];
   const u64 n_nan = readlane64(lane == 0 ? bins[kBins] : 0ull, 0);
   const u64 n_inf = readlane64(lane == 0 ? bins[kBins + 1] : 0ull, 0);
-  const double s = exact_sum(v, n_nan, n_inf, stage);
+  const double s = exact_sum(v, n_nan, n_inf);
   if (lane == 0) {
     if (sumsq_out) *sumsq_out = s;
     if (norm_out) *norm_out = static_cast<float>(sqrt(s));
