@@ -288,9 +288,6 @@ __device__ __forceinline__ void row_pass_vec(const uint16_t* __restrict__ rowp, 
   }
 }
 
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x2 __attribute__((ext_vector_type(2)));
-
 // Window slots of the two BF16 values packed in one 32-bit word (low half =
 // first value), on 16-bit integer lane pairs: the sign bit, then
 // 2 * b + sign (the product drops the sign bit, leaving 2 * m + sign), then
