@@ -11,10 +11,11 @@
 //   k_merge            one thread per row: the same fixed-order merge over the
 //                      rank-major summaries (groups > 1, rlk_logp_merge).
 //   k_nucleus_g1       groups == 1 support path in one launch: the shard-waves
-//                      also count every token into an LDS histogram of
-//                      compressed BF16 ranks; then the merge (reference
-//                      logprob), the top-k/top-p support from the exact
-//                      integer histogram, and the policy logprob.
+//                      also count every token into an LDS window of BF16
+//                      classes; then the merge (reference logprob, wavefront
+//                      1) beside the top-k/top-p support from the exact
+//                      integer class masses (wavefront 0), and the policy
+//                      logprob.
 //   k_nucleus          groups > 1: the same per-row support search on the
 //                      summaries k_rank_summaries stored.
 //   k_backward         gradient of the reference and policy logprobs with

@@ -29,9 +29,11 @@
 // the support costs no extra pass; otherwise one pass builds it. The row
 // maximum is the first non-empty class, class masses are count * weight, and
 // the thresholds come from prefix sums over the classes, computed by one
-// wavefront while the rest of the workgroup has finished. When top-k is off,
+// wavefront while the rest of the workgroup has finished (with groups == 1 a
+// second wavefront merges the shard summaries meanwhile). When top-k is off,
 // the top-p threshold ceil(p * Z) is first bracketed from the float shard
-// sums, so the total Z is summed only when the bracket cannot decide.
+// sums, so the total Z is summed only when the bracket cannot decide; a scan
+// that runs past three steps skips ahead by four-step mass totals.
 // General path, for rows with a token outside the window (a nonzero value of
 // magnitude below 2^-24, or 65536 and beyond): an exact-maximum pass, then a
 // 4096-bin histogram of (count, mass) over key >> 4, then the 16 keys of each
