@@ -851,14 +851,25 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
       // vectors plus a partial one, 3 pairwise levels, 6 butterfly levels):
       // relative error <= depth * 2^-24. A term and the token's integer
       // weight floor(2^(x*c - R) * 2^40) differ by the rounding of their
-      // exponent arguments (half an ulp of |x*c - r_s| < 100, since a shard
-      // total reaches 2^100 only on the exact-maximum recompute, plus half an
-      // ulp of |x*c - R| <= 42 where the weight is nonzero: < 2^-17 relative),
-      // by v_exp_f32 (about 2^-23 each), by the floor (under one unit per
-      // token on a total of at least 2^39 units) and by terms whose weight
-      // floors to 0 (under 1/4 unit each). The bracket takes twice the sum.
+      // exponent arguments, by v_exp_f32 (about 2^-23 each), by the floor
+      // (under one unit per token on a total of at least 2^39 units) and by
+      // terms whose weight floors to 0 (under 1/4 unit each). The arguments:
+      // x*c - r_s is below D_s + 1 (D_s = R - r_s >= 0), and the term of the
+      // maximum of the chunk that fixed r_s makes l_s >= 1/2, so the terms
+      // with x*c - r_s >= -31 are rounded by at most half an ulp of
+      // max(31, D_s + 1) and all the others together move l_s by under 2^-30
+      // relative; likewise x*c - R lies in [-42, 0] where a weight is nonzero,
+      // rounded by at most 2^-20 (half an ulp of 31) above -31, the rest under
+      // 2^-30 relative. A relative argument error d changes 2^arg by d*ln 2 <
+      // d. The bracket takes twice the sum.
       const int depth = (shard_width / 8 + kWave) / kWave + 1 + 3 + 6;
-      const double eps = 2.0 * (static_cast<double>(depth) * 0x1p-24 + 0x1p-17 + 0x1p-22 +
+      float dmax = 0.0f;
+#pragma unroll
+      for (int sh = 0; sh < kShards; ++sh)
+        if (L.sm[sh].l > 0.0f) dmax = fmaxf(dmax, R - L.sm[sh].r);
+      const double karg = fmax(31.0, static_cast<double>(dmax) + 1.0);
+      const double half_ulp = ldexp(1.0, ilogb(karg) - 24);
+      const double eps = 2.0 * (static_cast<double>(depth) * 0x1p-24 + half_ulp + 0x1p-20 + 0x1p-22 + 0x1p-30 +
                                 1.25 * static_cast<double>(vocab_real) * 0x1p-39);
       double zf = 0.0;
 #pragma unroll

@@ -69,12 +69,19 @@ def totals(x, t):
     w = np.exp2(fl32_fma(x, c, R)).astype(np.float32).astype(np.float64)
     z_int = int(np.floor(w * 2.0 ** 40).astype(np.int64).sum())
     zf = sum(math.ldexp(l, r - R + 40) for l, r in zf_terms)
-    return zf, z_int
+    dmax = max(R - r for l, r in zf_terms if l > 0)
+    return zf, z_int, dmax
 
 
-def kernel_eps(shard_width, vocab_real):
+def kernel_eps(shard_width, vocab_real, dmax):
+    """The kernel's bracket half-width: float-sum depth, half an ulp of the
+    largest shard-argument magnitude max(31, D + 1) and of 31 for the weight
+    argument, v_exp_f32, the neglected tails and the floor, twice."""
     depth = (shard_width // 8 + WAVE) // WAVE + 1 + 3 + 6
-    return 2.0 * (depth * 2.0 ** -24 + 2.0 ** -17 + 2.0 ** -22 + 1.25 * vocab_real * 2.0 ** -39)
+    karg = max(31.0, dmax + 1.0)
+    half_ulp = math.ldexp(1.0, math.frexp(karg)[1] - 1 - 24)
+    return 2.0 * (depth * 2.0 ** -24 + half_ulp + 2.0 ** -20 + 2.0 ** -22 + 2.0 ** -30 +
+                  1.25 * vocab_real * 2.0 ** -39)
 
 
 def rows():
@@ -93,9 +100,9 @@ def rows():
 
 @pytest.mark.parametrize("name,x,t", rows(), ids=[r[0] for r in rows()])
 def test_shard_sums_bracket_the_integer_total(name, x, t):
-    zf, z_int = totals(x, t)
+    zf, z_int, dmax = totals(x, t)
     rel = abs(zf - z_int) / z_int
-    eps = kernel_eps(SHARD, VOCAB_REAL)
+    eps = kernel_eps(SHARD, VOCAB_REAL, dmax)
     assert z_int >= 2 ** 39
     # the kernel brackets with eps; the observed gap must sit far inside it
     assert rel < eps / 8, (name, rel, eps)
