@@ -527,7 +527,8 @@ __device__ __forceinline__ void weight_parts(uint32_t b, float c, float nr, uint
 // count * floor(w * 2^40) for a count below 2^24 (hi <= 256, so the high part
 // is a 24-bit product).
 __device__ __forceinline__ u64 class_mass(uint32_t cnt, uint32_t hi, uint32_t lo) {
-  return (static_cast<u64>(__umul24(cnt, hi)) << 32) + static_cast<u64>(cnt) * lo;
+  const uint32_t hp = static_cast<uint32_t>(__umul24(cnt, hi));  // below 2^32; __umul24 returns int
+  return (static_cast<u64>(hp) << 32) + static_cast<u64>(cnt) * lo;
 }
 
 // One step: per-class counts and masses, and the inclusive cumulative count
@@ -605,7 +606,7 @@ __device__ __forceinline__ void batch_lane_sums(const NucLds& L, int s, int s_en
     for (int e = 0; e < 4; ++e) {
       uint32_t hi, lo;
       weight_parts(step_bits(s + b, lane, e), c, nr, hi, lo);
-      sum_hi += __umul24(cn[b][e], hi);
+      sum_hi += static_cast<uint32_t>(__umul24(cn[b][e], hi));
       sum_lo += static_cast<u64>(cn[b][e]) * lo;
       pc[b] += cn[b][e];
     }

@@ -40,9 +40,9 @@ def run_nucleus(logits_np, vr, temps, top_p, top_k, targets, groups=1, vp=None):
     return to_host(pol), to_host(ref), to_host(full)
 
 
-def check(logits, vr, temps, top_p, top_k, targets, what, vp=None, groups_list=GROUPS):
+def check(logits, vr, temps, top_p, top_k, targets, what, vp=None, groups_list=GROUPS, extra_tol=0.0):
     want_pol, want_ref, infos = O.nucleus_logp(logits, vr, temps, top_p, top_k, targets)
-    tol = row_tolerance(logits, vr, temps)
+    tol = row_tolerance(logits, vr, temps) + extra_tol
     first = None
     for groups in groups_list:
         pol, ref, full = run_nucleus(logits, vr, temps, top_p, top_k, targets, groups, vp)
@@ -193,6 +193,41 @@ def test_deep_top_p_scans():
     top_k = np.array(K, np.int32)
     targets = support_targets(logits, vr, temps, top_p, top_k, 84)
     check(logits, vr, temps, top_p, top_k, targets, "deep top-p scans", groups_list=(1, 8))
+
+
+def test_classes_of_millions_of_tokens():
+    """Rows of 10,000,000 columns where one class holds 6 to 10 million tokens,
+    so a class mass count * weight has a high part above 2^31 (the widest the
+    search's integer masses get below the 2^24-token limit): all tokens equal
+    (top-k 5 keeps the whole tied class), and 60% of the tokens on the maximum
+    with the rest spread below (top-p 0.5 and 0.9)."""
+    say("case: classes of millions of tokens")
+    vp = vr = 10_000_000
+    rng = np.random.default_rng(97)
+    rows, T, P, K = [], [], [], []
+    eq = np.full(vp, datagen.f32_to_bf16_bits(np.array([3.0], np.float32))[0], dtype=np.uint16)
+    rows.append(eq)
+    T.append(0.7)
+    P.append(1.0)
+    K.append(5)
+    for p in (0.5, 0.9):
+        r = datagen.f32_to_bf16_bits(rng.normal(0.0, 1.0, vp).astype(np.float32))
+        r[rng.random(vp) < 0.6] = datagen.f32_to_bf16_bits(np.array([6.0], np.float32))[0]
+        rows.append(r)
+        T.append(1.0)
+        P.append(p)
+        K.append(-1)
+    logits = np.stack(rows)
+    temps = np.array(T, np.float32)
+    top_p = np.array(P, np.float32)
+    top_k = np.array(K, np.int32)
+    targets = np.array([123, int(np.argmax(datagen.bf16_bits_to_f32(rows[1]))), 7], dtype=np.int64)
+    # the float32 shard sums of the reference add one rounding per term of an
+    # accumulator: 2441 terms here against 38 at the benchmark's vocabulary, so
+    # the reference (and a policy equal to it) gets that many 2^-24 more
+    depth = (vp // 8 // 8 + 64) // 64 + 1 + 3 + 6
+    check(logits, vr, temps, top_p, top_k, targets, "classes of millions of tokens", vp=vp, groups_list=(1, 8),
+          extra_tol=depth * 2.0 ** -24)
 
 
 # BF16 patterns at and just past the ends of the support window's value
