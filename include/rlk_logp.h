@@ -117,7 +117,8 @@ typedef struct rlk_support_state {
                         the whole real vocabulary */
   int32_t status;    /* 1: the target is in the support (policy logprob finite or
                         -inf only through a -inf target logit); 0: the target is
-                        outside it (policy -inf); -1: invalid top_p / top_k (policy
+                        outside it (policy -inf); -1: no support (invalid top_p /
+                        top_k, or a row maximum beyond the search's range; policy
                         NaN); -2: invalid row (reference NaN) */
   int32_t reserved;  /* 0 */
 } rlk_support_state;
@@ -144,7 +145,10 @@ typedef struct rlk_support_state {
  * Greedy rows (temperature 0) put a point mass on the lowest-index maximum for
  * both outputs. The support decision is taken on integer masses (64-bit, in
  * units of 2^-40 of the row's largest weight), so it is the same for any batch
- * or grouping; vocab_real must stay below 2^24 (else RLK_ERR_SHAPE). */
+ * or grouping; vocab_real must stay below 2^24 - 2^20 = 15728640 (else
+ * RLK_ERR_SHAPE). A row whose largest scaled logit has |max x * log2(e) / T|
+ * >= 2^20 (|x / T| above about 726817) gets no support: policy NaN and status
+ * -1, the reference as usual. */
 int32_t rlk_logp_nucleus(const uint16_t* logits, int64_t n_rows, const rlk_vocab_layout* layout,
                          const float* temperature, const float* top_p, const int32_t* top_k,
                          const int64_t* target, float* policy_out, float* ref_out,

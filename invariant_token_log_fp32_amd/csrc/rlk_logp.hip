@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_backward(
 // Host side
 // ----------------------------------------------------------------------------
 constexpr int64_t kMaxVocab = int64_t(1) << 30;
-constexpr int64_t kMaxNucleusVocab = int64_t(1) << 24;  // vocab_real limit of rlk_logp_nucleus
+constexpr int64_t kMaxNucleusVocab = (int64_t(1) << 24) - (int64_t(1) << 20);  // vocab_real limit of rlk_logp_nucleus
 constexpr int64_t kMaxRows = int64_t(1) << 22;       // one workgroup per row: rows * 1024 threads < 2^32
 constexpr int64_t kMaxBwdBlocks = int64_t(1) << 21;  // backward grid cap; larger jobs loop over items
 
@@ -431,8 +431,10 @@ int32_t rlk_logp_nucleus(const uint16_t* logits, int64_t n_rows, const rlk_vocab
   using namespace rlk;
   int32_t st = check_layout(n_rows, layout);
   if (st != RLK_OK) return st;
-  // support masses are 64-bit integers in units of 2^-40 of the largest
-  // token's weight, so a row holds fewer than 2^24 real tokens
+  // support masses are 64-bit integers in units of 2^-40 of 2^R, and a
+  // token weighs at most 2^(2^-5) * 2^40 of them (support.hpp,
+  // kMaxSupportArg): fewer than 2^24 - 2^20 real tokens keep a row's total
+  // below 2^64
   if (layout->vocab_real >= kMaxNucleusVocab) return RLK_ERR_SHAPE;
   if (n_rows == 0) return RLK_OK;  // nothing to read or write: pointers may be NULL
   if (!logits || !temperature || !top_p || !top_k || !target || !policy_out || !ref_out) return RLK_ERR_NULL;

@@ -66,6 +66,12 @@ constexpr int kZeroRank = kNMag;
 constexpr int kRanks = kWin + 1;
 constexpr int kNoRank = kRanks;
 constexpr uint32_t kNegInfBits = 0xFF80u;
+// Range of the support search: the row maximum's exponent argument
+// |fl32(M*c)| < 2^20. Then fl32(M*c) is within 2^-5 of M*c, so no token's
+// weight exceeds 2^(2^-5) * 2^40 and, with fewer than 2^24 - 2^20 real tokens
+// (the entry points' limit), a row's total mass stays below 2^64. A row beyond
+// it gets no support (policy NaN, status -1); its reference is unaffected.
+constexpr float kMaxSupportArg = 0x1p20f;
 
 typedef unsigned long long u64;
 
@@ -215,6 +221,7 @@ struct NucLds {
   int scan_bin;
   uint32_t scan_cnt_above;
   u64 scan_mass_above;
+  int in_range;      // general path: the row maximum lies in the search's range
   // the row merge, handed from wavefront 1 to wavefront 0 (RowStart)
   float rs_ref;
   float rs_lse;
@@ -443,6 +450,7 @@ struct FastSupport {
   int kappa;       // rank of the last kept class, or kNoRank for the -inf class
   uint32_t cnt_s;  // tokens in the support
   u64 z_s;         // support mass (2^-40 units relative to 2^R)
+  bool in_range;   // the row maximum lies in the search's range (kMaxSupportArg)
 };
 
 constexpr int kStepRanks = 4 * kWave;           // 256 ranks per step
@@ -666,11 +674,14 @@ __device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_
   out.cnt_s = total_c + ninf_n;
   out.z_s = 0;
   out.R = 0.0f;
+  out.in_range = true;
   if (jtop == kNoRank) return out;  // no finite token: not reached on a searched row
   const float m = rank_value(jtop);
   const float R = ref_exponent(m, c);
   const float nr = -R;
   out.R = R;
+  out.in_range = fabsf(m * c) < kMaxSupportArg;  // wave-uniform
+  if (!out.in_range) return out;
   const int sfirst = rank_step(jtop);
 
   // exact mass of the classes from step s_start on: lane-local sums over the
@@ -996,7 +1007,10 @@ __device__ __forceinline__ void support_general(NucLds& L, const uint16_t* __res
   __syncthreads();
   for (int w = 0; w < kNucWaves; ++w) mx = fmaxf(mx, __uint_as_float(L.red_u32[w][0]));
   const float nr = -ref_exponent(mx, c);
-  if (tid == 0) L.R = -nr;
+  if (tid == 0) {
+    L.R = -nr;
+    L.in_range = fabsf(mx * c) < kMaxSupportArg;
+  }
   for (int i = tid; i < kBinsA; i += kNucThreads) {
     L.u.gen.cnt[i] = 0;
     L.u.gen.mass[i] = 0;
@@ -1154,9 +1168,17 @@ __device__ __forceinline__ void write_unsearched(int64_t row, const RowStart& rs
 
 // Policy logprob and support record of a searched row. `fast`: kappa is a
 // rank (kNoRank = the -inf class); otherwise a key16 (general path).
+// A row whose maximum lies outside the search's range (!in_range) is written
+// as a row without a support: policy NaN, status -1.
 __device__ __forceinline__ void write_policy(int64_t row, int64_t vocab_real, bool fast, int kappa, uint32_t cnt_s,
-                                             u64 z_s, float R, const RowStart& rs, float t,
+                                             u64 z_s, float R, bool in_range, const RowStart& rs, float t,
                                              float* __restrict__ policy_out, rlk_support_state* __restrict__ state_out) {
+  if (!in_range) {
+    RowStart none = rs;
+    none.status = -1;
+    write_unsearched(row, none, policy_out, state_out);
+    return;
+  }
   const uint32_t bt = rs.bt;
   const int trank = (bt == kNegInfBits) ? kNoRank : slot_rank(window_slot(bt));
   const bool in_support = fast ? (trank <= kappa) : (static_cast<int>(key16(bt)) >= kappa);
@@ -1206,7 +1228,8 @@ __device__ __forceinline__ void nucleus_row_wave(const NucLds& L, int64_t row, i
   const bool k_active = (k != -1) && (k < vocab_real);
   const bool p_active = (p < 1.0f);
   const FastSupport fs = support_fast_wave(L, vocab_real, shard_width, k_active, k, p_active, p, kLog2e / t);
-  if (lead) write_policy(row, vocab_real, true, fs.kappa, fs.cnt_s, fs.z_s, fs.R, rs, t, policy_out, state_out);
+  if (lead) write_policy(row, vocab_real, true, fs.kappa, fs.cnt_s, fs.z_s, fs.R, fs.in_range, rs, t, policy_out,
+                 state_out);
 }
 
 // A searched row whose window is complete, in two wavefronts: wavefront 1
@@ -1246,7 +1269,8 @@ __device__ __forceinline__ void nucleus_row_pair(NucLds& L, int wave, int64_t ro
     if (rs.status != 0)
       write_unsearched(row, rs, policy_out, state_out);
     else
-      write_policy(row, vocab_real, true, fs.kappa, fs.cnt_s, fs.z_s, fs.R, rs, t, policy_out, state_out);
+      write_policy(row, vocab_real, true, fs.kappa, fs.cnt_s, fs.z_s, fs.R, fs.in_range, rs, t, policy_out,
+                 state_out);
   }
 }
 
@@ -1300,12 +1324,14 @@ __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restric
     if (tid >= kWave) return;
     const FastSupport fs =
         support_fast_wave(L, vocab_real, shard_width, L.k_active != 0, L.k, L.p_active != 0, L.p, L.c);
-    if (tid == 0) write_policy(row, vocab_real, true, fs.kappa, fs.cnt_s, fs.z_s, fs.R, rs, t, policy_out, state_out);
+    if (tid == 0) write_policy(row, vocab_real, true, fs.kappa, fs.cnt_s, fs.z_s, fs.R, fs.in_range, rs, t, policy_out,
+                 state_out);
     return;
   }
   __syncthreads();  // the flags above are read before the general path reuses the block scratch
   support_general(L, rowp, vocab_real);
-  if (tid == 0) write_policy(row, vocab_real, false, L.kappa, L.cnt_s, L.z_s, L.R, rs, t, policy_out, state_out);
+  if (tid == 0)
+    write_policy(row, vocab_real, false, L.kappa, L.cnt_s, L.z_s, L.R, L.in_range != 0, rs, t, policy_out, state_out);
 }
 
 }  // namespace rlk

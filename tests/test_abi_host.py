@@ -103,10 +103,19 @@ def test_full_rejects_bad_arguments(lib, kw, code):
     (dict(lse=P + 0x502), ALIGN), (dict(state=P + 0x508), ALIGN),
     (dict(L=lay(vp=1 << 24, vr=1 << 24, stride=1 << 24)), SHAPE),
     (dict(L=lay(vp=(1 << 24) + 1024, vr=(1 << 24) + 7, stride=(1 << 24) + 1024)), SHAPE),
+    # the support search's limit: fewer than 2^24 - 2^20 real tokens
+    (dict(L=lay(vp=15728640, vr=15728640, stride=15728640)), SHAPE),
+    (dict(L=lay(vp=15728704, vr=15728641, stride=15728704)), SHAPE),
     (dict(n=0, L=lay(vp=1 << 25, vr=1 << 25, stride=1 << 25)), SHAPE),
 ])
 def test_nucleus_rejects_bad_arguments(lib, kw, code):
     assert nuc(lib, **kw) == code
+
+
+def test_nucleus_accepts_the_largest_vocabulary(lib):
+    # 2^24 - 2^20 - 1 real tokens pass the checks (an empty batch enqueues nothing)
+    assert nuc(lib, n=0, wsb=0, L=lay(vp=15728640, vr=15728639, stride=15728640)) == OK
+    assert noalloc(lib, n=0, L=lay(vp=15728640, vr=15728639, stride=15728640)) == OK
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -230,6 +230,60 @@ def test_classes_of_millions_of_tokens():
           extra_tol=depth * 2.0 ** -24)
 
 
+def test_row_maximum_beyond_the_search_range():
+    """The support search covers rows whose largest scaled logit has
+    |max x * log2(e) / T| < 2^20. At T 0.05 a maximum of 35840 (2^20 - 14k)
+    is inside and is compared with the oracle; 37120, and a row of -40000
+    everywhere, are beyond it: policy NaN, status -1, the reference as usual.
+    Both the window path and the general path (a 1e-9 logit in the row) are
+    covered."""
+    import torch
+    say("case: row maximum beyond the search range")
+    vp, vr = 3072, 3000
+    rng = np.random.default_rng(99)
+    base = datagen.f32_to_bf16_bits(rng.normal(0.0, 2.5, vr).astype(np.float32))
+    tiny = datagen.f32_to_bf16_bits(np.array([1e-9], np.float32))[0]
+    rows, inside = [], []
+    for top in (35840.0, 37120.0):
+        for general in (False, True):
+            r = np.full(vp, datagen.BF16_NEG_INF, dtype=np.uint16)
+            r[:vr] = base
+            r[17] = datagen.f32_to_bf16_bits(np.array([top], np.float32))[0]
+            if general:
+                r[29] = tiny
+            rows.append(r)
+            inside.append(top == 35840.0)
+    r = np.full(vp, datagen.BF16_NEG_INF, dtype=np.uint16)
+    r[:vr] = datagen.f32_to_bf16_bits(np.array([-40000.0], np.float32))[0]
+    rows.append(r)
+    inside.append(False)
+    logits = np.stack(rows)
+    n = logits.shape[0]
+    temps = np.full(n, 0.05, np.float32)
+    top_p = np.full(n, 0.9, np.float32)
+    top_k = np.full(n, -1, np.int32)
+    targets = np.full(n, 17, np.int64)
+    inside = np.array(inside)
+    c = np.float32(np.float32(1.4426950408889634) / np.float32(0.05))
+    for i in range(n):
+        m = float(datagen.bf16_bits_to_f32(logits[i, :vr]).max())
+        assert (abs(float(np.float32(np.float32(m) * c))) < 2.0 ** 20) == inside[i]
+    want_pol, want_ref, infos = O.nucleus_logp(logits, vr, temps, top_p, top_k, targets)
+    tol = row_tolerance(logits, vr, temps)
+    lg = upload_logits(logits)
+    for groups in (1, 8):
+        pol, ref, lse, state = rlk.logp_nucleus(lg, upload(temps, torch.float32), upload(top_p, torch.float32),
+                                                upload(top_k, torch.int32), upload(targets, torch.int64),
+                                                vocab_real=vr, groups=groups, return_state=True)
+        torch.cuda.synchronize()
+        pol, ref, state = to_host(pol), to_host(ref), to_host(state)
+        assert_close(ref, want_ref, tol=tol, what=f"search range ref g{groups}")
+        assert np.all(np.isnan(pol[~inside])), pol
+        assert np.all(state[~inside, 2] == -1), state
+        assert_nucleus_close(pol[inside], want_pol[inside], [infos[i] for i in np.flatnonzero(inside)],
+                             tol=tol[inside], what=f"search range policy g{groups}")
+
+
 # BF16 patterns at and just past the ends of the support window's value
 # ranges: the top (65535.x is the largest magnitude inside, 65536 and the next
 # value outside, both signs), the smallest magnitudes (2^-24 inside, the next
