@@ -135,9 +135,21 @@ typedef struct rlk_support_state {
  *                   is the whole real vocabulary; NaN for an invalid top_p
  *                   (outside (0, 1]) or top_k (not -1 and not in
  *                   [1, vocab_real]).
- *   ref_out[i]    = byte-identical to rlk_logp_full's logp_out[i].
- *   lse_out        [n_rows] float32, byte-identical to rlk_logp_full's
- *                  lse_out, or NULL.
+ *   ref_out[i]    = z_t - lse, the full-vocabulary logprob. For a row that
+ *                   needs a support search (top_p < 1 or top_k < vocab_real,
+ *                   T > 0) whose real tokens all lie in the search's window
+ *                   (BF16 magnitudes in [2^-24, 65536), +-0, or -inf), with its
+ *                   target among the real columns and its maximum in the
+ *                   search's range (below), lse comes from the same exact
+ *                   integer class masses as the policy: lse = (R +
+ *                   log2(Z) - 40) * ln 2 with Z the row's total mass in units
+ *                   of 2^(R-40); within the tolerance of rlk_logp_full's value
+ *                   (a float32 ulp apart on the benchmark rows). Every other
+ *                   row's reference is byte-identical to rlk_logp_full's
+ *                   logp_out[i]. Either way the bytes depend only on the row.
+ *   lse_out        [n_rows] float32, that lse (byte-identical to
+ *                  rlk_logp_full's lse_out on the rows of its reference), or
+ *                  NULL.
  *   support_out    [n_rows] rlk_support_state (16 bytes each), or NULL.
  *   top_p  [n_rows] float32;  top_k [n_rows] int32.
  *   workspace      rlk_logp_workspace_bytes(n_rows, layout, 1) bytes, 16-byte

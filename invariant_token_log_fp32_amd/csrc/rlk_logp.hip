@@ -10,14 +10,18 @@
 //                      groups > 1 and by rlk_logp_shard_summaries on a slice.
 //   k_merge            one thread per row: the same fixed-order merge over the
 //                      rank-major summaries (groups > 1, rlk_logp_merge).
-//   k_nucleus_g1       groups == 1 support path in one launch: the shard-waves
-//                      also count every token into an LDS window of BF16
-//                      classes; then the merge (reference logprob, wavefront
-//                      1) beside the top-k/top-p support from the exact
-//                      integer class masses (wavefront 0), and the policy
-//                      logprob.
-//   k_nucleus          groups > 1: the same per-row support search on the
-//                      summaries k_rank_summaries stored.
+//   k_nucleus_g1       groups == 1 support path in one launch: a row that
+//                      needs a search is streamed once by the shard-waves,
+//                      which only count its tokens into an LDS window of BF16
+//                      classes; the eight waves then sum the exact integer
+//                      class masses step by step, and wave 0 takes the
+//                      reference logprob, the top-k/top-p support and the
+//                      policy logprob from them. Other rows stream the float32
+//                      shard summaries (a second pass for the rare searched
+//                      rows that cannot use the window).
+//   k_nucleus          groups > 1: the same per-row logic on the summaries
+//                      k_rank_summaries stored, after a pass that fills the
+//                      window.
 //   k_backward         gradient of the reference and policy logprobs with
 //                      respect to the BF16 logits, from the forward's per-row
 //                      statistics; 1024-thread workgroups over (row, column
@@ -161,38 +165,42 @@ __global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(6, 
   const float p = top_p[row];
   const int64_t k = top_k[row];
   const int64_t tg = target[row];
-  if (search_needed(t, p, k, vocab_real)) {
-    // the shard-waves build the key histogram while they stream the row
-    window_clear(L);
-    __syncthreads();
-    WindowHook hook(L.u.win);
-    const ShardSummary s = summarize_row_shard(rowp + col0, col0, shard_width, vocab_real, t, tg, hook);
+  if (!search_needed(t, p, k, vocab_real)) {
+    // the reference from the shard summaries; the policy is the reference or NaN
+    NoHookLate none;
+    const ShardSummary s = summarize_row_shard(rowp + col0, col0, shard_width, vocab_real, t, tg, none);
     if ((threadIdx.x & (kWave - 1)) == 0) L.sm[wave] = s;
+    __syncthreads();
+    if (wave == 0) unsearched_row(L, row, vocab_real, shard_width, t, p, k, tg, policy_out, ref_out, lse_out, state_out);
+    return;
+  }
+  // The shard-waves only count the row's tokens into the window; the wavefront
+  // whose shard holds the target reads its BF16 pattern.
+  window_clear(L);
+  __syncthreads();
+  {
+    int64_t nc = vocab_real - col0;
+    nc = nc < 0 ? 0 : (nc > shard_width ? shard_width : nc);
+    const bool own_target = (tg >= col0) && (tg < col0 + nc);  // wave-uniform
+    const uint32_t tb = own_target ? static_cast<uint32_t>(rowp[tg]) : 0u;  // issued before the pass
+    WindowHook hook(L.u.win);
+    count_shard<kRefGroup>(rowp + col0, static_cast<int>(nc), static_cast<int>(threadIdx.x & (kWave - 1)), hook);
     hook.publish(L);
-  } else {
+    if (own_target && (threadIdx.x & (kWave - 1)) == 0) L.tbits = tb;
+  }
+  __syncthreads();
+  bool odd = false;  // block-uniform: a real token outside the window
+  for (int w = 0; w < kNucWaves; ++w) odd |= (L.red_flag[w] != 0);
+  if (!odd && exact_row(L, row, vocab_real, t, p, k, tg, L.tbits, policy_out, ref_out, lse_out, state_out)) return;
+  // The other rows (a token outside the window, no finite token, a target
+  // outside the real columns, a maximum beyond the search's range): the
+  // float32 shard summaries from a second pass, then the block-wide driver.
+  {
     NoHookLate none;
     const ShardSummary s = summarize_row_shard(rowp + col0, col0, shard_width, vocab_real, t, tg, none);
     if ((threadIdx.x & (kWave - 1)) == 0) L.sm[wave] = s;
   }
   __syncthreads();
-  // A row with every token in the window finishes in wavefronts 0 (search)
-  // and 1 (merge), a row with no search in wavefront 0; the other wavefronts
-  // are done. A row with a token outside the window takes the general path
-  // with the whole block.
-  bool odd = false;  // block-uniform
-  const bool searched = search_needed(t, p, k, vocab_real);
-  if (searched)
-    for (int w = 0; w < kNucWaves; ++w) odd |= (L.red_flag[w] != 0);
-  if (!odd) {
-    if (searched) {
-      if (wave <= 1)
-        nucleus_row_pair(L, wave, row, vocab_real, shard_width, t, p, k, tg, policy_out, ref_out, lse_out,
-                         state_out);
-    } else if (wave == 0) {
-      nucleus_row_wave(L, row, vocab_real, shard_width, t, p, k, tg, policy_out, ref_out, lse_out, state_out);
-    }
-    return;
-  }
   nucleus_row(L, rowp, row, vocab_real, shard_width, t, p, k, tg, true, policy_out, ref_out, lse_out, state_out);
 }
 

@@ -17,28 +17,30 @@
 // the support does not depend on the schedule of any atomic; the test
 // "cumulative >= p * Z" is evaluated exactly as cumulative >= ceil(p * Z).
 //
-// Fast path: every token is counted (LDS u32 atomics) in a window of classes:
+// Exact path: every token is counted (LDS u32 atomics) in a window of classes:
 // the BF16 values of magnitude in [2^-24, 65536) of either sign, interleaved
 // by magnitude (slot 2*(m - m_lo) + sign, m the 15-bit magnitude pattern),
 // plus one class for +-0; -inf tokens are counted apart (mass 0). The slots of
 // two tokens come from three packed 16-bit instructions, and one maximum over
 // a vector's eight slots tells whether all of them lie in the window. Classes
 // are visited in value order (positive slots from the largest magnitude down,
-// the zero class, negative slots from the smallest magnitude up). With groups == 1 the
-// shard-waves count while they stream the row for the reference logprob, so
-// the support costs no extra pass; otherwise one pass builds it. The row
-// maximum is the first non-empty class, class masses are count * weight, and
-// the thresholds come from prefix sums over the classes, computed by one
-// wavefront while the rest of the workgroup has finished (with groups == 1 a
-// second wavefront merges the shard summaries meanwhile). When top-k is off,
-// the top-p threshold ceil(p * Z) is first bracketed from the float shard
-// sums, so the total Z is summed only when the bracket cannot decide; a scan
-// that runs past three steps skips ahead by four-step mass totals.
+// the zero class, negative slots from the smallest magnitude up). With
+// groups == 1 the shard-waves count while they stream the row, and that is
+// all they do with it; otherwise one pass builds the window. The row maximum
+// is the first non-empty class and class masses are count * weight. The eight
+// wavefronts sum the classes' counts and masses in steps of 256 classes in
+// parallel; from the step totals one wavefront has the exact total Z, finds
+// the steps of the thresholds by prefix sums over the steps, and scans only
+// those steps class by class. The same exact total gives the row's reference
+// logprob, so a searched row needs no float32 sums at all. A row without a
+// search, or whose tokens are not all in the window, or whose maximum is
+// beyond the search's range, takes its reference from the float32 shard sums
+// instead (a second pass over the row when the first one only counted).
 // General path, for rows with a token outside the window (a nonzero value of
 // magnitude below 2^-24, or 65536 and beyond): an exact-maximum pass, then a
 // 4096-bin histogram of (count, mass) over key >> 4, then the 16 keys of each
 // boundary bin, each from another pass over the row. Both paths produce the
-// same integers and therefore the same output bytes.
+// same integers and therefore the same support and policy bytes.
 #pragma once
 
 #include "logp_device.hpp"
@@ -196,6 +198,15 @@ struct NucGeneral {
   u64 sub_mass[kSub];
 };
 
+// Classes are visited in steps of 256 ranks: the positive slots in 20 steps,
+// the zero class alone, the negative slots in 20 steps.
+constexpr int kStepRanks = 4 * kWave;           // 256 ranks per step
+constexpr int kPosSteps = kNMag / kStepRanks;   // 20
+constexpr int kZeroStep = kPosSteps;
+constexpr int kSteps = 2 * kPosSteps + 1;
+static_assert(kNMag % kStepRanks == 0, "steps cover whole magnitude ranges");
+static_assert(kSteps <= kWave, "one lane per step in the step prefix sums");
+
 struct NucLds {
   ShardSummary sm[kShards];
   // row state, written by thread 0 before a block-wide support search
@@ -222,11 +233,11 @@ struct NucLds {
   uint32_t scan_cnt_above;
   u64 scan_mass_above;
   int in_range;      // general path: the row maximum lies in the search's range
-  // the row merge, handed from wavefront 1 to wavefront 0 (RowStart)
-  float rs_ref;
-  float rs_lse;
-  uint32_t rs_bt;
-  int rs_status;
+  // exact path: count and mass of each step of 256 classes, and the target's
+  // BF16 pattern
+  uint32_t st_c[kSteps];
+  u64 st_m[kSteps];
+  uint32_t tbits;
   union alignas(16) {
     uint32_t win[kWinWords];        // interleaved slots, the zero class, a pad word
     u64 win_pairs[kWinWords / 2];   // the same as 64-bit pairs, for clearing
@@ -389,6 +400,58 @@ struct WindowHook {
   }
 };
 
+// One wavefront's pass over its shard of a row that only counts the tokens
+// into the window (groups == 1; no float32 sums). Lane l takes the shard's
+// 16-byte vectors l, l + 64, ... in chunks of U per lane, and the next chunk's
+// loads are issued before the current chunk is counted; the vectors after the
+// last whole chunk go in one batch, then the partial vector of the shard's
+// last columns. `shard` points at the shard's first column; ncols of its
+// columns are real.
+template <int U>
+__device__ __forceinline__ void count_shard(const uint16_t* __restrict__ shard, int ncols, int lane,
+                                            WindowHook& hook) {
+  const u32x4* __restrict__ base = reinterpret_cast<const u32x4*>(shard);
+  const int nfull = ncols >> 3;
+  const int tail = ncols & 7;
+  constexpr int kStep = U * kWave;
+  const int nmain = nfull - nfull % kStep;
+  int first = 0;
+  if (nmain > 0) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(base + u * kWave + lane);
+    for (; first + kStep < nmain; first += kStep) {
+      u32x4 nv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) nv[u] = __builtin_nontemporal_load(base + first + kStep + u * kWave + lane);
+#pragma unroll
+      for (int u = 0; u < U; ++u) hook.full(v[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = nv[u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) hook.full(v[u]);
+    first = nmain;
+  }
+  if (first < nfull) {
+    const int cnt = (nfull - first + kWave - 1) / kWave;  // at most U vectors per lane, wave-uniform
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int vi = first + u * kWave + lane;
+      if (u < cnt && vi < nfull) v[u] = __builtin_nontemporal_load(base + vi);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (u < cnt && first + u * kWave + lane < nfull) hook.full(v[u]);
+  }
+  if (tail && lane == (nfull & (kWave - 1))) {
+    const u32x4 v = base[nfull];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int e = 0; e < tail; ++e) hook.one((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+  }
+}
+
 template <typename Lds>
 __device__ __forceinline__ void window_clear(Lds& L) {
   for (int i = threadIdx.x; i < kWinWords / 2; i += kNucThreads) L.u.win_pairs[i] = 0ull;
@@ -432,32 +495,23 @@ __device__ __forceinline__ int wave_min(int v) {
 }
 
 // ---------------------------------------------------------------------------
-// Fast path, in one wavefront (no block barriers), for a row whose every real
-// token is in the window or is -inf (the hook totals say so). The row maximum
-// is the first non-empty class, R = ceil(fl32(M*c)), and a class weighs
-// count * floor(2^(x*c - R) * 2^40): exactly the integers the general path
-// sums per token. Scans in value order find the top-k boundary (count >= k)
-// and then the top-p boundary (cumulative mass >= ceil(p * Z_k), an exact
-// integer test). The classes are visited in steps of 256 ranks: the positive
-// slots in 20 steps, the zero class alone, the negative slots in 20 steps. In
-// a step lane l holds ranks 4l .. 4l+3 (two 16-byte LDS reads cover the 8
-// interleaved slots of its 4 magnitudes); prefix sums come from a lane-local
-// scan plus a DPP scan of the lane totals, and a crossing is located with a
-// ballot. Every value it returns is wave-uniform.
+// Exact path, for a row whose every real token is in the window or is -inf
+// (the hook totals say so): all eight wavefronts, then wavefront 0. The row
+// maximum M is the first non-empty class, R = ceil(fl32(M*c)), and a class
+// weighs count * floor(2^(x*c - R) * 2^40): exactly the integers the general
+// path sums per token. The classes are visited in steps of 256 ranks: the
+// positive slots in 20 steps, the zero class alone, the negative slots in 20
+// steps. In a step lane l holds ranks 4l .. 4l+3 (two 16-byte LDS reads cover
+// the 8 interleaved slots of its 4 magnitudes). The wavefronts sum the count
+// and the mass of every step from the maximum's on in parallel; one barrier;
+// then wavefront 0 has the row's exact total Z from the step totals, and
+// prefix sums over the steps locate the step of the top-k boundary (first
+// class whose cumulative count reaches k) and of the top-p boundary (first
+// class, inside the top-k set, whose cumulative mass reaches ceil(p * Z_k), an
+// exact integer test); each of those steps is then scanned class by class (a
+// lane-local prefix plus a DPP scan of the lane totals, and a ballot). The
+// same total gives the reference logprob: lse = (R + log2(Z) - 40) * ln 2.
 // ---------------------------------------------------------------------------
-struct FastSupport {
-  float R;
-  int kappa;       // rank of the last kept class, or kNoRank for the -inf class
-  uint32_t cnt_s;  // tokens in the support
-  u64 z_s;         // support mass (2^-40 units relative to 2^R)
-  bool in_range;   // the row maximum lies in the search's range (kMaxSupportArg)
-};
-
-constexpr int kStepRanks = 4 * kWave;           // 256 ranks per step
-constexpr int kPosSteps = kNMag / kStepRanks;   // 20
-constexpr int kZeroStep = kPosSteps;
-constexpr int kSteps = 2 * kPosSteps + 1;
-static_assert(kNMag % kStepRanks == 0, "steps cover whole magnitude ranges");
 
 // Rank of element e of lane `lane` in step s (-1 for the unused elements of
 // the zero step).
@@ -539,11 +593,9 @@ __device__ __forceinline__ u64 class_mass(uint32_t cnt, uint32_t hi, uint32_t lo
   return (static_cast<u64>(hp) << 32) + static_cast<u64>(cnt) * lo;
 }
 
-// One step: per-class counts and masses, and the inclusive cumulative count
-// and mass of each class counted from the step's first class (lane-local
-// prefix plus the exclusive DPP scan of the lanes). Returns the step's totals
-// through rc / rm, and false (wave-uniform, with zero totals and Q left
-// unset) when all its classes are empty.
+// One step, class by class: per-class counts and masses, and the inclusive
+// cumulative count and mass of each class counted from the step's first class
+// (lane-local prefix plus the exclusive DPP scan of the lanes).
 struct StepRound {
   uint32_t cnt[4];
   u64 mass[4];
@@ -551,15 +603,9 @@ struct StepRound {
   u64 cum_m[4];
 };
 
-__device__ __forceinline__ bool step_round(const NucLds& L, int s, float c, float nr, StepRound& Q, uint32_t& rc,
-                                           u64& rm) {
+__device__ __forceinline__ void step_round(const NucLds& L, int s, float c, float nr, StepRound& Q) {
   const int lane = threadIdx.x & (kWave - 1);
   step_counts(L, s, lane, Q.cnt);
-  if (__ballot((Q.cnt[0] | Q.cnt[1] | Q.cnt[2] | Q.cnt[3]) != 0u) == 0ull) {  // wave-uniform
-    rc = 0u;
-    rm = 0ull;
-    return false;
-  }
   uint32_t pc = 0;
   u64 pm = 0;
 #pragma unroll
@@ -573,351 +619,74 @@ __device__ __forceinline__ bool step_round(const NucLds& L, int s, float c, floa
     Q.cum_c[e] = pc;
     Q.cum_m[e] = pm;
   }
-  const uint32_t ic = wave_incl_scan<uint32_t>(pc, lane);
-  const u64 im = wave_incl_scan<u64>(pm, lane);
-  const uint32_t ec = ic - pc;
-  const u64 em = im - pm;
+  const uint32_t ec = wave_incl_scan<uint32_t>(pc, lane) - pc;
+  const u64 em = wave_incl_scan<u64>(pm, lane) - pm;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     Q.cum_c[e] += ec;
     Q.cum_m[e] += em;
   }
-  rc = readlane_u32(ic, kWave - 1);
-  rm = readlane_u64(im, kWave - 1);
-  return true;
 }
 
-constexpr int kBatch = 4;       // steps whose LDS reads a scan issues together
-constexpr int kRoundSteps = 3;  // steps a top-p scan takes class by class before it skips ahead
+constexpr int kBatch = 4;  // steps whose LDS reads the row-maximum scan issues together
 
-// Count and mass of the classes that `lane` holds in steps s .. s + kBatch - 1
-// (steps at or past s_end count zero), summed lane-locally; the LDS reads of
-// the kBatch steps are issued before any of them is used.
-__device__ __forceinline__ void batch_lane_sums(const NucLds& L, int s, int s_end, int lane, float c, float nr,
-                                                uint32_t (&pc)[kBatch], u64 (&pm)[kBatch]) {
-  uint32_t cn[kBatch][4];
+// Rank of the first non-empty class (the row maximum), kNoRank when the
+// window is empty (wave-uniform). The LDS reads of kBatch steps are issued
+// together and one wave minimum finds the first non-empty class.
+__device__ __forceinline__ int window_top_rank(const NucLds& L, int lane) {
+  for (int s0 = 0; s0 < kSteps; s0 += kBatch) {
+    uint32_t cn[kBatch][4];
 #pragma unroll
-  for (int b = 0; b < kBatch; ++b) {
-    if (s + b < s_end) {
-      step_counts(L, s + b, lane, cn[b]);
-    } else {
+    for (int b = 0; b < kBatch; ++b) {
+      if (s0 + b < kSteps) {
+        step_counts(L, s0 + b, lane, cn[b]);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) cn[b][e] = 0u;
+        for (int e = 0; e < 4; ++e) cn[b][e] = 0u;
+      }
+    }
+    int hit = -1;  // first step of the batch with a token (wave-uniform)
+#pragma unroll
+    for (int b = kBatch - 1; b >= 0; --b)
+      if (__ballot((cn[b][0] | cn[b][1] | cn[b][2] | cn[b][3]) != 0u)) hit = b;
+    if (hit >= 0) {
+      int j = kNoRank;
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b)
+        if (b == hit) {
+#pragma unroll
+          for (int e = 3; e >= 0; --e)
+            if (cn[b][e]) j = step_rank(s0 + b, lane, e);
+        }
+      return wave_min(j);
     }
   }
-#pragma unroll
-  for (int b = 0; b < kBatch; ++b) {
-    uint32_t sum_hi = 0u;  // sum of count * hi: below 2^24 * 256 over a row
-    u64 sum_lo = 0ull;
-    pc[b] = 0u;
+  return kNoRank;
+}
+
+// Count and mass of one step, summed over the wave (wave-uniform). The
+// weights of a step whose classes are all empty, or that lies at or past
+// s_end (no class of nonzero weight), are skipped.
+__device__ __forceinline__ void step_total(const NucLds& L, int s, int s_end, int lane, float c, float nr,
+                                           uint32_t& tc, u64& tm) {
+  uint32_t cn[4];
+  step_counts(L, s, lane, cn);
+  const uint32_t pc = (cn[0] + cn[1]) + (cn[2] + cn[3]);
+  uint32_t sum_hi = 0u;  // sum of count * hi: below 2^24 * 256 over a row
+  u64 sum_lo = 0ull;
+  if (s < s_end && __ballot(pc != 0u)) {  // wave-uniform
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       uint32_t hi, lo;
-      weight_parts(step_bits(s + b, lane, e), c, nr, hi, lo);
-      sum_hi += static_cast<uint32_t>(__umul24(cn[b][e], hi));
-      sum_lo += static_cast<u64>(cn[b][e]) * lo;
-      pc[b] += cn[b][e];
+      weight_parts(step_bits(s, lane, e), c, nr, hi, lo);
+      sum_hi += static_cast<uint32_t>(__umul24(cn[e], hi));
+      sum_lo += static_cast<u64>(cn[e]) * lo;
     }
-    pm[b] = (static_cast<u64>(sum_hi) << 32) + sum_lo;
   }
+  tc = wave_total<uint32_t>(pc);
+  tm = wave_total<u64>((static_cast<u64>(sum_hi) << 32) + sum_lo);
 }
 
-__device__ __forceinline__ FastSupport support_fast_wave(const NucLds& L, int64_t vocab_real, int shard_width,
-                                                         bool k_active, int64_t k_in, bool p_active, float p,
-                                                         float c) {
-  const int lane = threadIdx.x & (kWave - 1);
-  FastSupport out;
-  uint32_t ninf_n = 0;
-  for (int w = 0; w < kNucWaves; ++w) ninf_n += L.red_u32[w][1];
-  const uint32_t total_c = static_cast<uint32_t>(vocab_real) - ninf_n;
-
-  // the row maximum: the first non-empty class, at or above the class of the
-  // largest shard-summary m (each is a token of the row, so it lies in the
-  // window); kBatch steps per iteration, their LDS reads issued together
-  float mb = -INFINITY;
-#pragma unroll
-  for (int sh = 0; sh < kShards; ++sh) mb = fmaxf(mb, L.sm[sh].m);
-  int jtop = kNoRank;
-  if (mb > -INFINITY) {
-    const uint32_t sl = window_slot(__float_as_uint(mb) >> 16);
-    const int sb = (sl == kSlotOut) ? kSteps - 1 : rank_step(slot_rank(sl));
-    for (int s0 = 0; s0 <= sb; s0 += kBatch) {
-      uint32_t cn[kBatch][4];
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        if (s0 + b <= sb) {
-          step_counts(L, s0 + b, lane, cn[b]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) cn[b][e] = 0u;
-        }
-      }
-      int hit = -1;  // first step of the batch with a token (wave-uniform)
-#pragma unroll
-      for (int b = kBatch - 1; b >= 0; --b)
-        if (__ballot((cn[b][0] | cn[b][1] | cn[b][2] | cn[b][3]) != 0u)) hit = b;
-      if (hit >= 0) {
-        int j = kNoRank;
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b)
-          if (b == hit) {
-#pragma unroll
-            for (int e = 3; e >= 0; --e)
-              if (cn[b][e]) j = step_rank(s0 + b, lane, e);
-          }
-        jtop = wave_min(j);
-        break;
-      }
-    }
-  }
-  out.kappa = kNoRank;
-  out.cnt_s = total_c + ninf_n;
-  out.z_s = 0;
-  out.R = 0.0f;
-  out.in_range = true;
-  if (jtop == kNoRank) return out;  // no finite token: not reached on a searched row
-  const float m = rank_value(jtop);
-  const float R = ref_exponent(m, c);
-  const float nr = -R;
-  out.R = R;
-  out.in_range = fabsf(m * c) < kMaxSupportArg;  // wave-uniform
-  if (!out.in_range) return out;
-  const int sfirst = rank_step(jtop);
-
-  // exact mass of the classes from step s_start on: lane-local sums over the
-  // steps, one wave reduction. Every class with a nonzero weight lies before
-  // the first step whose first class is below 2^-42 (the classes are in
-  // decreasing value order).
-  // The steps from s_end on hold no class of nonzero weight: the first step
-  // after sfirst whose first (largest) class weighs 0, found by one ballot
-  // with lane l testing step l.
-  const u64 zero_from = __ballot(lane > sfirst && lane < kSteps &&
-                                 fmaf(rank_value(step_rank(lane < kSteps ? lane : 0, 0, 0)), c, nr) < -42.0f);
-  const int s_end = zero_from ? __builtin_ctzll(zero_from) : kSteps;
-  auto exact_mass_from = [&](int s_start) -> u64 {
-    u64 acc = 0;
-    for (int s = s_start; s < s_end; s += kBatch) {
-      uint32_t pc[kBatch];
-      u64 pm[kBatch];
-      batch_lane_sums(L, s, s_end, lane, c, nr, pc, pm);
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) acc += pm[b];
-    }
-    return wave_total<u64>(acc);
-  };
-
-  // top-k boundary by count (the -inf class when the window holds fewer than k)
-  int jk = kNoRank;
-  uint32_t cnt_k = total_c + ninf_n;
-  u64 z_k = 0;
-  bool z_k_known = false;  // otherwise z_k is the row's total mass, not yet summed
-  if (k_active && static_cast<uint64_t>(total_c) >= static_cast<uint64_t>(k_in)) {
-    const uint64_t k = static_cast<uint64_t>(k_in);
-    uint32_t carry_c = 0;
-    u64 carry_m = 0;
-    for (int s = sfirst; s < kSteps; ++s) {
-      StepRound Q;
-      uint32_t rc;
-      u64 rm;
-      if (!step_round(L, s, c, nr, Q, rc, rm)) continue;  // no token in this step
-      int hit_e = -1;
-#pragma unroll
-      for (int e = 3; e >= 0; --e) {
-        const uint64_t cum = carry_c + Q.cum_c[e];
-        if (cum >= k && cum - Q.cnt[e] < k) hit_e = e;
-      }
-      const u64 ball = __ballot(hit_e >= 0);
-      if (ball) {  // wave-uniform
-        const int hl = __builtin_ctzll(ball);
-        const int he = __builtin_amdgcn_readlane(hit_e, hl);
-        uint32_t hc = 0;
-        u64 hm = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (e == he) {
-            hc = Q.cum_c[e];
-            hm = Q.cum_m[e];
-          }
-        jk = step_rank(s, hl, he);
-        cnt_k = carry_c + readlane_u32(hc, hl);
-        z_k = carry_m + readlane_u64(hm, hl);
-        z_k_known = true;
-        break;
-      }
-      carry_c += rc;
-      carry_m += rm;
-    }
-  }
-
-  // top-p boundary by mass inside the top-k set: the first class whose
-  // cumulative mass reaches P = ceil(p * z_k). Scanning for thresholds
-  // p_lo <= P <= p_hi finds classes j_lo <= j* <= j_hi (cumulative masses only
-  // grow), so j_lo == j_hi decides j* exactly. A scan runs from a position
-  // (a step and the count and mass of every class before it) and leaves the
-  // position after the step where it found p_hi's crossing (or at the end of
-  // the classes); `lo_pos` is the start of the step holding j_lo.
-  struct Hit {
-    int j;
-    uint32_t cnt;
-    u64 mass;
-  };
-  struct ScanPos {
-    int s;
-    uint32_t c;
-    u64 m;
-  };
-  auto scan_p = [&](ScanPos& pos, u64 p_lo, u64 p_hi, Hit& lo, ScanPos& lo_pos, int& j_hi) {
-    lo.j = -1;
-    j_hi = -1;
-    for (int n_round = 0; pos.s < kSteps; ++pos.s, ++n_round) {
-      if (n_round >= kRoundSteps) {
-        // skip ahead: the totals of the next kBatch steps carry the position
-        // up to the step where the pending threshold is crossed (cumulative
-        // masses only grow, so no class before it can be the crossing)
-        const u64 thr = (lo.j < 0) ? p_lo : p_hi;
-        uint32_t pc[kBatch];
-        u64 pm[kBatch];
-        batch_lane_sums(L, pos.s, s_end, lane, c, nr, pc, pm);
-        const u64 tm_all = wave_total<u64>((pm[0] + pm[1]) + (pm[2] + pm[3]));
-        if (pos.m + tm_all < thr) {  // wave-uniform: no crossing in the batch
-          pos.m += tm_all;
-          pos.c += wave_total<uint32_t>((pc[0] + pc[1]) + (pc[2] + pc[3]));
-          pos.s += kBatch - 1;  // the loop's increment moves past the batch
-          if (pos.s + 1 >= s_end) pos.s = kSteps - 1;  // no weight below: the end of the classes
-          continue;
-        }
-        // the crossing lies in the batch: the steps before it by their totals
-        u64 run = pos.m;
-        uint32_t runc = 0u;
-        int skip = kBatch - 1;
-#pragma unroll
-        for (int b = 0; b < kBatch - 1; ++b) {
-          if (skip == kBatch - 1) {
-            const u64 tm = wave_total<u64>(pm[b]);
-            if (run + tm >= thr) {
-              skip = b;
-            } else {
-              run += tm;
-              runc += pc[b];
-            }
-          }
-        }
-        pos.m = run;
-        pos.c += wave_total<uint32_t>(runc);
-        pos.s += skip;  // the step holding the crossing, scanned class by class below
-      }
-      StepRound Q;
-      uint32_t rc;
-      u64 rm;
-      if (!step_round(L, pos.s, c, nr, Q, rc, rm)) continue;  // no token in this step
-      int e_lo = -1, e_hi = -1;
-#pragma unroll
-      for (int e = 3; e >= 0; --e) {
-        const u64 cum = pos.m + Q.cum_m[e];
-        const int r = step_rank(pos.s, lane, e);
-        const bool inside = r >= 0 && r <= jk;
-        if (inside && cum >= p_lo && cum - Q.mass[e] < p_lo) e_lo = e;
-        if (inside && cum >= p_hi && cum - Q.mass[e] < p_hi) e_hi = e;
-      }
-      const u64 b_lo = __ballot(e_lo >= 0);
-      if (b_lo && lo.j < 0) {  // wave-uniform
-        const int hl = __builtin_ctzll(b_lo);
-        const int he = __builtin_amdgcn_readlane(e_lo, hl);
-        uint32_t hc = 0;
-        u64 hm = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (e == he) {
-            hc = Q.cum_c[e];
-            hm = Q.cum_m[e];
-          }
-        lo.j = step_rank(pos.s, hl, he);
-        lo.cnt = pos.c + readlane_u32(hc, hl);
-        lo.mass = pos.m + readlane_u64(hm, hl);
-        lo_pos = pos;
-      }
-      pos.c += rc;
-      pos.m += rm;
-      const u64 b_hi = __ballot(e_hi >= 0);
-      if (b_hi) {  // wave-uniform
-        const int hl = __builtin_ctzll(b_hi);
-        j_hi = step_rank(pos.s, hl, __builtin_amdgcn_readlane(e_hi, hl));
-        ++pos.s;
-        break;
-      }
-    }
-  };
-
-  int kappa = jk;
-  uint32_t cnt_s = cnt_k;
-  u64 z_s = z_k;
-  if (p_active) {
-    Hit lo;
-    ScanPos lo_pos = {sfirst, 0u, 0ull};
-    ScanPos pos = {sfirst, 0u, 0ull};
-    int j_hi = -1;
-    bool decided = false;
-    if (!z_k_known) {
-      // The shard summaries bound the total. Each l_s sums positive float32
-      // terms 2^(x*c - r_s) through at most `depth` roundings (a lane's
-      // vectors plus a partial one, 3 pairwise levels, 6 butterfly levels):
-      // relative error <= depth * 2^-24. A term and the token's integer
-      // weight floor(2^(x*c - R) * 2^40) differ by the rounding of their
-      // exponent arguments, by v_exp_f32 (about 2^-23 each), by the floor
-      // (under one unit per token on a total of at least 2^39 units) and by
-      // terms whose weight floors to 0 (under 1/4 unit each). The arguments:
-      // x*c - r_s is below D_s + 1 (D_s = R - r_s >= 0), and the term of the
-      // maximum of the chunk that fixed r_s makes l_s >= 1/2, so the terms
-      // with x*c - r_s >= -31 are rounded by at most half an ulp of
-      // max(31, D_s + 1) and all the others together move l_s by under 2^-30
-      // relative; likewise x*c - R lies in [-42, 0] where a weight is nonzero,
-      // rounded by at most 2^-20 (half an ulp of 31) above -31, the rest under
-      // 2^-30 relative. A relative argument error d changes 2^arg by d*ln 2 <
-      // d. The bracket takes twice the sum.
-      const int depth = (shard_width / 8 + kWave) / kWave + 1 + 3 + 6;
-      float dmax = 0.0f;
-#pragma unroll
-      for (int sh = 0; sh < kShards; ++sh)
-        if (L.sm[sh].l > 0.0f) dmax = fmaxf(dmax, R - L.sm[sh].r);
-      const double karg = fmax(31.0, static_cast<double>(dmax) + 1.0);
-      const double half_ulp = ldexp(1.0, ilogb(karg) - 24);
-      const double eps = 2.0 * (static_cast<double>(depth) * 0x1p-24 + half_ulp + 0x1p-20 + 0x1p-22 + 0x1p-30 +
-                                1.25 * static_cast<double>(vocab_real) * 0x1p-39);
-      double zf = 0.0;
-#pragma unroll
-      for (int sh = 0; sh < kShards; ++sh) {
-        const float l = L.sm[sh].l;
-        if (l > 0.0f) zf += ldexp(static_cast<double>(l), static_cast<int>(L.sm[sh].r - R) + 40);
-      }
-      const u64 z_lo = static_cast<u64>(zf * (1.0 - eps));
-      const u64 z_hi = static_cast<u64>(zf * (1.0 + eps)) + 1ull;
-      ScanPos lo_pos_b = lo_pos;
-      scan_p(pos, ceil_mul(p, z_lo), ceil_mul(p, z_hi), lo, lo_pos_b, j_hi);
-      decided = (lo.j >= 0) && (lo.j == j_hi);
-      if (!decided) {
-        // the exact total: the scanned classes' mass plus the mass below them
-        z_k = pos.m + exact_mass_from(pos.s);
-        z_k_known = true;
-        // P >= ceil(p * z_lo), so the exact crossing is not above j_lo: the
-        // exact scan restarts at the step holding j_lo
-        pos = (lo.j >= 0) ? lo_pos_b : ScanPos{sfirst, 0u, 0ull};
-      }
-    }
-    if (!decided) {
-      const u64 P = ceil_mul(p, z_k);
-      scan_p(pos, P, P, lo, lo_pos, j_hi);
-    }
-    kappa = lo.j;
-    cnt_s = lo.cnt;
-    z_s = lo.mass;
-  }
-  // (top-p off and top-k keeping every finite token: the support is the whole
-  // vocabulary, whose policy output is the reference output; z_s is unused)
-  out.kappa = kappa;
-  out.cnt_s = cnt_s;
-  out.z_s = z_s;
-  return out;
-}
 
 // ---------------------------------------------------------------------------
 // General path (any row whose thresholds are not resolved by the fast path).
@@ -1206,82 +975,174 @@ __device__ __forceinline__ void write_policy(int64_t row, int64_t vocab_real, bo
   }
 }
 
-// Whole row in wavefront 0 alone, for a row whose window is complete (every
-// real token in the window or -inf) or that needs no search: no block
-// barriers, so the other wavefronts of the workgroup may already have ended.
-// Every lane computes the same merge; lane 0 writes.
-__device__ __forceinline__ void nucleus_row_wave(const NucLds& L, int64_t row, int64_t vocab_real, int shard_width,
-                                                 float t, float p, int64_t k, int64_t tg,
-                                                 float* __restrict__ policy_out, float* __restrict__ ref_out,
-                                                 float* __restrict__ lse_out,
-                                                 rlk_support_state* __restrict__ state_out) {
-  const bool lead = (threadIdx.x == 0);
+// Outputs of a row that needs no search, in wavefront 0 (lane 0 writes): the
+// merge of the shard summaries gives the reference, and the policy is the
+// reference or NaN.
+__device__ __forceinline__ void unsearched_row(const NucLds& L, int64_t row, int64_t vocab_real, int shard_width,
+                                               float t, float p, int64_t k, int64_t tg,
+                                               float* __restrict__ policy_out, float* __restrict__ ref_out,
+                                               float* __restrict__ lse_out,
+                                               rlk_support_state* __restrict__ state_out) {
   const RowStart rs = row_start(L.sm, vocab_real, shard_width, t, p, k, tg);
-  if (lead) {
+  if (threadIdx.x == 0) {
     ref_out[row] = rs.ref;
     if (lse_out) lse_out[row] = rs.lse;
+    write_unsearched(row, rs, policy_out, state_out);
   }
-  if (rs.status != 0) {
-    if (lead) write_unsearched(row, rs, policy_out, state_out);
-    return;
-  }
-  const bool k_active = (k != -1) && (k < vocab_real);
-  const bool p_active = (p < 1.0f);
-  const FastSupport fs = support_fast_wave(L, vocab_real, shard_width, k_active, k, p_active, p, kLog2e / t);
-  if (lead) write_policy(row, vocab_real, true, fs.kappa, fs.cnt_s, fs.z_s, fs.R, fs.in_range, rs, t, policy_out,
-                 state_out);
 }
 
-// A searched row whose window is complete, in two wavefronts: wavefront 1
-// merges the summaries and writes the reference outputs while wavefront 0
-// runs the support search, then wavefront 0 writes the policy outputs. The
-// other wavefronts of the workgroup have ended, and a barrier waits only for
-// the wavefronts still running.
-__device__ __forceinline__ void nucleus_row_pair(NucLds& L, int wave, int64_t row, int64_t vocab_real,
-                                                 int shard_width, float t, float p, int64_t k, int64_t tg,
-                                                 float* __restrict__ policy_out, float* __restrict__ ref_out,
-                                                 float* __restrict__ lse_out,
-                                                 rlk_support_state* __restrict__ state_out) {
-  const bool lead = (threadIdx.x & (kWave - 1)) == 0;
-  FastSupport fs;
-  if (wave == 1) {
-    const RowStart rs = row_start(L.sm, vocab_real, shard_width, t, p, k, tg);
-    if (lead) {
-      ref_out[row] = rs.ref;
-      if (lse_out) lse_out[row] = rs.lse;
-      L.rs_ref = rs.ref;
-      L.rs_lse = rs.lse;
-      L.rs_bt = rs.bt;
-      L.rs_status = rs.status;
+// The reference and the policy of a row whose window is complete and holds
+// every real token or counts it as -inf, from the exact class masses. All
+// kNucWaves wavefronts call it. It returns false, block-uniformly and before
+// any barrier, when the row takes the float32 reference instead: a target
+// outside the real columns, no finite token, or a row maximum beyond the
+// search's range. Otherwise the wavefronts other than 0 return true after the
+// one barrier and wavefront 0 writes ref_out, lse_out, policy_out and
+// state_out for the row; bt is the target's BF16 pattern.
+__device__ __forceinline__ bool exact_row(NucLds& L, int64_t row, int64_t vocab_real, float t, float p, int64_t k,
+                                          int64_t tg, uint32_t bt, float* __restrict__ policy_out,
+                                          float* __restrict__ ref_out, float* __restrict__ lse_out,
+                                          rlk_support_state* __restrict__ state_out) {
+  if (tg < 0 || tg >= vocab_real) return false;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const float c = kLog2e / t;  // IEEE float32 division
+  // every wavefront finds the row maximum from the same counts
+  const int jtop = window_top_rank(L, lane);
+  if (jtop == kNoRank) return false;
+  const float m = rank_value(jtop);
+  if (!(fabsf(m * c) < kMaxSupportArg)) return false;
+  const float R = ref_exponent(m, c);
+  const float nr = -R;
+  const int sfirst = rank_step(jtop);
+  // The steps from s_end on hold no class of nonzero weight: the first step
+  // after sfirst whose first (largest) class weighs 0, found by one ballot
+  // with lane l testing step l (classes are in decreasing value order).
+  const u64 zero_from = __ballot(lane > sfirst && lane < kSteps &&
+                                 fmaf(rank_value(step_rank(lane < kSteps ? lane : 0, 0, 0)), c, nr) < -42.0f);
+  const int s_end = zero_from ? __builtin_ctzll(zero_from) : kSteps;
+  // step totals, in parallel: wavefront w takes steps sfirst + w, + 8, ...
+  for (int s = sfirst + wave; s < kSteps; s += kNucWaves) {
+    uint32_t tc;
+    u64 tm;
+    step_total(L, s, s_end, lane, c, nr, tc, tm);
+    if (lane == 0) {
+      L.st_c[s] = tc;
+      L.st_m[s] = tm;
     }
-  } else {
-    const bool k_active = (k != -1) && (k < vocab_real);
-    const bool p_active = (p < 1.0f);
-    fs = support_fast_wave(L, vocab_real, shard_width, k_active, k, p_active, p, kLog2e / t);
   }
   __syncthreads();
-  if (wave == 0 && lead) {
-    RowStart rs;
-    rs.ref = L.rs_ref;
-    rs.lse = L.rs_lse;
-    rs.bt = L.rs_bt;
-    rs.status = L.rs_status;
-    if (rs.status != 0)
-      write_unsearched(row, rs, policy_out, state_out);
-    else
-      write_policy(row, vocab_real, true, fs.kappa, fs.cnt_s, fs.z_s, fs.R, fs.in_range, rs, t, policy_out,
-                 state_out);
+  if (wave != 0) return true;
+
+  // Wavefront 0: lane s holds step s (nothing before sfirst); inclusive
+  // prefix sums over the steps.
+  const bool live = lane >= sfirst && lane < kSteps;
+  const uint32_t sc = live ? L.st_c[lane] : 0u;
+  const u64 sm = live ? L.st_m[lane] : 0ull;
+  const uint32_t cc = wave_incl_scan<uint32_t>(sc, lane);
+  const u64 cm = wave_incl_scan<u64>(sm, lane);
+  const uint32_t total_c = lane63(cc);  // the finite tokens
+  const u64 z = lane63(cm);             // the row's exact total mass
+  uint32_t ninf_n = 0;
+  for (int w = 0; w < kNucWaves; ++w) ninf_n += L.red_u32[w][1];
+
+  // top-k boundary by count (the -inf class when the row holds fewer than k
+  // finite tokens)
+  const bool k_active = (k != -1) && (k < vocab_real);
+  int jk = kNoRank;
+  uint32_t cnt_k = total_c + ninf_n;
+  u64 z_k = z;
+  if (k_active && static_cast<uint64_t>(total_c) >= static_cast<uint64_t>(k)) {
+    const uint64_t kk = static_cast<uint64_t>(k);
+    const int s = __builtin_ctzll(__ballot(static_cast<uint64_t>(cc) >= kk));  // first step reaching k
+    const uint32_t carry_c = readlane_u32(cc - sc, s);
+    const u64 carry_m = readlane_u64(cm - sm, s);
+    StepRound Q;
+    step_round(L, s, c, nr, Q);
+    int hit_e = -1;
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+      const uint64_t cum = carry_c + Q.cum_c[e];
+      if (cum >= kk && cum - Q.cnt[e] < kk) hit_e = e;
+    }
+    const u64 ball = __ballot(hit_e >= 0);  // nonzero: the step holds the k-th token
+    const int hl = __builtin_ctzll(ball);
+    const int he = __builtin_amdgcn_readlane(hit_e, hl);
+    uint32_t hc = 0;
+    u64 hm = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e == he) {
+        hc = Q.cum_c[e];
+        hm = Q.cum_m[e];
+      }
+    jk = step_rank(s, hl, he);
+    cnt_k = carry_c + readlane_u32(hc, hl);
+    z_k = carry_m + readlane_u64(hm, hl);
   }
+
+  // top-p boundary by mass inside the top-k set: the first class whose
+  // cumulative mass reaches P = ceil(p * z_k) <= z_k. Its step is the first
+  // whose inclusive mass reaches P, which is not after jk's step.
+  int kappa = jk;
+  uint32_t cnt_s = cnt_k;
+  u64 z_s = z_k;
+  if (p < 1.0f) {
+    const u64 P = ceil_mul(p, z_k);
+    const int s = __builtin_ctzll(__ballot(cm >= P));
+    const uint32_t carry_c = readlane_u32(cc - sc, s);
+    const u64 carry_m = readlane_u64(cm - sm, s);
+    StepRound Q;
+    step_round(L, s, c, nr, Q);
+    int e_p = -1;
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+      const u64 cum = carry_m + Q.cum_m[e];
+      const int r = step_rank(s, lane, e);
+      const bool inside = r >= 0 && r <= jk;
+      if (inside && cum >= P && cum - Q.mass[e] < P) e_p = e;
+    }
+    const u64 ball = __ballot(e_p >= 0);  // nonzero: the crossing lies in this step
+    const int hl = __builtin_ctzll(ball);
+    const int he = __builtin_amdgcn_readlane(e_p, hl);
+    uint32_t hc = 0;
+    u64 hm = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e == he) {
+        hc = Q.cum_c[e];
+        hm = Q.cum_m[e];
+      }
+    kappa = step_rank(s, hl, he);
+    cnt_s = carry_c + readlane_u32(hc, hl);
+    z_s = carry_m + readlane_u64(hm, hl);
+  }
+
+  if (lane == 0) {
+    // the reference: lse = (R + log2(Z) - 40) * ln 2, in float64 as for the shard merge
+    const double lse = (static_cast<double>(R) + (log2(static_cast<double>(z)) - 40.0)) * kLn2;
+    const float zt = __uint_as_float(bt << 16) / t;  // IEEE float32 division
+    RowStart rs;
+    rs.ref = static_cast<float>(static_cast<double>(zt) - lse);
+    rs.lse = static_cast<float>(lse);
+    rs.bt = bt;
+    rs.status = 0;
+    ref_out[row] = rs.ref;
+    if (lse_out) lse_out[row] = rs.lse;
+    write_policy(row, vocab_real, true, kappa, cnt_s, z_s, R, true, rs, t, policy_out, state_out);
+  }
+  return true;
 }
 
 // ---------------------------------------------------------------------------
-// Whole-row driver for all threads of the block: L.sm must hold the row's 8
-// shard summaries; when `window_built` the window and the hook totals are
-// already filled (the streaming pass counted the row). After the window is
-// complete, a row whose tokens all lie in it continues in wavefront 0 alone
-// (support_fast_wave; the other wavefronts return); other rows take the
-// general path with the whole block. Writes ref_out[row], policy_out[row] and,
-// when given, lse_out[row] and state_out[row].
+// Whole-row driver for all threads of the block, from the row's 8 float32
+// shard summaries in L.sm; when `window_built` the window and the hook totals
+// are already filled. A row that needs a search and whose real tokens all lie
+// in the window (or are -inf) takes the exact path; the other searched rows
+// take the float32 reference, with no support when the row maximum is beyond
+// the search's range, or with the general path's support when a token lies
+// outside the window. Writes ref_out[row], policy_out[row] and, when given,
+// lse_out[row] and state_out[row].
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restrict__ rowp, int64_t row,
                                             int64_t vocab_real, int shard_width, float t, float p, int64_t k,
@@ -1296,16 +1157,16 @@ __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restric
   rs.status = -2;
   if (tid == 0) {
     rs = row_start(L.sm, vocab_real, shard_width, t, p, k, tg);
-    ref_out[row] = rs.ref;
-    if (lse_out) lse_out[row] = rs.lse;
     L.search = (rs.status == 0);
-    if (rs.status == 0) {
-      L.k_active = (k != -1) && (k < vocab_real);
-      L.p_active = (p < 1.0f);
-      L.k = k;
-      L.p = p;
-      L.c = kLog2e / t;
-    } else {
+    L.tbits = rs.bt;
+    L.k_active = (k != -1) && (k < vocab_real);
+    L.p_active = (p < 1.0f);
+    L.k = k;
+    L.p = p;
+    L.c = kLog2e / t;
+    if (rs.status != 0) {
+      ref_out[row] = rs.ref;
+      if (lse_out) lse_out[row] = rs.lse;
       write_unsearched(row, rs, policy_out, state_out);
     }
   }
@@ -1321,12 +1182,20 @@ __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restric
   bool odd = false;  // block-uniform: a real token outside the window
   for (int w = 0; w < kNucWaves; ++w) odd |= (L.red_flag[w] != 0);
   if (!odd) {
-    if (tid >= kWave) return;
-    const FastSupport fs =
-        support_fast_wave(L, vocab_real, shard_width, L.k_active != 0, L.k, L.p_active != 0, L.p, L.c);
-    if (tid == 0) write_policy(row, vocab_real, true, fs.kappa, fs.cnt_s, fs.z_s, fs.R, fs.in_range, rs, t, policy_out,
-                 state_out);
+    if (exact_row(L, row, vocab_real, t, p, k, tg, L.tbits, policy_out, ref_out, lse_out, state_out)) return;
+    // the row maximum lies beyond the search's range: no support
+    if (tid == 0) {
+      ref_out[row] = rs.ref;
+      if (lse_out) lse_out[row] = rs.lse;
+      RowStart none = rs;
+      none.status = -1;
+      write_unsearched(row, none, policy_out, state_out);
+    }
     return;
+  }
+  if (tid == 0) {
+    ref_out[row] = rs.ref;
+    if (lse_out) lse_out[row] = rs.lse;
   }
   __syncthreads();  // the flags above are read before the general path reuses the block scratch
   support_general(L, rowp, vocab_real);

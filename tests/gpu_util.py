@@ -123,3 +123,47 @@ def assert_nucleus_close(pol_gpu, pol_want, infos, tol=TOL, what=""):
                                 f"alternatives {info.alternatives if info.ambiguous else []}")
     assert n_alt_only <= n_amb
     return n_amb, n_alt_only
+
+
+# The nucleus entry point's window of BF16 classes: magnitudes [2^-24, 65536)
+# of either sign, +-0, and -inf counted apart.
+WINDOW_MAG_LO = 0x3380
+WINDOW_N_MAG = 5120
+SEARCH_ARG_LIMIT = 2.0 ** 20
+
+
+def exact_reference_rows(logits, vocab_real, temps, top_p, top_k, targets):
+    """Rows whose rlk_logp_nucleus reference comes from the exact integer class
+    masses of the support search rather than from the float32 shard sums: rows
+    that need a search (T > 0 finite, top-p in (0, 1], top-k -1 or 1..V, and
+    top-p < 1 or top-k < V), whose real tokens all lie in the window or are
+    -inf, with a target among the real columns, at least one finite token and
+    |fl32(M * c)| < 2^20 for the row maximum M and c = fl32(log2(e) / T). The
+    other rows' reference bytes equal rlk_logp_full's."""
+    n = logits.shape[0]
+    out = np.zeros(n, dtype=bool)
+    log2e = np.float32(1.44269504088896340736)
+    for lo in range(0, n, 256):
+        hi = min(n, lo + 256)
+        b = logits[lo:hi, :vocab_real]
+        mag = b & 0x7FFF
+        inw = ((mag >= WINDOW_MAG_LO) & (mag < WINDOW_MAG_LO + WINDOW_N_MAG)) | (mag == 0) | (b == 0xFF80)
+        finite = b != 0xFF80
+        for j, i in enumerate(range(lo, hi)):
+            t = np.float32(temps[i])
+            p = np.float32(top_p[i])
+            k = int(top_k[i])
+            tg = int(targets[i])
+            if not (np.isfinite(t) and t > 0):
+                continue
+            if not (0 < p <= 1) or not (k == -1 or 1 <= k <= vocab_real):
+                continue
+            if not ((k != -1 and k < vocab_real) or p < 1):
+                continue
+            if not (0 <= tg < vocab_real) or not inw[j].all() or not finite[j].any():
+                continue
+            x = (b[j][finite[j]].astype(np.uint32) << 16).view(np.float32)
+            c = np.float32(log2e / t)
+            if abs(float(np.float32(x.max() * c))) < SEARCH_ARG_LIMIT:
+                out[i] = True
+    return out

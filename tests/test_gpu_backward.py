@@ -24,7 +24,7 @@ import datagen
 import invariant_token_log_fp32_amd as rlk
 from oracle import logp as O
 
-from gpu_util import assert_close, row_tolerance, say, to_host, upload, upload_logits
+from gpu_util import assert_close, exact_reference_rows, row_tolerance, say, to_host, upload, upload_logits
 
 pytestmark = pytest.mark.gpu
 
@@ -87,15 +87,22 @@ def compare_row(got_bits, want, tol, what):
     return int(exact[fin].sum()), int(fin.sum())
 
 
-def run_forward(lg, t, p, k, tg, vr, vp=None, groups=1):
-    """GPU forward (nucleus with its support record, and the full path's lse)."""
+def run_forward(lg, t, p, k, tg, vr, vp=None, groups=1, host_logits=None):
+    """GPU forward (nucleus with its support record). Its reference and lse
+    equal rlk_logp_full's bytes on the rows that take the float32 shard sums,
+    and lie within the tolerance of them on the rows that take the exact
+    class masses."""
     import torch
     pol, ref, lse, state = rlk.logp_nucleus(lg, t, p, k, tg, vocab_real=vr, vocab_padded=vp, groups=groups,
                                             return_state=True)
     full, full_lse = rlk.logp_full(lg, t, tg, vocab_real=vr, vocab_padded=vp, groups=groups, return_lse=True)
     torch.cuda.synchronize()
-    assert to_host(ref).tobytes() == to_host(full).tobytes()
-    assert to_host(lse).tobytes() == to_host(full_lse).tobytes()
+    logits = host_logits if host_logits is not None else to_host(lg).view(np.uint16)
+    exact = exact_reference_rows(logits, vr, to_host(t), to_host(p), to_host(k), to_host(tg))
+    for a, b in ((ref, full), (lse, full_lse)):
+        a, b = to_host(a), to_host(b)
+        assert a[~exact].tobytes() == b[~exact].tobytes()
+        assert_close(a[exact], b[exact], tol=row_tolerance(logits[exact], vr, to_host(t)[exact]), what="exact-mass reference")
     return pol, ref, lse, state
 
 
@@ -264,7 +271,7 @@ def test_full_size_sampled_and_batch_invariant():
     k = upload(w.top_k, torch.int32)
     tg = upload(targets, torch.int64)
     say("case: full-size forward + backward")
-    pol, ref, lse, state = run_forward(lg, t, p, k, tg, vr)
+    pol, ref, lse, state = run_forward(lg, t, p, k, tg, vr, host_logits=logits)
     kw = dict(vocab_real=vr, ref_logp=ref, lse=lse, grad_ref=upload(gr, torch.float32), policy_logp=pol,
               support_state=state, grad_policy=upload(gp, torch.float32))
     out = rlk.logp_backward(lg, t, tg, **kw)
@@ -319,7 +326,7 @@ def test_support_record_matches_oracle_and_groups():
     first = None
     for groups in (1, 2, 4, 8):
         say(f"case: support record, groups {groups}")
-        _, _, _, state = run_forward(lg, *args, w.vocab_real, groups=groups)
+        _, _, _, state = run_forward(lg, *args, w.vocab_real, groups=groups, host_logits=logits)
         b = to_host(state).tobytes()
         first = first or b
         assert b == first, f"support record bytes differ at groups {groups}"

@@ -21,7 +21,8 @@ import datagen
 import invariant_token_log_fp32_amd as rlk
 from oracle import logp as O
 
-from gpu_util import TOL, assert_close, assert_nucleus_close, report, row_tolerance, say, to_host, upload, upload_logits
+from gpu_util import (TOL, assert_close, assert_nucleus_close, exact_reference_rows, report, row_tolerance, say,
+                      to_host, upload, upload_logits)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,14 +41,31 @@ def run_nucleus(logits_np, vr, temps, top_p, top_k, targets, groups=1, vp=None):
     return to_host(pol), to_host(ref), to_host(full)
 
 
+def check_ref_against_full(ref, full, logits, vr, temps, top_p, top_k, targets, tol, what):
+    """The nucleus reference against rlk_logp_full's on every row: the same
+    bytes where both come from the float32 shard sums, within the tolerance
+    where the nucleus reference comes from the exact class masses."""
+    exact = exact_reference_rows(logits, vr, temps, top_p, top_k, targets)
+    assert ref[~exact].tobytes() == full[~exact].tobytes(), f"{what}: float32-reference rows differ from rlk_logp_full"
+    tol = np.broadcast_to(np.asarray(tol, dtype=np.float64), ref.shape)
+    err = assert_close(ref[exact], full[exact], tol=tol[exact], what=f"{what}: exact-mass reference vs rlk_logp_full")
+    report(f"{what}: {int(exact.sum())} exact-mass reference rows, largest |ref - full| {err:.2e}")
+
+
 def check(logits, vr, temps, top_p, top_k, targets, what, vp=None, groups_list=GROUPS, extra_tol=0.0):
     want_pol, want_ref, infos = O.nucleus_logp(logits, vr, temps, top_p, top_k, targets)
     tol = row_tolerance(logits, vr, temps) + extra_tol
+    float_ref = ~exact_reference_rows(logits, vr, temps, top_p, top_k, targets)
     first = None
+    first_ref = None
     for groups in groups_list:
         pol, ref, full = run_nucleus(logits, vr, temps, top_p, top_k, targets, groups, vp)
-        assert ref.tobytes() == full.tobytes(), f"{what}: reference bytes differ from rlk_logp_full"
+        assert ref[float_ref].tobytes() == full[float_ref].tobytes(), \
+            f"{what}: reference bytes of the float32-reference rows differ from rlk_logp_full"
         assert_close(ref, want_ref, tol=tol, what=f"{what} ref g{groups}")
+        if first_ref is None:
+            first_ref = ref.tobytes()
+        assert ref.tobytes() == first_ref, f"{what}: reference bytes differ between groups"
         n_amb, n_alt = assert_nucleus_close(pol, want_pol, infos, tol=tol, what=f"{what} policy g{groups}")
         if n_amb:
             report(f"{what} g{groups}: {n_amb} rows in the ambiguity band, {n_alt} matched a neighbouring cut")
@@ -135,13 +153,12 @@ def test_tied_classes_without_zero():
     check(logits, vr, temps, top_p, top_k, targets, "ties without zero")
 
 
-def test_top_p_near_one_and_bracket_edges():
-    """Top-p values just below 1 (the upper end of the bracket the kernel puts
-    around a row's total mass can exceed the total, so the exact total must be
-    summed), a tiny top-p (the argmax class) and mid values, with top-k off, on
-    rows of 8 shards of 2400 columns (several 512-slot scan rounds) and the
+def test_top_p_near_one_and_edges():
+    """Top-p values just below 1 (the threshold ceil(p * Z) then lies within a
+    few tokens' mass of the total), a tiny top-p (the argmax class) and mid
+    values, with top-k off, on rows of 8 shards of 2400 columns and the
     benchmark's value distribution, with and without a spike."""
-    say("case: top-p near 1 and bracket edges")
+    say("case: top-p near 1 and edges")
     vp, vr = 19200, 19137
     n = 48
     rng = np.random.default_rng(71)
@@ -166,9 +183,9 @@ def test_deep_top_p_scans():
     that the top-p crossing lies many 256-class steps below the maximum: the
     values are +-2^U(-24, 3) (a few zeros in every other row), at temperatures
     2 and 8 where the masses of all tokens are within a small factor of each
-    other. The p grid puts the crossing in many different steps (and at each
-    position of a four-step batch of the scan's skip-ahead), with top-k off and
-    on (k = 12000, so the top-p threshold comes from the exact top-k mass)."""
+    other. The p grid puts the crossing in many different steps, with top-k off
+    and on (k = 12000, so the top-p threshold comes from the exact top-k
+    mass)."""
     say("case: deep top-p scans")
     vp, vr = 19200, 19137
     p_grid = np.array([0.05, 0.2, 0.35, 0.5, 0.65, 0.8, 0.95, 0.999], dtype=np.float32)
@@ -427,8 +444,8 @@ def test_full_size_nucleus_sampled(qwen_logits):
     """8192 x 152576, T = 0.7, top-p 0.95, top-k off, in the benchmark's launch
     configuration: 40 sampled rows and every row holding a zero (the window's
     zero class) or a token outside the window (the general path) get targets
-    from their oracle nucleus; reference bytes equal rlk_logp_full's. No
-    sampled row may match only a neighbouring top-p cut."""
+    from their oracle nucleus; every row's reference is checked against
+    rlk_logp_full's. No sampled row may match only a neighbouring top-p cut."""
     w, logits, targets = qwen_logits
     rows = np.random.default_rng(3003).choice(w.n_rows, 40, replace=False)
     gen = general_path_rows(logits, w.vocab_real, zeros=True)
@@ -440,7 +457,8 @@ def test_full_size_nucleus_sampled(qwen_logits):
     tg[sel] = support_targets(logits[sel], w.vocab_real, w.temperature[sel], w.top_p[sel], w.top_k[sel], 3003)
     say("case: nucleus full size, groups 1")
     pol, ref, full = run_nucleus(logits, w.vocab_real, w.temperature, w.top_p, w.top_k, tg)
-    assert ref.tobytes() == full.tobytes()
+    check_ref_against_full(ref, full, logits, w.vocab_real, w.temperature, w.top_p, w.top_k, tg, TOL,
+                           "nucleus full")
     assert np.isfinite(pol[sel]).all()
     _, n_alt = compare_rows(logits, w, tg, pol, ref, rows, "nucleus full, sampled rows")
     assert n_alt == 0
@@ -467,7 +485,8 @@ def test_per_request_sampled():
     for groups in (1, 4):
         say(f"case: per-request groups {groups}")
         pol, ref, full = run_nucleus(logits, w.vocab_real, w.temperature, w.top_p, w.top_k, tg, groups)
-        assert ref.tobytes() == full.tobytes()
+        check_ref_against_full(ref, full, logits, w.vocab_real, w.temperature, w.top_p, w.top_k, tg, TOL,
+                               f"per-request g{groups}")
         compare_rows(logits, w, tg, pol, ref, np.unique(rows), f"per-request g{groups}, sampled rows")
         compare_rows(logits, w, tg, pol, ref, gen, f"per-request g{groups}, rows with a zero or an outside token")
 
