@@ -72,7 +72,8 @@ constexpr uint32_t kNegInfBits = 0xFF80u;
 // |fl32(M*c)| < 2^20. Then fl32(M*c) is within 2^-5 of M*c, so no token's
 // weight exceeds 2^(2^-5) * 2^40 and, with fewer than 2^24 - 2^20 real tokens
 // (the entry points' limit), a row's total mass stays below 2^64. A row beyond
-// it gets no support (policy NaN, status -1); its reference is unaffected.
+// it gets no support (policy NaN, status -1); its reference comes from the
+// float32 shard sums.
 constexpr float kMaxSupportArg = 0x1p20f;
 
 typedef unsigned long long u64;
