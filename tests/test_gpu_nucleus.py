@@ -385,6 +385,15 @@ def test_special_rows():
     add(0.7, 0.9, -1, 3, row=np.full(vr, datagen.f32_to_bf16_bits(np.float32([1.0]))[0], np.uint16))  # all equal
     add(float("nan"), 0.9, 5, 3)
     add(0.7, 0.9, 5, -4)
+    add(0.7, 0.9, -1, vr)                    # target past the real columns
+    # rows a search would take whose reference cannot come from the window's masses: no finite
+    # token, a NaN or a +inf logit (both outputs NaN), a huge finite logit (general path)
+    add(0.7, 0.9, -1, 3, row=np.full(vr, datagen.BF16_NEG_INF, np.uint16))
+    for bad in (datagen.BF16_NAN, datagen.BF16_POS_INF, datagen.f32_to_bf16_bits(np.float32([70000.0]))[0]):
+        r = base.copy()
+        r[17] = bad
+        add(0.7, 0.9, -1, 3, row=r)
+        add(1.3, 0.95, 128, 17, row=r)
     logits = np.stack(rows)
     check(logits, vr, np.array(T, np.float32), np.array(P, np.float32), np.array(K, np.int32),
           np.array(TG, np.int64), "special")
