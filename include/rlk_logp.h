@@ -138,7 +138,7 @@ typedef struct rlk_support_state {
  *   ref_out[i]    = z_t - lse, the full-vocabulary logprob. For a row that
  *                   needs a support search (top_p < 1 or top_k < vocab_real,
  *                   T > 0) whose real tokens all lie in the search's window
- *                   (BF16 magnitudes in [2^-24, 65536), +-0, or -inf), with its
+ *                   (BF16 magnitudes in [2^-24, 4096), +-0, or -inf), with its
  *                   target among the real columns and its maximum in the
  *                   search's range (below), lse comes from the same exact
  *                   integer class masses as the policy: lse = (R +

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void k_merge(const ShardSummary* __restrict__ 
 // ----------------------------------------------------------------------------
 // Support path (top-k then top-p): see support.hpp.
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(6, 6))) void k_nucleus_g1(
+__global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_nucleus_g1(
     const uint16_t* __restrict__ logits, int64_t row_stride, int shard_width, int64_t vocab_real,
     const float* __restrict__ temperature, const float* __restrict__ top_p, const int32_t* __restrict__ top_k,
     const int64_t* __restrict__ target, float* __restrict__ policy_out, float* __restrict__ ref_out,

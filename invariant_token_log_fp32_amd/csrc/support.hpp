@@ -18,7 +18,7 @@
 // "cumulative >= p * Z" is evaluated exactly as cumulative >= ceil(p * Z).
 //
 // Exact path: every token is counted (LDS u32 atomics) in a window of classes:
-// the BF16 values of magnitude in [2^-24, 65536) of either sign, interleaved
+// the BF16 values of magnitude in [2^-24, 4096) of either sign, interleaved
 // by magnitude (slot 2*(m - m_lo) + sign, m the 15-bit magnitude pattern),
 // plus one class for +-0; -inf tokens are counted apart (mass 0). The slots of
 // two tokens come from three packed 16-bit instructions, and one maximum over
@@ -37,8 +37,8 @@
 // beyond the search's range, takes its reference from the float32 shard sums
 // instead (a second pass over the row when the first one only counted).
 // General path, for rows with a token outside the window (a nonzero value of
-// magnitude below 2^-24, or 65536 and beyond): an exact-maximum pass, then a
-// 4096-bin histogram of (count, mass) over key >> 4, then the 16 keys of each
+// magnitude below 2^-24, or 4096 and beyond): an exact-maximum pass, then a
+// 2048-bin histogram of (count, mass) over key >> 5, then the 32 keys of each
 // boundary bin, each from another pass over the row. Both paths produce the
 // same integers and therefore the same support and policy bytes.
 #pragma once
@@ -50,13 +50,17 @@ namespace rlk {
 
 constexpr int kNucThreads = 512;
 constexpr int kNucWaves = kNucThreads / kWave;
-constexpr int kBinsA = 4096;
-constexpr int kSub = 16;
-// The window: magnitudes kMagLo .. kMagLo + kNMag - 1 (2^-24 <= |x| < 65536)
-// of both signs, interleaved, then the zero class. 40 KB of counts: three rows
+constexpr int kBinsA = 2048;  // general path: level-A bins of key16 >> kSubBits
+constexpr int kSubBits = 5;
+constexpr int kSub = 1 << kSubBits;  // keys per level-A bin
+constexpr int kPerLane = kBinsA / kWave;  // level-A bins per lane of the one-wave scan
+static_assert(kPerLane * kWave == kBinsA && kPerLane <= kWave && (kPerLane & (kPerLane - 1)) == 0,
+              "the scan's lane blocks are whole powers of two");
+// The window: magnitudes kMagLo .. kMagLo + kNMag - 1 (2^-24 <= |x| < 4096)
+// of both signs, interleaved, then the zero class. 36 KB of counts: four rows
 // per CU with the general path's histogram in the same LDS.
 constexpr uint32_t kMagLo = 0x3380u;               // magnitude pattern of 2^-24
-constexpr int kNMag = 5120;                        // 40 binades of 128 BF16 values
+constexpr int kNMag = 4608;                        // 36 binades of 128 BF16 values
 constexpr int kWin = 2 * kNMag;                    // interleaved slots
 constexpr int kZeroSlot = kWin;                    // the +-0 class
 constexpr int kWinWords = kWin + 2;                // + zero slot + pad (64-bit clearing)
@@ -92,7 +96,7 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 
 // Window slot of a BF16 pattern: 2 * (m - kMagLo) + sign for magnitudes in the
 // window, kZeroSlot for +-0, kSlotOut for everything else (-inf, NaN, +-inf,
-// nonzero magnitudes below 2^-24, magnitudes of 65536 and beyond).
+// nonzero magnitudes below 2^-24, magnitudes of 4096 and beyond).
 __device__ __forceinline__ uint32_t window_slot(uint32_t b) {
   const uint32_t m = b & 0x7FFFu;
   if (m == 0u) return static_cast<uint32_t>(kZeroSlot);
@@ -199,10 +203,10 @@ struct NucGeneral {
   u64 sub_mass[kSub];
 };
 
-// Classes are visited in steps of 256 ranks: the positive slots in 20 steps,
-// the zero class alone, the negative slots in 20 steps.
+// Classes are visited in steps of 256 ranks: the positive slots in 18 steps,
+// the zero class alone, the negative slots in 18 steps.
 constexpr int kStepRanks = 4 * kWave;           // 256 ranks per step
-constexpr int kPosSteps = kNMag / kStepRanks;   // 20
+constexpr int kPosSteps = kNMag / kStepRanks;   // 18
 constexpr int kZeroStep = kPosSteps;
 constexpr int kSteps = 2 * kPosSteps + 1;
 static_assert(kNMag % kStepRanks == 0, "steps cover whole magnitude ranges");
@@ -221,6 +225,7 @@ struct NucLds {
   // block reductions
   uint32_t red_u32[kNucWaves][2];
   int red_flag[kNucWaves];
+  int top_w[kNucWaves];  // the row-maximum scan: first non-empty rank per wavefront
   // general path results
   int jk;            // key of the top-k boundary inside bin bk
   int kappa;         // smallest kept key
@@ -335,7 +340,8 @@ __device__ __forceinline__ uint32_t slots_outside(const uint32_t (&sl)[4]) {
       "v_pk_max_u16 %[e], %[e0], %[e1]\n\t"
       "v_pk_sub_u16 %[out], %[e], %[top] clamp"
       : [e0] "=&v"(e0), [e1] "=&v"(e1), [e] "=&v"(e), [out] "=&v"(out)
-      : [s0] "v"(sl[0]), [s1] "v"(sl[1]), [s2] "v"(sl[2]), [s3] "v"(sl[3]), [top] "v"(0x27FF27FFu));
+      : [s0] "v"(sl[0]), [s1] "v"(sl[1]), [s2] "v"(sl[2]), [s3] "v"(sl[3]),
+        [top] "v"(static_cast<uint32_t>(kWin - 1) * 0x10001u));
   return out;
 }
 
@@ -501,7 +507,7 @@ __device__ __forceinline__ int wave_min(int v) {
 // maximum M is the first non-empty class, R = ceil(fl32(M*c)), and a class
 // weighs count * floor(2^(x*c - R) * 2^40): exactly the integers the general
 // path sums per token. The classes are visited in steps of 256 ranks: the
-// positive slots in 20 steps, the zero class alone, the negative slots in 20
+// positive slots in 18 steps, the zero class alone, the negative slots in 18
 // steps. In a step lane l holds ranks 4l .. 4l+3 (two 16-byte LDS reads cover
 // the 8 interleaved slots of its 4 magnitudes). The wavefronts sum the count
 // and the mass of every step from the maximum's on in parallel; one barrier;
@@ -629,40 +635,55 @@ __device__ __forceinline__ void step_round(const NucLds& L, int s, float c, floa
   }
 }
 
-constexpr int kBatch = 4;  // steps whose LDS reads the row-maximum scan issues together
+constexpr int kBatch = 4;  // steps per wavefront in the row-maximum scan
+static_assert(kBatch * kNucWaves <= kSteps, "the parallel scan covers whole batches of the window");
 
-// Rank of the first non-empty class (the row maximum), kNoRank when the
-// window is empty (wave-uniform). The LDS reads of kBatch steps are issued
-// together and one wave minimum finds the first non-empty class.
-__device__ __forceinline__ int window_top_rank(const NucLds& L, int lane) {
-  for (int s0 = 0; s0 < kSteps; s0 += kBatch) {
-    uint32_t cn[kBatch][4];
+// First non-empty class among steps s0 .. s0 + kBatch - 1 (steps past the
+// window count as empty), kNoRank when they are all empty (wave-uniform). The
+// LDS reads of the kBatch steps are issued together; one wave minimum.
+__device__ __forceinline__ int batch_top_rank(const NucLds& L, int s0, int lane) {
+  uint32_t cn[kBatch][4];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      if (s0 + b < kSteps) {
-        step_counts(L, s0 + b, lane, cn[b]);
-      } else {
+  for (int b = 0; b < kBatch; ++b) {
+    if (s0 + b < kSteps) {
+      step_counts(L, s0 + b, lane, cn[b]);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) cn[b][e] = 0u;
-      }
-    }
-    int hit = -1;  // first step of the batch with a token (wave-uniform)
-#pragma unroll
-    for (int b = kBatch - 1; b >= 0; --b)
-      if (__ballot((cn[b][0] | cn[b][1] | cn[b][2] | cn[b][3]) != 0u)) hit = b;
-    if (hit >= 0) {
-      int j = kNoRank;
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b)
-        if (b == hit) {
-#pragma unroll
-          for (int e = 3; e >= 0; --e)
-            if (cn[b][e]) j = step_rank(s0 + b, lane, e);
-        }
-      return wave_min(j);
+      for (int e = 0; e < 4; ++e) cn[b][e] = 0u;
     }
   }
-  return kNoRank;
+  int hit = -1;  // first step of the batch with a token (wave-uniform)
+#pragma unroll
+  for (int b = kBatch - 1; b >= 0; --b)
+    if (__ballot((cn[b][0] | cn[b][1] | cn[b][2] | cn[b][3]) != 0u)) hit = b;
+  if (hit < 0) return kNoRank;
+  int j = kNoRank;
+#pragma unroll
+  for (int b = 0; b < kBatch; ++b)
+    if (b == hit) {
+#pragma unroll
+      for (int e = 3; e >= 0; --e)
+        if (cn[b][e]) j = step_rank(s0 + b, lane, e);
+    }
+  return wave_min(j);
+}
+
+// Rank of the first non-empty class (the row maximum), kNoRank when the
+// window is empty; the same in every thread. Called by the whole block (one
+// barrier): wavefront w scans steps kBatch*w .. kBatch*w + kBatch - 1 and the
+// minimum over the wavefronts is the answer, so where the maximum lies in the
+// window does not lengthen the scan. Only when those steps are all empty (every
+// token negative with a magnitude in the last steps) are the remaining steps
+// scanned in order.
+__device__ __forceinline__ int window_top_rank(NucLds& L, int lane, int wave) {
+  const int jw = batch_top_rank(L, kBatch * wave, lane);
+  if (lane == 0) L.top_w[wave] = jw;
+  __syncthreads();
+  int j = kNoRank;
+#pragma unroll
+  for (int w = 0; w < kNucWaves; ++w) j = min(j, L.top_w[w]);
+  for (int s0 = kBatch * kNucWaves; j == kNoRank && s0 < kSteps; s0 += kBatch) j = batch_top_rank(L, s0, lane);
+  return j;
 }
 
 // Count and mass of one step, summed over the wave (wave-uniform). The
@@ -693,7 +714,7 @@ __device__ __forceinline__ void step_total(const NucLds& L, int s, int s_end, in
 // General path (any row whose thresholds are not resolved by the fast path).
 // ---------------------------------------------------------------------------
 
-// Wave 0: scan level-A bins from the top (4095 down to 0) for the first bin
+// Wave 0: scan level-A bins from the top (kBinsA - 1 down to 0) for the first bin
 // where the inclusive cumulative count (by_mass = 0) or mass (by_mass = 1)
 // reaches `thresh`. Bins above L.bk count fully, bin L.bk counts (L.rc, L.rm),
 // bins below L.bk count zero (when L.bk >= 0).
@@ -712,11 +733,12 @@ __device__ __forceinline__ void general_scan(NucLds& L, bool by_mass, u64 thresh
       mm = 0;
     }
   };
-  const int hi = kBinsA - 1 - kWave * lane;
+  const int hi = kBinsA - 1 - kPerLane * lane;
   uint32_t tc = 0;
   u64 tm = 0;
-  for (int i = 0; i < kWave; ++i) {
-    const int b = hi - ((i + lane) & (kWave - 1));  // rotated to spread LDS banks
+#pragma unroll 1
+  for (int i = 0; i < kPerLane; ++i) {
+    const int b = hi - ((i + lane) & (kPerLane - 1));  // rotated to spread LDS banks
     uint32_t cc;
     u64 mm;
     val(b, cc, mm);
@@ -730,15 +752,16 @@ __device__ __forceinline__ void general_scan(NucLds& L, bool by_mass, u64 thresh
   const int Ln = ball ? __ffsll(static_cast<long long>(ball)) - 1 : kWave - 1;
   const uint32_t ec = __shfl(ic - tc, Ln, kWave);
   const u64 em = __shfl(im - tm, Ln, kWave);
-  const int b = kBinsA - 1 - kWave * Ln - lane;
-  uint32_t cc;
-  u64 mm;
-  val(b, cc, mm);
+  // the kPerLane bins of lane Ln's block, one per lane (the other lanes hold none)
+  const int b = kBinsA - 1 - kPerLane * Ln - (lane < kPerLane ? lane : kPerLane - 1);
+  uint32_t cc = 0;
+  u64 mm = 0;
+  if (lane < kPerLane) val(b, cc, mm);
   const uint32_t jc = wave_incl_scan<uint32_t>(cc, lane);
   const u64 jm = wave_incl_scan<u64>(mm, lane);
   const bool reach2 = by_mass ? (em + jm >= thresh) : (static_cast<u64>(ec + jc) >= thresh);
-  const u64 ball2 = __ballot(reach2);
-  const int J = ball2 ? __ffsll(static_cast<long long>(ball2)) - 1 : kWave - 1;
+  const u64 ball2 = __ballot(reach2 && lane < kPerLane);
+  const int J = ball2 ? __ffsll(static_cast<long long>(ball2)) - 1 : kPerLane - 1;
   if (lane == J) {
     L.scan_bin = b;
     L.scan_cnt_above = ec + jc - cc;
@@ -756,10 +779,10 @@ __device__ __forceinline__ void general_sub(NucLds& L, const uint16_t* __restric
   __syncthreads();
   row_pass(rowp, vocab_real, [&](uint32_t b) {
     const uint32_t key = key16(b);
-    if ((key >> 4) != bin) return;
-    atomicAdd(&L.u.gen.sub_cnt[key & 15u], 1u);
+    if ((key >> kSubBits) != bin) return;
+    atomicAdd(&L.u.gen.sub_cnt[key & (kSub - 1u)], 1u);
     const u64 q = weight(b, c, nr);
-    if (q) atomicAdd(&L.u.gen.sub_mass[key & 15u], q);
+    if (q) atomicAdd(&L.u.gen.sub_mass[key & (kSub - 1u)], q);
   });
   __syncthreads();
 }
@@ -792,7 +815,7 @@ __device__ __forceinline__ void support_general(NucLds& L, const uint16_t* __res
   }
   __syncthreads();
   row_pass(rowp, vocab_real, [&](uint32_t b) {
-    const uint32_t bin = key16(b) >> 4;
+    const uint32_t bin = key16(b) >> kSubBits;
     atomicAdd(&L.u.gen.cnt[bin], 1u);
     const u64 q = weight(b, c, nr);
     if (q) atomicAdd(&L.u.gen.mass[bin], q);
@@ -1008,8 +1031,8 @@ __device__ __forceinline__ bool exact_row(NucLds& L, int64_t row, int64_t vocab_
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const float c = kLog2e / t;  // IEEE float32 division
-  // every wavefront finds the row maximum from the same counts
-  const int jtop = window_top_rank(L, lane);
+  // the row maximum, the same in every wavefront
+  const int jtop = window_top_rank(L, lane, wave);
   if (jtop == kNoRank) return false;
   const float m = rank_value(jtop);
   if (!(fabsf(m * c) < kMaxSupportArg)) return false;

@@ -125,10 +125,10 @@ def assert_nucleus_close(pol_gpu, pol_want, infos, tol=TOL, what=""):
     return n_amb, n_alt_only
 
 
-# The nucleus entry point's window of BF16 classes: magnitudes [2^-24, 65536)
+# The nucleus entry point's window of BF16 classes: magnitudes [2^-24, 4096)
 # of either sign, +-0, and -inf counted apart.
 WINDOW_MAG_LO = 0x3380
-WINDOW_N_MAG = 5120
+WINDOW_N_MAG = 4608
 SEARCH_ARG_LIMIT = 2.0 ** 20
 
 

@@ -302,15 +302,15 @@ def test_row_maximum_beyond_the_search_range():
 
 
 # BF16 patterns at and just past the ends of the support window's value
-# ranges: the top (65535.x is the largest magnitude inside, 65536 and the next
+# ranges: the top (4080 is the largest magnitude inside, 4096 and the next
 # value outside, both signs), the smallest magnitudes (2^-24 inside, the next
 # smaller value outside, both signs), +-0 (a class of the window), large
 # negative values (-4.24e9 / -4.26e9 and -1.823e19 / -1.830e19, outside), and
 # values inside it around +-256.
 EDGE_BITS = [0x4380, 0x4381, 0xC37D, 0xC37E, 0x437E, 0x3380, 0x337F, 0xB380, 0xB37F,
-             0x477F, 0x4780, 0x4781, 0xC77F, 0xC780, 0x0000, 0x8000,
+             0x457F, 0x4580, 0x4581, 0xC57F, 0xC580, 0x0000, 0x8000,
              0xCF7D, 0xCF7E, 0xDF7D, 0xDF7E]
-OUTSIDE_WINDOW = {0x337F, 0xB37F, 0x4780, 0x4781, 0xC780, 0xCF7D, 0xCF7E, 0xDF7D, 0xDF7E}
+OUTSIDE_WINDOW = {0x337F, 0xB37F, 0x4580, 0x4581, 0xC580, 0xCF7D, 0xCF7E, 0xDF7D, 0xDF7E}
 
 
 def test_window_edge_values():
@@ -410,13 +410,13 @@ def qwen_logits():
 def general_path_rows(logits, vocab_real, chunk=512, zeros=False):
     """Rows that the kernel sends to its general path, found from the BF16 bits:
     a real token other than -inf and +-0 whose magnitude is below 2^-24 or at
-    least 65536 (NaN and +-inf included). With `zeros`, also the rows holding a
+    least 4096 (NaN and +-inf included). With `zeros`, also the rows holding a
     +-0, which the window's zero class takes."""
     out = []
     for r0 in range(0, logits.shape[0], chunk):
         b = logits[r0:r0 + chunk, :vocab_real]
         mag = b & np.uint16(0x7FFF)
-        outside = ((mag < np.uint16(0x3380)) | (mag >= np.uint16(0x4780))) & (mag != 0) & (b != np.uint16(0xFF80))
+        outside = ((mag < np.uint16(0x3380)) | (mag >= np.uint16(0x4580))) & (mag != 0) & (b != np.uint16(0xFF80))
         if zeros:
             outside |= mag == 0
         hit = outside.any(axis=1)
@@ -503,8 +503,8 @@ def test_per_request_sampled():
 def test_full_width_general_path_rows():
     """64 rows of 151936 real columns (benchmark's value distribution) with
     zeros, values below 2^-24 and, in some rows, a value below -4.24e9 injected:
-    every row takes the general path (exact-maximum pass, 4096-bin histogram of
-    counts and 64-bit masses, 16-key sub-passes, and its top-k branch), at
+    every row takes the general path (exact-maximum pass, 2048-bin histogram of
+    counts and 64-bit masses, 32-key sub-passes, and its top-k branch), at
     top-k 128 or off, top-p 0.95 or 0.99, T 0.7 or 1.3."""
     vp, vr = datagen.QWEN3_VOCAB_PADDED, datagen.QWEN3_VOCAB_REAL
     n = 64
@@ -537,13 +537,13 @@ def test_every_window_class_as_a_top_k_boundary():
     exactly the k-th largest value, for every class of the window in turn. A
     sample of rows is compared with the oracle as well."""
     import torch
-    mags = np.arange(0x3380, 0x4780, dtype=np.uint16)
+    mags = np.arange(0x3380, 0x4580, dtype=np.uint16)
     vals_bits = np.concatenate([mags, mags | np.uint16(0x8000), np.array([0x0000, 0x8000], np.uint16)])
     vals = datagen.bf16_bits_to_f32(vals_bits).astype(np.float64)
     order = np.argsort(-vals, kind="stable")
     sorted_vals = vals[order]
-    n_tok = len(vals_bits)                       # 10242 tokens, 10241 classes
-    vp = 10368                                   # multiple of 64
+    n_tok = len(vals_bits)                       # 9218 tokens, 9217 classes
+    vp = 9280                                    # multiple of 64
     ks = np.arange(1, n_tok + 1)                 # k = n_tok disables top-k (threshold -inf)
     n = len(ks)
     rng = np.random.default_rng(91)

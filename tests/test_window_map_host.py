@@ -1,14 +1,14 @@
 """Host check of the support window's slot arithmetic (no GPU).
 
 The nucleus kernel counts each BF16 token into a window of classes with
-magnitudes in [2^-24, 65536) of both signs, interleaved (slot
+magnitudes in [2^-24, 4096) of both signs, interleaved (slot
 2 * (m - 0x3380) + sign), plus a class for +-0. Two tokens packed in a 32-bit
 word get their slots from three packed 16-bit integer instructions (shift
 right by 15, multiply-add 2 * b + sign, subtract 2 * 0x3380); a slot below
-10240 means "in the window". This emulates those instructions' 16-bit
+9216 means "in the window". This emulates those instructions' 16-bit
 wrap-around arithmetic on all 65536 patterns and checks:
 - the packed result equals the scalar definition for every in-window pattern
-  and is 10240 or more for every pattern outside (zeros, tiny and huge
+  and is 9216 or more for every pattern outside (zeros, tiny and huge
   magnitudes, infinities, NaN), in both halves of a word;
 - visiting the slots in the kernel's rank order (positive slots from the top,
   the zero class, negative slots from the top) lists the in-window values in
@@ -22,7 +22,7 @@ import numpy as np
 import datagen
 
 MAG_LO = 0x3380
-N_MAG = 5120
+N_MAG = 4608
 WIN = 2 * N_MAG
 
 
@@ -76,5 +76,5 @@ def test_rank_order_is_value_order():
     assert len(ranks) == WIN + 1
     inside = [b for b in range(65536) if scalar_slot(b) not in (None, "zero")]
     assert sorted(inside) == sorted(b for b in ranks if b != 0)
-    assert vals[0] == 65280.0 and vals[-1] == -65280.0
+    assert vals[0] == 4080.0 and vals[-1] == -4080.0
     assert vals[N_MAG - 1] == 2.0 ** -24 and vals[N_MAG + 1] == -(2.0 ** -24)
