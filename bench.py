@@ -387,11 +387,12 @@ def main():
         modes = {}
         mism = 0
         for bs in (1, 7, nseq):
-            _, ms_s = time_calls(lambda i, bs=bs: spass(bs), 3, 1)
+            # 2 warm-up passes, then the median of 3 blocks of 4 passes (as the other secondary legs)
+            ms_s, blk_s = time_blocks(lambda i, bs=bs: spass(bs), 4, 2, 3)
             mism += int((pol_s.view(torch.int32) != base_s[0].view(torch.int32)).sum().item())
             mism += int((ref_s.view(torch.int32) != base_s[1].view(torch.int32)).sum().item())
             modes[f"batches of {bs} sequences"] = {"calls": (nseq + bs - 1) // bs, "ms_per_pass": ms_s,
-                                                   "tokens_per_s": wst.n_rows / (ms_s * 1e-3)}
+                                                   "ms_blocks": blk_s, "tokens_per_s": wst.n_rows / (ms_s * 1e-3)}
         ab_s = bytes_nucleus(wst.n_rows, wst.vocab_real)
         ms_one = modes[f"batches of {nseq} sequences"]["ms_per_pass"]
         sec.append({"workload": f"invariance stress: {nseq} ragged sequences ({wst.n_rows} rows) x 152576, "
