@@ -21,8 +21,8 @@ import datagen
 import invariant_token_log_fp32_amd as rlk
 from oracle import logp as O
 
-from gpu_util import (TOL, assert_close, assert_nucleus_close, exact_reference_rows, report, row_tolerance, say,
-                      to_host, upload, upload_logits)
+from gpu_util import (TOL, WINDOW_MAG_LO, WINDOW_N_MAG, assert_close, assert_nucleus_close, exact_reference_rows,
+                      report, row_tolerance, say, to_host, upload, upload_logits)
 
 pytestmark = pytest.mark.gpu
 
@@ -336,6 +336,52 @@ def test_window_edge_values():
     logits = np.stack(rows)
     check(logits, vr, np.array(T, np.float32), np.array(P, np.float32), np.array(K, np.int32),
           np.array(TG, np.int64), "window edges")
+
+
+def window_rank_bits(r):
+    """BF16 pattern of the window class at rank r in value order: positive
+    magnitudes from the largest down, then +-0, then negative magnitudes from
+    the smallest up."""
+    n = WINDOW_N_MAG
+    if r < n:
+        return WINDOW_MAG_LO + (n - 1 - r)
+    if r == n:
+        return 0
+    return 0x8000 | (WINDOW_MAG_LO + (r - n - 1))
+
+
+def test_row_maximum_in_every_step():
+    """Rows whose maximum is the first or the last class of each 256-class
+    step of the window (the kernel's row-maximum scan and step totals work in
+    these steps; the eight wavefronts scan the first 32 steps in parallel and a
+    row whose every token is at most -4 has its maximum in the steps scanned
+    after them), the other tokens drawn from the classes below the maximum,
+    ties of the maximum included; top-p 0.9 alone and top-p 0.95 with top-k 50."""
+    n_mag = WINDOW_N_MAG
+    last = 2 * n_mag
+    starts = [256 * s for s in range(n_mag // 256)] + [n_mag] + [n_mag + 1 + 256 * s for s in range(n_mag // 256)]
+    maxima = sorted({r for s0 in starts for r in (s0, s0 if s0 == n_mag else s0 + 255)})
+    assert maxima[-1] == last and len(maxima) == 4 * (n_mag // 256) + 1
+    vp, vr = 2048, 2000
+    rng = np.random.default_rng(77)
+    rows, T, P, K = [], [], [], []
+    for t, p, k in ((1.0, 0.9, -1), (0.7, 0.95, 50)):
+        for r in maxima:
+            ranks = rng.integers(r + 1, min(r + 1500, last) + 1, size=vr) if r < last else np.full(vr, r)
+            ranks[rng.choice(vr, 3, replace=False)] = r
+            row = np.full(vp, datagen.BF16_NEG_INF, dtype=np.uint16)
+            row[:vr] = np.array([window_rank_bits(int(q)) for q in ranks], dtype=np.uint16)
+            rows.append(row)
+            T.append(t)
+            P.append(p)
+            K.append(k)
+    logits = np.stack(rows)
+    temps, top_p, top_k = np.array(T, np.float32), np.array(P, np.float32), np.array(K, np.int32)
+    tg = support_targets(logits, vr, temps, top_p, top_k, 78)
+    tg[::5] = rng.integers(0, vr, size=len(tg[::5]))  # some targets outside the support
+    assert exact_reference_rows(logits, vr, temps, top_p, top_k, tg).all()
+    say(f"case: row maximum in every window step ({len(rows)} rows)")
+    check(logits, vr, temps, top_p, top_k, tg, "maximum in every step")
 
 
 def test_support_limited_rows_match_enumeration():
