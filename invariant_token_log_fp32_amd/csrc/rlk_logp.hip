@@ -10,18 +10,17 @@
 //                      groups > 1 and by rlk_logp_shard_summaries on a slice.
 //   k_merge            one thread per row: the same fixed-order merge over the
 //                      rank-major summaries (groups > 1, rlk_logp_merge).
-//   k_nucleus_g1       groups == 1 support path in one launch: a row that
-//                      needs a search is streamed once by the shard-waves,
-//                      which only count its tokens into an LDS window of BF16
-//                      classes; the eight waves then sum the exact integer
-//                      class masses step by step, and wave 0 takes the
-//                      reference logprob, the top-k/top-p support and the
-//                      policy logprob from them. Other rows stream the float32
-//                      shard summaries (a second pass for the rare searched
-//                      rows that cannot use the window).
-//   k_nucleus          groups > 1: the same per-row logic on the summaries
-//                      k_rank_summaries stored, after a pass that fills the
-//                      window.
+//   k_nucleus_g1       the support path: a row that needs a search is
+//                      streamed once by the shard-waves, which only count its
+//                      tokens into an LDS window of BF16 classes; the eight
+//                      waves then sum the exact integer class masses step by
+//                      step, and wave 0 takes the reference logprob, the
+//                      top-k/top-p support and the policy logprob from them
+//                      (a second pass for the float32 shard summaries on the
+//                      rare searched rows that cannot use the window). Rows
+//                      without a search stream the float32 shard summaries
+//                      (groups == 1) or read those k_rank_summaries stored
+//                      for them (groups > 1).
 //   k_backward         gradient of the reference and policy logprobs with
 //                      respect to the BF16 logits, from the forward's per-row
 //                      statistics; 1024-thread workgroups over (row, column
@@ -105,15 +104,20 @@ __global__ __launch_bounds__(kRowThreads) void k_full_g1(const uint16_t* __restr
 // whose slice of the row starts at base + (b % ranks_in_grid) * rank_col_step +
 // row * slice_stride and holds shards [rank * spr, rank * spr + spr) (spr =
 // 8 / groups = waves per workgroup). Writes out[((b % ranks_in_grid) * n_rows +
-// row) * spr + wave].
+// row) * spr + wave]. With the support parameters (top_p non-null), rows that
+// need a support search are skipped: the support kernel takes their
+// reference from the exact class masses, or streams their summaries itself.
 __global__ __launch_bounds__(kRowThreads) void k_rank_summaries(const uint16_t* __restrict__ base,
                                                                 int64_t slice_stride, int64_t rank_col_step,
                                                                 int rank0, int ranks_in_grid, int spr,
                                                                 int shard_width, int64_t vocab_real, int64_t n_rows,
                                                                 const float* __restrict__ temperature,
                                                                 const int64_t* __restrict__ target,
+                                                                const float* __restrict__ top_p,
+                                                                const int32_t* __restrict__ top_k,
                                                                 ShardSummary* __restrict__ out) {
   const int64_t row = blockIdx.x / ranks_in_grid;
+  if (top_p != nullptr && search_needed(temperature[row], top_p[row], top_k[row], vocab_real)) return;
   const int rr = static_cast<int>(blockIdx.x % ranks_in_grid);
   const int wave = static_cast<int>(threadIdx.x / kWave);
   const int shard = (rank0 + rr) * spr + wave;
@@ -151,14 +155,21 @@ __global__ __launch_bounds__(256) void k_merge(const ShardSummary* __restrict__ 
 // ----------------------------------------------------------------------------
 // Support path (top-k then top-p): see support.hpp.
 // ----------------------------------------------------------------------------
+// kStored == false (groups == 1): a row without a search streams its float32
+// shard summaries here. kStored == true (groups > 1): k_rank_summaries stored
+// them, split over `groups` workgroups per row, rank-major in ws (spr = 8 /
+// groups summaries per rank); a row with a search is handled the same way in
+// both, from one pass that counts its tokens.
+template <bool kStored>
 __global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_nucleus_g1(
     const uint16_t* __restrict__ logits, int64_t row_stride, int shard_width, int64_t vocab_real,
     const float* __restrict__ temperature, const float* __restrict__ top_p, const int32_t* __restrict__ top_k,
     const int64_t* __restrict__ target, float* __restrict__ policy_out, float* __restrict__ ref_out,
-    float* __restrict__ lse_out, rlk_support_state* __restrict__ state_out) {
+    float* __restrict__ lse_out, rlk_support_state* __restrict__ state_out, const ShardSummary* __restrict__ ws,
+    int64_t n_rows, int spr) {
   __shared__ NucLds L;
   const int64_t row = blockIdx.x;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform: offsets in SGPRs
   const int64_t col0 = static_cast<int64_t>(wave) * shard_width;
   const uint16_t* __restrict__ rowp = logits + row * row_stride;
   const float t = temperature[row];
@@ -167,9 +178,16 @@ __global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(8, 
   const int64_t tg = target[row];
   if (!search_needed(t, p, k, vocab_real)) {
     // the reference from the shard summaries; the policy is the reference or NaN
-    NoHookLate none;
-    const ShardSummary s = summarize_row_shard(rowp + col0, col0, shard_width, vocab_real, t, tg, none);
-    if ((threadIdx.x & (kWave - 1)) == 0) L.sm[wave] = s;
+    if constexpr (kStored) {
+      if (threadIdx.x < kShards) {
+        const int sh = threadIdx.x;
+        L.sm[sh] = ws[(static_cast<int64_t>(sh / spr) * n_rows + row) * spr + (sh % spr)];
+      }
+    } else {
+      NoHookLate none;
+      const ShardSummary s = summarize_row_shard(rowp + col0, col0, shard_width, vocab_real, t, tg, none);
+      if ((threadIdx.x & (kWave - 1)) == 0) L.sm[wave] = s;
+    }
     __syncthreads();
     if (wave == 0) unsearched_row(L, row, vocab_real, shard_width, t, p, k, tg, policy_out, ref_out, lse_out, state_out);
     return;
@@ -201,28 +219,7 @@ __global__ __launch_bounds__(kNucThreads) __attribute__((amdgpu_waves_per_eu(8, 
     if ((threadIdx.x & (kWave - 1)) == 0) L.sm[wave] = s;
   }
   __syncthreads();
-  nucleus_row(L, rowp, row, vocab_real, shard_width, t, p, k, tg, true, policy_out, ref_out, lse_out, state_out);
-}
-
-__global__ __launch_bounds__(kNucThreads) void k_nucleus(const uint16_t* __restrict__ logits, int64_t row_stride,
-                                                         int64_t n_rows, int spr, int shard_width, int64_t vocab_real,
-                                                         const float* __restrict__ temperature,
-                                                         const float* __restrict__ top_p,
-                                                         const int32_t* __restrict__ top_k,
-                                                         const int64_t* __restrict__ target,
-                                                         const ShardSummary* __restrict__ ws,
-                                                         float* __restrict__ policy_out, float* __restrict__ ref_out,
-                                                         float* __restrict__ lse_out,
-                                                         rlk_support_state* __restrict__ state_out) {
-  __shared__ NucLds L;
-  const int64_t row = blockIdx.x;
-  if (threadIdx.x < kShards) {
-    const int k = threadIdx.x;
-    L.sm[k] = ws[(static_cast<int64_t>(k / spr) * n_rows + row) * spr + (k % spr)];
-  }
-  __syncthreads();
-  nucleus_row(L, logits + row * row_stride, row, vocab_real, shard_width, temperature[row], top_p[row], top_k[row],
-              target[row], false, policy_out, ref_out, lse_out, state_out);
+  nucleus_row(L, rowp, row, vocab_real, shard_width, t, p, k, tg, policy_out, ref_out, lse_out, state_out);
 }
 
 // ----------------------------------------------------------------------------
@@ -360,16 +357,17 @@ static ShardSummary* scratch_on_current_device() {
   return static_cast<ShardSummary*>(g_scratch_ptr[dev]);
 }
 
-// groups > 1: every rank's summaries of the full rows, rank-major, into ws.
+// groups > 1: every rank's summaries of the full rows, rank-major, into ws
+// (with top_p / top_k: of the rows without a support search only).
 static int32_t launch_all_ranks(const uint16_t* logits, int64_t n_rows, const rlk_vocab_layout* L,
-                                const float* temperature, const int64_t* target, ShardSummary* ws,
-                                hipStream_t stream) {
+                                const float* temperature, const int64_t* target, const float* top_p,
+                                const int32_t* top_k, ShardSummary* ws, hipStream_t stream) {
   const int S = static_cast<int>(L->vocab_padded / kShards);
   const int G = L->groups;
   const int spr = kShards / G;
   k_rank_summaries<<<dim3(static_cast<unsigned>(n_rows * G)), dim3(spr * kWave), 0, stream>>>(
       logits, L->row_stride, static_cast<int64_t>(spr) * S, 0, G, spr, S, L->vocab_real, n_rows, temperature, target,
-      ws);
+      top_p, top_k, ws);
   return launched();
 }
 
@@ -425,7 +423,8 @@ int32_t rlk_logp_full(const uint16_t* logits, int64_t n_rows, const rlk_vocab_la
     return launched();
   }
   ShardSummary* ws = static_cast<ShardSummary*>(workspace);
-  if ((st = launch_all_ranks(logits, n_rows, layout, temperature, target, ws, stream)) != RLK_OK) return st;
+  if ((st = launch_all_ranks(logits, n_rows, layout, temperature, target, nullptr, nullptr, ws, stream)) != RLK_OK)
+    return st;
   const unsigned blocks = static_cast<unsigned>((n_rows + 255) / 256);
   k_merge<<<dim3(blocks), dim3(256), 0, stream>>>(ws, n_rows, kShards / G, S, layout->vocab_real, temperature, target,
                                                   logp_out, lse_out);
@@ -458,16 +457,17 @@ int32_t rlk_logp_nucleus(const uint16_t* logits, int64_t n_rows, const rlk_vocab
   const int S = static_cast<int>(layout->vocab_padded / kShards);
   const int G = layout->groups;
   if (G == 1) {
-    k_nucleus_g1<<<dim3(static_cast<unsigned>(n_rows)), dim3(kNucThreads), 0, stream>>>(
+    k_nucleus_g1<false><<<dim3(static_cast<unsigned>(n_rows)), dim3(kNucThreads), 0, stream>>>(
         logits, layout->row_stride, S, layout->vocab_real, temperature, top_p, top_k, target, policy_out, ref_out,
-        lse_out, support_out);
+        lse_out, support_out, nullptr, n_rows, kShards);
     return launched();
   }
   ShardSummary* ws = static_cast<ShardSummary*>(workspace);
-  if ((st = launch_all_ranks(logits, n_rows, layout, temperature, target, ws, stream)) != RLK_OK) return st;
-  k_nucleus<<<dim3(static_cast<unsigned>(n_rows)), dim3(kNucThreads), 0, stream>>>(
-      logits, layout->row_stride, n_rows, kShards / G, S, layout->vocab_real, temperature, top_p, top_k, target, ws,
-      policy_out, ref_out, lse_out, support_out);
+  if ((st = launch_all_ranks(logits, n_rows, layout, temperature, target, top_p, top_k, ws, stream)) != RLK_OK)
+    return st;
+  k_nucleus_g1<true><<<dim3(static_cast<unsigned>(n_rows)), dim3(kNucThreads), 0, stream>>>(
+      logits, layout->row_stride, S, layout->vocab_real, temperature, top_p, top_k, target, policy_out, ref_out,
+      lse_out, support_out, ws, n_rows, kShards / G);
   return launched();
 }
 
@@ -517,7 +517,7 @@ int32_t rlk_logp_shard_summaries(const uint16_t* logits_slice, int64_t n_rows, c
   if (summaries_bytes < summary_bytes_all(n_rows) / static_cast<size_t>(G)) return RLK_ERR_WORKSPACE;
   k_rank_summaries<<<dim3(static_cast<unsigned>(n_rows)), dim3(spr * kWave), 0, stream>>>(
       logits_slice, slice_stride, 0, rank, 1, spr, static_cast<int>(S), layout->vocab_real, n_rows, temperature,
-      target, static_cast<ShardSummary*>(summaries_out));
+      target, nullptr, nullptr, static_cast<ShardSummary*>(summaries_out));
   return launched();
 }
 

@@ -24,9 +24,9 @@
 // two tokens come from three packed 16-bit instructions, and one maximum over
 // a vector's eight slots tells whether all of them lie in the window. Classes
 // are visited in value order (positive slots from the largest magnitude down,
-// the zero class, negative slots from the smallest magnitude up). With
-// groups == 1 the shard-waves count while they stream the row, and that is
-// all they do with it; otherwise one pass builds the window. The row maximum
+// the zero class, negative slots from the smallest magnitude up). The
+// shard-waves count while they stream the row, and that is all they do with
+// it, whatever the number of physical groups. The row maximum
 // is the first non-empty class and class masses are count * weight. The eight
 // wavefronts sum the classes' counts and masses in steps of 256 classes in
 // parallel; from the step totals one wavefront has the exact total Z, finds
@@ -285,35 +285,6 @@ __device__ __forceinline__ void row_pass(const uint16_t* __restrict__ rowp, int6
   }
 }
 
-// As row_pass, but hands whole 16-byte vectors (4 words, 8 values in column
-// order) to fv; the partial tail vector's values go one by one to fe.
-template <typename FV, typename FE>
-__device__ __forceinline__ void row_pass_vec(const uint16_t* __restrict__ rowp, int64_t vocab_real, FV fv, FE fe) {
-  const u32x4* __restrict__ base = reinterpret_cast<const u32x4*>(rowp);
-  const int nvec = static_cast<int>(vocab_real >> 3);
-  const int tail = static_cast<int>(vocab_real & 7);
-  const int step = kNucThreads * kPassLoads;
-  const int nmain = (nvec / step) * step;
-  for (int v0 = threadIdx.x; v0 < nmain; v0 += step) {  // every load in range
-    u32x4 w[kPassLoads];
-#pragma unroll
-    for (int u = 0; u < kPassLoads; ++u) w[u] = base[v0 + u * kNucThreads];
-#pragma unroll
-    for (int u = 0; u < kPassLoads; ++u) {
-      const uint32_t ws4[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-      fv(ws4);
-    }
-  }
-  for (int v = nmain + threadIdx.x; v < nvec; v += kNucThreads) {
-    const u32x4 w = base[v];
-    const uint32_t ws4[4] = {w.x, w.y, w.z, w.w};
-    fv(ws4);
-  }
-  if (tail && threadIdx.x == 0) {
-    for (int e = 0; e < tail; ++e) fe(static_cast<uint32_t>(rowp[nvec * 8 + e]));
-  }
-}
-
 // Window slots of the two BF16 values packed in one 32-bit word (low half =
 // first value), on 16-bit integer lane pairs: the sign bit, then
 // 2 * b + sign (the product drops the sign bit, leaving 2 * m + sign), then
@@ -348,7 +319,6 @@ __device__ __forceinline__ uint32_t slots_outside(const uint32_t (&sl)[4]) {
 // Counts tokens into the window while a pass streams them. Per lane: the
 // number of -inf tokens and whether any other token fell outside the window.
 struct WindowHook {
-  static constexpr bool kLateWiden = true;
   uint32_t* win;
   uint32_t ninf;
   bool odd;
@@ -382,16 +352,6 @@ struct WindowHook {
     } else {  // rare: a zero, -inf or a value outside the window, taken one by one
 #pragma unroll
       for (int e = 0; e < 8; ++e) one((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
-    }
-  }
-
-  // v: one vector of 8 BF16 columns as loaded; x: their float32 widenings;
-  // nvalid of them are real (the first nvalid).
-  __device__ __forceinline__ void operator()(const u32x4& v, const float (&x)[8], int nvalid) {
-    if (nvalid == 8) {
-      full(v);
-    } else {
-      for (int e = 0; e < nvalid; ++e) one(__float_as_uint(x[e]) >> 16);
     }
   }
 
@@ -462,26 +422,6 @@ __device__ __forceinline__ void count_shard(const uint16_t* __restrict__ shard, 
 template <typename Lds>
 __device__ __forceinline__ void window_clear(Lds& L) {
   for (int i = threadIdx.x; i < kWinWords / 2; i += kNucThreads) L.u.win_pairs[i] = 0ull;
-}
-
-// One pass over the row that fills the window (when the streaming pass did not).
-__device__ __forceinline__ void window_pass(NucLds& L, const uint16_t* __restrict__ rowp, int64_t vocab_real) {
-  WindowHook hook(L.u.win);
-  row_pass_vec(rowp, vocab_real,
-               [&](const uint32_t (&ws4)[4]) {
-                 u32x4 v;
-                 v.x = ws4[0]; v.y = ws4[1]; v.z = ws4[2]; v.w = ws4[3];
-                 float x[8];
-                 unpack8(v, x);
-                 hook(v, x, 8);
-               },
-               [&](uint32_t b) {
-                 u32x4 v;
-                 v.x = b; v.y = 0u; v.z = 0u; v.w = 0u;
-                 const float x[8] = {__uint_as_float(b << 16), 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                 hook(v, x, 1);
-               });
-  hook.publish(L);
 }
 
 template <int Ctrl, int RowMask = 0xF>
@@ -1160,8 +1100,8 @@ __device__ __forceinline__ bool exact_row(NucLds& L, int64_t row, int64_t vocab_
 
 // ---------------------------------------------------------------------------
 // Whole-row driver for all threads of the block, from the row's 8 float32
-// shard summaries in L.sm; when `window_built` the window and the hook totals
-// are already filled. A row that needs a search and whose real tokens all lie
+// shard summaries in L.sm, the window and the count totals of the streaming
+// pass. A row that needs a search and whose real tokens all lie
 // in the window (or are -inf) takes the exact path; the other searched rows
 // take the float32 reference, with no support when the row maximum is beyond
 // the search's range, or with the general path's support when a token lies
@@ -1170,7 +1110,7 @@ __device__ __forceinline__ bool exact_row(NucLds& L, int64_t row, int64_t vocab_
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restrict__ rowp, int64_t row,
                                             int64_t vocab_real, int shard_width, float t, float p, int64_t k,
-                                            int64_t tg, bool window_built, float* __restrict__ policy_out,
+                                            int64_t tg, float* __restrict__ policy_out,
                                             float* __restrict__ ref_out, float* __restrict__ lse_out,
                                             rlk_support_state* __restrict__ state_out) {
   const int tid = threadIdx.x;
@@ -1197,12 +1137,6 @@ __device__ __forceinline__ void nucleus_row(NucLds& L, const uint16_t* __restric
   __syncthreads();
   if (!L.search) return;
 
-  if (!window_built) {
-    window_clear(L);
-    __syncthreads();
-    window_pass(L, rowp, vocab_real);
-    __syncthreads();
-  }
   bool odd = false;  // block-uniform: a real token outside the window
   for (int w = 0; w < kNucWaves; ++w) odd |= (L.red_flag[w] != 0);
   if (!odd) {
