@@ -957,12 +957,13 @@ __device__ __forceinline__ void unsearched_row(const NucLds& L, int64_t row, int
 
 // The reference and the policy of a row whose window is complete and holds
 // every real token or counts it as -inf, from the exact class masses. All
-// kNucWaves wavefronts call it. It returns false, block-uniformly and before
-// any barrier, when the row takes the float32 reference instead: a target
-// outside the real columns, no finite token, or a row maximum beyond the
-// search's range. Otherwise the wavefronts other than 0 return true after the
-// one barrier and wavefront 0 writes ref_out, lse_out, policy_out and
-// state_out for the row; bt is the target's BF16 pattern.
+// kNucWaves wavefronts call it. It returns false, block-uniformly, when the
+// row takes the float32 reference instead: a target outside the real columns
+// (before any barrier), no finite token or a row maximum beyond the search's
+// range (after the row-maximum scan's barrier). Otherwise the wavefronts other
+// than 0 return true after the step totals' barrier and wavefront 0 writes
+// ref_out, lse_out, policy_out and state_out for the row; bt is the target's
+// BF16 pattern.
 __device__ __forceinline__ bool exact_row(NucLds& L, int64_t row, int64_t vocab_real, float t, float p, int64_t k,
                                           int64_t tg, uint32_t bt, float* __restrict__ policy_out,
                                           float* __restrict__ ref_out, float* __restrict__ lse_out,
