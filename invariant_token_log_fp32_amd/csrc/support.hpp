@@ -26,12 +26,13 @@
 // are visited in value order (positive slots from the largest magnitude down,
 // the zero class, negative slots from the smallest magnitude up). The
 // shard-waves count while they stream the row, and that is all they do with
-// it, whatever the number of physical groups. The row maximum
-// is the first non-empty class and class masses are count * weight. The eight
-// wavefronts sum the classes' counts and masses in steps of 256 classes in
-// parallel; from the step totals one wavefront has the exact total Z, finds
-// the steps of the thresholds by prefix sums over the steps, and scans only
-// those steps class by class. The same exact total gives the row's reference
+// it, whatever the number of physical groups. The row maximum is the largest
+// raw pattern the count saw (a signed 16-bit maximum) when the row holds +0 or
+// a positive token, else the first non-empty class; class masses are count *
+// weight. The eight wavefronts sum the classes' counts and masses in steps
+// of 256 classes in parallel; from the step totals one wavefront has the exact
+// total Z, finds the steps of the thresholds by prefix sums over the steps,
+// and scans only those steps class by class. The same exact total gives the row's reference
 // logprob, so a searched row needs no float32 sums at all. A row without a
 // search, or whose tokens are not all in the window, or whose maximum is
 // beyond the search's range, takes its reference from the float32 shard sums
@@ -226,6 +227,7 @@ struct NucLds {
   uint32_t red_u32[kNucWaves][2];
   int red_flag[kNucWaves];
   int top_w[kNucWaves];  // the row-maximum scan: first non-empty rank per wavefront
+  int vmax_w[kNucWaves];  // per wavefront: its largest BF16 pattern read as a signed 16-bit number
   // general path results
   int jk;            // key of the top-k boundary inside bin bk
   int kappa;         // smallest kept key
@@ -302,6 +304,17 @@ __device__ __forceinline__ uint32_t window_slots2(uint32_t w) {
   return slot;
 }
 
+// Lane-wise signed 16-bit maximum of two packed pairs. Read as signed 16-bit
+// numbers, the BF16 patterns of +0 and the positive values order by value and
+// lie above every pattern with the sign bit set, so a running maximum of raw
+// patterns that is >= 0 is the pattern of the largest value (checked on the
+// host against the value order).
+__device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_i16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Nonzero unless all 8 slots of a vector (4 words of slot pairs) are below
 // kWin: the packed maximum of the 8, then a saturating subtraction of kWin - 1.
 __device__ __forceinline__ uint32_t slots_outside(const uint32_t (&sl)[4]) {
@@ -317,16 +330,19 @@ __device__ __forceinline__ uint32_t slots_outside(const uint32_t (&sl)[4]) {
 }
 
 // Counts tokens into the window while a pass streams them. Per lane: the
-// number of -inf tokens and whether any other token fell outside the window.
+// number of -inf tokens, whether any other token fell outside the window, and
+// the largest raw pattern as a signed 16-bit number (both halves of vmax).
 struct WindowHook {
   uint32_t* win;
   uint32_t ninf;
   bool odd;
+  uint32_t vmax;
 
-  __device__ __forceinline__ explicit WindowHook(uint32_t* w) : win(w), ninf(0), odd(false) {}
+  __device__ __forceinline__ explicit WindowHook(uint32_t* w) : win(w), ninf(0), odd(false), vmax(0x80008000u) {}
 
   // One token: its exact slot (zero class included), or the outside tally.
   __device__ __forceinline__ void one(uint32_t b) {
+    vmax = pk_max_i16(vmax, b * 0x10001u);
     const uint32_t slot = window_slot(b);
     if (slot != kSlotOut) {
       atomicAdd(&win[slot], 1u);
@@ -340,6 +356,7 @@ struct WindowHook {
   // A vector of 8 real columns as loaded (column 2i in the low half of word i).
   __device__ __forceinline__ void full(const u32x4& v) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    vmax = pk_max_i16(vmax, pk_max_i16(pk_max_i16(w[0], w[1]), pk_max_i16(w[2], w[3])));
     uint32_t slots[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) slots[i] = window_slots2(w[i]);
@@ -355,14 +372,20 @@ struct WindowHook {
     }
   }
 
-  // Per-wave totals into L.red_u32[wave][1] (-inf count) and L.red_flag[wave].
+  // Per-wave totals into L.red_u32[wave][1] (-inf count), L.red_flag[wave]
+  // and L.vmax_w[wave].
   template <typename Lds>
   __device__ __forceinline__ void publish(Lds& L) {
     const uint32_t n = wave_total(ninf);
     const bool any = __any(odd);
+    const int lo = static_cast<int16_t>(vmax & 0xFFFFu);
+    const int hi = static_cast<int16_t>(vmax >> 16);
+    int m = lo > hi ? lo : hi;
+    for (int d = kWave / 2; d >= 1; d >>= 1) m = max(m, __shfl_xor(m, d, kWave));
     if ((threadIdx.x & (kWave - 1)) == 0) {
       L.red_u32[threadIdx.x / kWave][1] = n;
       L.red_flag[threadIdx.x / kWave] = any;
+      L.vmax_w[threadIdx.x / kWave] = m;
     }
   }
 };
@@ -972,8 +995,20 @@ __device__ __forceinline__ bool exact_row(NucLds& L, int64_t row, int64_t vocab_
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const float c = kLog2e / t;  // IEEE float32 division
-  // the row maximum, the same in every wavefront
-  const int jtop = window_top_rank(L, lane, wave);
+  // the row maximum, the same in every wavefront: the count's largest pattern
+  // when the row holds +0 or a positive token (every token lies in the window
+  // here), else the first non-empty class of the scan
+  int vm = -32768;
+#pragma unroll
+  for (int w = 0; w < kNucWaves; ++w) vm = max(vm, L.vmax_w[w]);
+  int jtop;
+  if (vm > 0) {
+    jtop = kNMag - 1 - (vm - static_cast<int>(kMagLo));
+  } else if (vm == 0) {
+    jtop = kZeroRank;
+  } else {
+    jtop = window_top_rank(L, lane, wave);
+  }
   if (jtop == kNoRank) return false;
   const float m = rank_value(jtop);
   if (!(fabsf(m * c) < kMaxSupportArg)) return false;

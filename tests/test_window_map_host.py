@@ -78,3 +78,36 @@ def test_rank_order_is_value_order():
     assert sorted(inside) == sorted(b for b in ranks if b != 0)
     assert vals[0] == 4080.0 and vals[-1] == -4080.0
     assert vals[N_MAG - 1] == 2.0 ** -24 and vals[N_MAG + 1] == -(2.0 ** -24)
+
+
+def test_signed_16_bit_maximum_of_patterns_is_the_row_maximum():
+    """The count's row maximum: a signed 16-bit maximum over the raw BF16
+    patterns of a row whose tokens lie in the window, are +-0 or -inf. When it
+    is >= 0 (the row holds +0 or a positive token) it must be the pattern of
+    the row's largest value; when it is negative the kernel scans the window
+    instead. Checked on every window pattern as a row of one token beside a
+    random row, and on random rows that mix signs, zeros and -inf."""
+    rng = np.random.default_rng(5)
+    window = np.array([b for b in range(65536) if scalar_slot(b) not in (None,)], dtype=np.uint16)
+    pool = np.concatenate([window, np.array([0x0000, 0x8000, 0xFF80], np.uint16)])
+
+    def check(row):
+        m = int(row.view(np.int16).max())
+        vals = datagen.bf16_bits_to_f32(row).astype(np.float64)
+        if m >= 0:
+            want = float(vals.max())
+            got = float(datagen.bf16_bits_to_f32(np.array([m], np.uint16))[0])
+            assert got == want, (hex(m), got, want)
+        else:
+            assert vals.max() <= 0.0
+    base = rng.choice(pool, 64)
+    for b in pool:
+        row = base.copy()
+        row[int(rng.integers(0, 64))] = b
+        check(row)
+    for _ in range(2000):
+        n = int(rng.integers(1, 200))
+        row = rng.choice(pool, n)
+        if rng.random() < 0.3:
+            row = row[(row & 0x8000) != 0] if np.any((row & 0x8000) != 0) else row
+        check(row)
