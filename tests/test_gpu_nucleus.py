@@ -356,7 +356,8 @@ def test_row_maximum_in_every_step():
     these steps; the eight wavefronts scan the first 32 steps in parallel and a
     row whose every token is at most -4 has its maximum in the steps scanned
     after them), the other tokens drawn from the classes below the maximum,
-    ties of the maximum included; top-p 0.9 alone and top-p 0.95 with top-k 50."""
+    ties of the maximum included (in one row the zero class holds only -0);
+    top-p 0.9 alone and top-p 0.95 with top-k 50."""
     n_mag = WINDOW_N_MAG
     last = 2 * n_mag
     starts = [256 * s for s in range(n_mag // 256)] + [n_mag] + [n_mag + 1 + 256 * s for s in range(n_mag // 256)]
@@ -368,9 +369,12 @@ def test_row_maximum_in_every_step():
     for t, p, k in ((1.0, 0.9, -1), (0.7, 0.95, 50)):
         for r in maxima:
             ranks = rng.integers(r + 1, min(r + 1500, last) + 1, size=vr) if r < last else np.full(vr, r)
-            ranks[rng.choice(vr, 3, replace=False)] = r
+            top = rng.choice(vr, 3, replace=False)
+            ranks[top] = r
             row = np.full(vp, datagen.BF16_NEG_INF, dtype=np.uint16)
             row[:vr] = np.array([window_rank_bits(int(q)) for q in ranks], dtype=np.uint16)
+            if r == n_mag and k != -1:
+                row[top] = 0x8000  # the zero class as -0 only: the maximum is not a non-negative pattern
             rows.append(row)
             T.append(t)
             P.append(p)
