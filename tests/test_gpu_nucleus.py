@@ -550,6 +550,32 @@ def test_per_request_sampled():
         compare_rows(logits, w, tg, pol, ref, gen, f"per-request g{groups}, rows with a zero or an outside token")
 
 
+def test_full_width_rows_with_and_without_a_search_at_every_grouping():
+    """96 rows of 151936 real columns (the benchmark's value distribution) in
+    one call, a third without a support search (top-p 1 and top-k off, or
+    greedy), a third with top-p 0.95, a third with top-k 128 and top-p 0.99,
+    at groups 1, 2, 4 and 8: with groups > 1 the float32 summaries of the rows
+    without a search come from the grouped summary kernel and the searched rows
+    are counted in one pass, so every grouping must give the same bytes, the
+    rows without a search rlk_logp_full's reference bytes, and all rows the
+    oracle's values."""
+    vp, vr = datagen.QWEN3_VOCAB_PADDED, datagen.QWEN3_VOCAB_REAL
+    n = 96
+    rng = np.random.default_rng(4242)
+    logits = np.full((n, vp), datagen.BF16_NEG_INF, dtype=np.uint16)
+    for i in range(n):
+        bits, _, _ = datagen.row_values((4242, i), vr, 2.5, 8.0 if i % 5 == 0 else None)
+        logits[i, :vr] = bits
+    kind = np.arange(n) % 3
+    temps = np.where(kind == 0, np.where(np.arange(n) % 2 == 0, 0.7, 0.0), np.array([1.0, 0.7, 1.3])[np.arange(n) % 3])
+    temps = temps.astype(np.float32)
+    top_p = np.array([1.0, 0.95, 0.99], np.float32)[kind]
+    top_k = np.array([-1, -1, 128], np.int32)[kind]
+    tg = rng.integers(0, vr, size=n).astype(np.int64)
+    say("case: full-width rows with and without a search, groups 1/2/4/8")
+    check(logits, vr, temps, top_p, top_k, tg, "full width, mixed search")
+
+
 def test_full_width_general_path_rows():
     """64 rows of 151936 real columns (benchmark's value distribution) with
     zeros, values below 2^-24 and, in some rows, a value below -4.24e9 injected:
